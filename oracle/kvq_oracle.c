@@ -1,0 +1,381 @@
+/*
+ * kvq_oracle.c -- the CPU definition of the quantized paged decode-attention
+ * path.  TEST INFRASTRUCTURE ONLY (see kvq_oracle.h): only tests, the smoke
+ * check and the CPU-baseline leg of the benchmark load it.
+ *
+ * Build: gcc -O2 -std=c99 -fPIC -shared -ffp-contract=off (no -ffast-math:
+ * the quantize step is defined as one IEEE fp32 division).
+ */
+#define _POSIX_C_SOURCE 200809L
+#include "kvq_oracle.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* codecs                                                                    */
+/* ------------------------------------------------------------------------ */
+
+double kvqo_e4m3_value(uint8_t code) {
+    int s = code >> 7;
+    int e = (code >> 3) & 15;
+    int m = code & 7;
+    double mag;
+    if (e == 15 && m == 7) return NAN;           /* the only NaN encodings */
+    if (e == 0) mag = ldexp((double)m / 8.0, -6); /* subnormal: 0.mmm * 2^-6 */
+    else mag = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -mag : mag;
+}
+
+uint8_t kvqo_e4m3_encode(float y) {
+    uint8_t sign = signbit(y) ? 0x80 : 0x00;
+    if (isnan(y)) return (uint8_t)(0x7F | sign);
+    double a = fabs((double)y);
+    if (a > 448.0) return (uint8_t)(0x7E | sign); /* saturate (Inf too) */
+    int best = 0;
+    double best_d = INFINITY;
+    for (int c = 0; c <= 0x7E; ++c) {             /* all non-negative finite codes */
+        double d = fabs(kvqo_e4m3_value((uint8_t)c) - a);
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return (uint8_t)(best | sign);
+}
+
+float kvqo_bf16_to_float(uint16_t bits) {
+    uint32_t w = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &w, sizeof f);
+    return f;
+}
+
+uint8_t kvqo_e4m3_quantize(uint16_t x_bf16, float scale) {
+    volatile float x = kvqo_bf16_to_float(x_bf16);
+    volatile float y = x / scale; /* one IEEE fp32 division, round to nearest even */
+    return kvqo_e4m3_encode(y);
+}
+
+double kvqo_e2m1_value(uint8_t nibble) {
+    static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    double v = mag[nibble & 7];
+    return (nibble & 8) ? -v : v;
+}
+
+uint8_t kvqo_e2m1_encode(float y) {
+    uint8_t sign = signbit(y) ? 0x8 : 0x0;
+    if (isnan(y)) return (uint8_t)(0x7 | sign);
+    double a = fabs((double)y);
+    if (a > 6.0) return (uint8_t)(0x7 | sign);
+    int best = 0;
+    double best_d = INFINITY;
+    for (int c = 0; c < 8; ++c) {
+        double d = fabs(kvqo_e2m1_value((uint8_t)c) - a);
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return (uint8_t)(best | sign);
+}
+
+/* ------------------------------------------------------------------------ */
+/* calibration                                                               */
+/* ------------------------------------------------------------------------ */
+
+static int scale_from_amax(const float* amax, float* scale, int n, double top) {
+    for (int i = 0; i < n; ++i)
+        if (!(amax[i] >= 0.0f) || isinf(amax[i])) return -1;
+    for (int i = 0; i < n; ++i) {
+        double s = (double)amax[i] * 1.05 / top;
+        if (s < 1e-12) s = 1e-12;
+        scale[i] = (float)s;
+    }
+    return 0;
+}
+
+int kvqo_calibrate(const float* amax, float* scale, int n) {
+    return scale_from_amax(amax, scale, n, 448.0);
+}
+
+int kvqo_nvfp4_calibrate(const float* amax, float* gscale, int n) {
+    return scale_from_amax(amax, gscale, n, 6.0 * 448.0);
+}
+
+float kvqo_amax_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t row_stride) {
+    double m = 0.0;
+    int saw_nan = 0;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) {
+            double a = fabs((double)kvqo_bf16_to_float(x[r * row_stride + c]));
+            if (isnan(a)) saw_nan = 1;
+            else if (a > m) m = a;
+        }
+    return saw_nan ? NAN : (float)m;
+}
+
+/* ------------------------------------------------------------------------ */
+/* paged cache                                                               */
+/* ------------------------------------------------------------------------ */
+
+int64_t kvqo_nvfp4_region_bytes(int D, int block_size) {
+    return (int64_t)block_size * D / 2 + (int64_t)block_size * D / 16;
+}
+
+/* byte/element offset of (slot, g, d) in the K and V layouts */
+static int64_t k_index(int64_t slot, int g, int d, int Hkv, int D, int bs) {
+    int64_t blk = slot / bs, off = slot % bs;
+    return ((blk * Hkv + g) * bs + off) * D + d;
+}
+static int64_t v_index(int64_t slot, int g, int d, int Hkv, int D, int bs) {
+    int64_t blk = slot / bs, off = slot % bs;
+    return ((blk * Hkv + g) * D + d) * bs + off;
+}
+
+void kvqo_cache_write(const uint16_t* k, const uint16_t* v, int64_t src_stride,
+                      const int64_t* slot_mapping, int T, int Hkv, int D,
+                      void* k_cache, void* v_cache, int block_size, int kv_dtype,
+                      float k_scale, float v_scale) {
+    for (int t = 0; t < T; ++t) {
+        int64_t slot = slot_mapping[t];
+        if (slot < 0) continue;
+        for (int g = 0; g < Hkv; ++g)
+            for (int d = 0; d < D; ++d) {
+                uint16_t xk = k[t * src_stride + (int64_t)g * D + d];
+                uint16_t xv = v[t * src_stride + (int64_t)g * D + d];
+                int64_t ki = k_index(slot, g, d, Hkv, D, block_size);
+                int64_t vi = v_index(slot, g, d, Hkv, D, block_size);
+                if (kv_dtype == 0) {
+                    ((uint16_t*)k_cache)[ki] = xk;
+                    ((uint16_t*)v_cache)[vi] = xv;
+                } else {
+                    ((uint8_t*)k_cache)[ki] = kvqo_e4m3_quantize(xk, k_scale);
+                    ((uint8_t*)v_cache)[vi] = kvqo_e4m3_quantize(xv, v_scale);
+                }
+            }
+    }
+}
+
+/* NVFP4: quantize one 16-element group x[0..15] into codes[16] and a scale code */
+static void nvfp4_group(const uint16_t* x, float gscale, uint8_t* codes, uint8_t* bscale_code) {
+    float bamax = 0.0f;
+    int saw_nan = 0;
+    for (int i = 0; i < 16; ++i) {
+        float a = fabsf(kvqo_bf16_to_float(x[i]));
+        if (isnan(a)) saw_nan = 1;
+        else if (a > bamax) bamax = a;
+    }
+    if (saw_nan) bamax = NAN;
+    volatile float top = 6.0f * gscale;       /* fp32 product */
+    volatile float ratio = bamax / top;        /* fp32 division */
+    *bscale_code = kvqo_e4m3_encode(ratio);
+    volatile float e = (float)kvqo_e4m3_value(*bscale_code) * gscale; /* fp32 product */
+    for (int i = 0; i < 16; ++i) {
+        if (e == 0.0f) {
+            codes[i] = 0;
+        } else {
+            volatile float y = kvqo_bf16_to_float(x[i]) / e; /* fp32 division */
+            codes[i] = kvqo_e2m1_encode(y);
+        }
+    }
+}
+
+static void set_nibble(uint8_t* p, int64_t nib_index, uint8_t code) {
+    uint8_t* byte = p + nib_index / 2;
+    if (nib_index % 2 == 0) *byte = (uint8_t)((*byte & 0xF0) | (code & 0xF));
+    else *byte = (uint8_t)((*byte & 0x0F) | ((code & 0xF) << 4));
+}
+
+static uint8_t get_nibble(const uint8_t* p, int64_t nib_index) {
+    uint8_t byte = p[nib_index / 2];
+    return (nib_index % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+}
+
+void kvqo_nvfp4_cache_write(const uint16_t* k, const uint16_t* v, int64_t src_stride,
+                            const int64_t* slot_mapping, int T, int Hkv, int D,
+                            uint8_t* k_cache, uint8_t* v_cache, int block_size,
+                            float k_gscale, float v_gscale) {
+    int64_t region = kvqo_nvfp4_region_bytes(D, block_size);
+    int64_t codes_bytes = (int64_t)block_size * D / 2;
+    for (int t = 0; t < T; ++t) {
+        int64_t slot = slot_mapping[t];
+        if (slot < 0) continue;
+        int64_t blk = slot / block_size, off = slot % block_size;
+        for (int g = 0; g < Hkv; ++g) {
+            uint8_t* kr = k_cache + (blk * Hkv + g) * region;
+            uint8_t* vr = v_cache + (blk * Hkv + g) * region;
+            for (int grp = 0; grp < D / 16; ++grp) {
+                uint8_t codes[16], sc;
+                const uint16_t* xk = k + t * src_stride + (int64_t)g * D + grp * 16;
+                nvfp4_group(xk, k_gscale, codes, &sc);
+                for (int i = 0; i < 16; ++i)
+                    set_nibble(kr, off * D + grp * 16 + i, codes[i]);      /* [bs][D] nibbles */
+                kr[codes_bytes + off * (D / 16) + grp] = sc;
+
+                const uint16_t* xv = v + t * src_stride + (int64_t)g * D + grp * 16;
+                nvfp4_group(xv, v_gscale, codes, &sc);
+                for (int i = 0; i < 16; ++i)
+                    set_nibble(vr, (int64_t)(grp * 16 + i) * block_size + off, codes[i]); /* [D][bs] nibbles */
+                vr[codes_bytes + off * (D / 16) + grp] = sc;
+            }
+        }
+    }
+}
+
+double kvqo_nvfp4_k_value(const uint8_t* k_cache, int64_t slot, int g, int d,
+                          int Hkv, int D, int block_size, float k_gscale) {
+    int64_t region = kvqo_nvfp4_region_bytes(D, block_size);
+    int64_t blk = slot / block_size, off = slot % block_size;
+    const uint8_t* r = k_cache + (blk * Hkv + g) * region;
+    uint8_t code = get_nibble(r, off * D + d);
+    uint8_t sc = r[(int64_t)block_size * D / 2 + off * (D / 16) + d / 16];
+    return kvqo_e2m1_value(code) * kvqo_e4m3_value(sc) * (double)k_gscale;
+}
+
+double kvqo_nvfp4_v_value(const uint8_t* v_cache, int64_t slot, int g, int d,
+                          int Hkv, int D, int block_size, float v_gscale) {
+    int64_t region = kvqo_nvfp4_region_bytes(D, block_size);
+    int64_t blk = slot / block_size, off = slot % block_size;
+    const uint8_t* r = v_cache + (blk * Hkv + g) * region;
+    uint8_t code = get_nibble(r, (int64_t)d * block_size + off);
+    uint8_t sc = r[(int64_t)block_size * D / 2 + off * (D / 16) + d / 16];
+    return kvqo_e2m1_value(code) * kvqo_e4m3_value(sc) * (double)v_gscale;
+}
+
+/* ------------------------------------------------------------------------ */
+/* attention                                                                 */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    const uint16_t* q;
+    const void* k_cache;
+    const void* v_cache;
+    int kv_dtype;
+    const int32_t* block_tables;
+    int max_blocks;
+    const int32_t* seq_lens;
+    int B, Hq, Hkv, D, block_size;
+    float k_scale, v_scale, sm_scale;
+    const int32_t* units; /* NULL: unit i is (i / Hq, i % Hq) */
+    int n_units;
+    double* out;
+    int next_unit;
+    pthread_mutex_t lock;
+} attn_job;
+
+static double k_value(const attn_job* j, int64_t slot, int g, int d) {
+    if (j->kv_dtype == 2)
+        return kvqo_nvfp4_k_value((const uint8_t*)j->k_cache, slot, g, d, j->Hkv, j->D,
+                                  j->block_size, j->k_scale);
+    int64_t i = k_index(slot, g, d, j->Hkv, j->D, j->block_size);
+    if (j->kv_dtype == 0) return (double)kvqo_bf16_to_float(((const uint16_t*)j->k_cache)[i]);
+    return kvqo_e4m3_value(((const uint8_t*)j->k_cache)[i]) * (double)j->k_scale;
+}
+
+static double v_value(const attn_job* j, int64_t slot, int g, int d) {
+    if (j->kv_dtype == 2)
+        return kvqo_nvfp4_v_value((const uint8_t*)j->v_cache, slot, g, d, j->Hkv, j->D,
+                                  j->block_size, j->v_scale);
+    int64_t i = v_index(slot, g, d, j->Hkv, j->D, j->block_size);
+    if (j->kv_dtype == 0) return (double)kvqo_bf16_to_float(((const uint16_t*)j->v_cache)[i]);
+    return kvqo_e4m3_value(((const uint8_t*)j->v_cache)[i]) * (double)j->v_scale;
+}
+
+static void attend_one(const attn_job* j, int b, int h, double* out, double* s) {
+    int G = j->Hq / j->Hkv;
+    int g = h / G;
+    int L = j->seq_lens[b];
+    int D = j->D;
+    const uint16_t* q = j->q + ((int64_t)b * j->Hq + h) * D;
+    for (int d = 0; d < D; ++d) out[d] = 0.0;
+    if (L <= 0) return;
+    double m = -INFINITY;
+    for (int t = 0; t < L; ++t) {
+        int64_t slot = (int64_t)j->block_tables[(int64_t)b * j->max_blocks + t / j->block_size] *
+                           j->block_size + t % j->block_size;
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d) dot += (double)kvqo_bf16_to_float(q[d]) * k_value(j, slot, g, d);
+        s[t] = (double)j->sm_scale * dot;
+        if (s[t] > m) m = s[t];
+    }
+    double denom = 0.0;
+    for (int t = 0; t < L; ++t) {
+        int64_t slot = (int64_t)j->block_tables[(int64_t)b * j->max_blocks + t / j->block_size] *
+                           j->block_size + t % j->block_size;
+        double w = exp(s[t] - m);
+        denom += w;
+        for (int d = 0; d < D; ++d) out[d] += w * v_value(j, slot, g, d);
+    }
+    for (int d = 0; d < D; ++d) out[d] /= denom;
+}
+
+static void* attn_worker(void* arg) {
+    attn_job* j = (attn_job*)arg;
+    int max_L = 0;
+    for (int b = 0; b < j->B; ++b)
+        if (j->seq_lens[b] > max_L) max_L = j->seq_lens[b];
+    double* s = (double*)malloc(sizeof(double) * (size_t)(max_L > 0 ? max_L : 1));
+    for (;;) {
+        pthread_mutex_lock(&j->lock);
+        int u = j->next_unit++;
+        pthread_mutex_unlock(&j->lock);
+        if (u >= j->n_units) break;
+        int b = j->units ? j->units[2 * u] : u / j->Hq;
+        int h = j->units ? j->units[2 * u + 1] : u % j->Hq;
+        attend_one(j, b, h, j->out + (int64_t)u * j->D, s);
+    }
+    free(s);
+    return NULL;
+}
+
+static void run_attn(attn_job* j, int nthreads) {
+    if (nthreads < 1) nthreads = 1;
+    pthread_mutex_init(&j->lock, NULL);
+    j->next_unit = 0;
+    if (nthreads == 1) {
+        attn_worker(j);
+    } else {
+        pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+        for (int i = 0; i < nthreads; ++i) pthread_create(&th[i], NULL, attn_worker, j);
+        for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+        free(th);
+    }
+    pthread_mutex_destroy(&j->lock);
+}
+
+void kvqo_decode_attn(const uint16_t* q, const void* k_cache, const void* v_cache,
+                      int kv_dtype, const int32_t* block_tables, int max_blocks,
+                      const int32_t* seq_lens, int B, int Hq, int Hkv, int D,
+                      int block_size, float k_scale, float v_scale, float sm_scale,
+                      double* out, int nthreads) {
+    attn_job j = {q, k_cache, v_cache, kv_dtype, block_tables, max_blocks, seq_lens,
+                  B, Hq, Hkv, D, block_size, k_scale, v_scale, sm_scale,
+                  NULL, B * Hq, out, 0};
+    run_attn(&j, nthreads);
+}
+
+void kvqo_decode_attn_units(const uint16_t* q, const void* k_cache, const void* v_cache,
+                            int kv_dtype, const int32_t* block_tables, int max_blocks,
+                            const int32_t* seq_lens, int B, int Hq, int Hkv, int D,
+                            int block_size, float k_scale, float v_scale, float sm_scale,
+                            const int32_t* units, int n_units, double* out, int nthreads) {
+    attn_job j = {q, k_cache, v_cache, kv_dtype, block_tables, max_blocks, seq_lens,
+                  B, Hq, Hkv, D, block_size, k_scale, v_scale, sm_scale,
+                  units, n_units, out, 0};
+    run_attn(&j, nthreads);
+}
+
+double kvqo_fp8_cos_sim(const uint16_t* x, int64_t n, float scale) {
+    double xy = 0.0, xx = 0.0, yy = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        double a = (double)kvqo_bf16_to_float(x[i]);
+        double r = kvqo_e4m3_value(kvqo_e4m3_quantize(x[i], scale)) * (double)scale;
+        xy += a * r;
+        xx += a * a;
+        yy += r * r;
+    }
+    return xy / sqrt(xx * yy);
+}

@@ -1,0 +1,159 @@
+/*
+ * kvq_oracle.h -- plain, slow, obviously-correct CPU definition of the FP8 /
+ * 4-bit KV-cache quantization and paged decode-attention path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, includes
+ * or calls this code; only the tests, the smoke check and the CPU-baseline leg
+ * of the benchmark do.  It shares no source with the GPU path.
+ *
+ * Every routine is written as the definition of its result: fp64 arithmetic
+ * except where a step is defined to happen in fp32 (the quantize division and
+ * the NVFP4 scale products), brute-force nearest-value search for the codecs,
+ * and a direct loop over logical tokens for attention.  No blocking, no
+ * fusion, no reordering.
+ *
+ * Sources (web pages; cited by title and the part of the page):
+ *   [CAL]  "FP8 KV calibration" operator guide for the Radiance vLLM fork on
+ *          Radeon AI PRO R9700 (thetechpanda.github.io, FP8-KV-CALIBRATION):
+ *          the calibrator paragraph (per-layer scale formula, OCP E4M3,
+ *          maximum 448, 5% headroom, 1e-12 floor, combine across ranks) and
+ *          the storage paragraph (FP8 is one byte per element, half of BF16).
+ *   [RUN26] "I Tested NVFP4 vs FP8 KV Cache on Blackwell" video description
+ *          (Skildcore Run 26: KV Cache Precision), "WHAT YOU'LL LEARN" list:
+ *          24,576 B/token in BF16; E4M3 one byte per number; block-scaled
+ *          4-bit float with FP8 scale factors at 4.5 bits per number; every
+ *          decode token reads the whole cache; chapter "The Missing Fused
+ *          Dequant Kernel"; "two-level FP32 accumulation".
+ *
+ * Readings where the pages are silent (the OCP E4M3 / E2M1 bit layouts, the
+ * cache layout, the NVFP4 global-scale formula, block axis and nibble order)
+ * are stated at each function.
+ */
+#ifndef KVQ_ORACLE_H
+#define KVQ_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- codecs ------------------------------------------------------------ */
+
+/* OCP E4M3 value of a code ([CAL] calibrator paragraph names OCP E4M3 with
+ * maximum 448).  Layout (OCP 8-bit FP spec): 1 sign, 4 exponent (bias 7),
+ * 3 mantissa bits; exponent 0 is subnormal; S.1111.111 is NaN; no Inf. */
+double kvqo_e4m3_value(uint8_t code);
+
+/* Saturating round-to-nearest-even fp32 -> E4M3 by brute-force search over
+ * the 127 non-negative finite codes; ties go to the even code; |y| > 448 and
+ * +-Inf saturate to +-448; NaN -> 0x7F with the NaN's sign; the sign of y is
+ * kept, so negative values that round to zero give 0x80. */
+uint8_t kvqo_e4m3_encode(float y);
+
+/* bf16 bit pattern -> fp32 (exact). */
+float kvqo_bf16_to_float(uint16_t bits);
+
+/* Quantize one bf16 element with a per-layer scale: the scale multiplies the
+ * code value to give the real value ([CAL] scale formula), so quantizing
+ * divides: y = fp32(x) / scale in IEEE fp32 (one rounding), then E4M3. */
+uint8_t kvqo_e4m3_quantize(uint16_t x_bf16, float scale);
+
+/* E2M1 value of a 4-bit code: bit 3 sign, 2 exponent bits (bias 1), 1
+ * mantissa bit: {0, 0.5, 1, 1.5, 2, 3, 4, 6}. */
+double kvqo_e2m1_value(uint8_t nibble);
+
+/* Saturating RNE fp32 -> E2M1 by brute force over the 8 non-negative values,
+ * ties to the even code, |y| > 6 and Inf -> 6, NaN -> 6 with its sign. */
+uint8_t kvqo_e2m1_encode(float y);
+
+/* ---- calibration ------------------------------------------------------- */
+
+/* [CAL] calibrator paragraph: scale = max(amax * 1.05 / 448, 1e-12), per
+ * layer.  Evaluated left to right in fp64, rounded once to fp32.  Returns 0,
+ * or -1 (and leaves scale[i] untouched) if any amax is negative, NaN or Inf. */
+int kvqo_calibrate(const float* amax, float* scale, int n);
+
+/* Max |x| over a bf16 matrix of `rows` rows of `cols` elements, row stride
+ * `row_stride` elements.  Exact.  Any NaN makes the result NaN. */
+float kvqo_amax_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t row_stride);
+
+/* NVFP4 global scale (reading of [RUN26] "block-scaled 4-bit float with FP8
+ * scale factors"; the pages print no formula): the [CAL] formula with the
+ * largest representable magnitude 6 * 448 = 2688 (E2M1 max times E4M3 max):
+ * gscale = fp32(max(amax * 1.05 / 2688, 1e-12)).  Same error rule. */
+int kvqo_nvfp4_calibrate(const float* amax, float* gscale, int n);
+
+/* ---- paged cache layout -------------------------------------------------
+ * A cache is num_blocks physical blocks; each block holds block_size tokens
+ * of Hkv heads.  Element (token t of a sequence, head g, dim d) with slot
+ * s = phys_block * block_size + off:
+ *   K cache (FP8 u8 or BF16 u16):  [num_blocks][Hkv][block_size][D]
+ *   V cache (FP8 u8 or BF16 u16):  [num_blocks][Hkv][D][block_size]
+ * (V is stored dim-major inside a block.)
+ * NVFP4 cache region per (block, head), bytes:
+ *   K: codes [block_size][D/2] (element 2i low nibble, 2i+1 high nibble)
+ *      then block scales [block_size][D/16] (E4M3 codes)
+ *   V: codes [D][block_size/2] (token 2j low nibble, 2j+1 high nibble)
+ *      then block scales [block_size][D/16]
+ *   region bytes = block_size*D/2 + block_size*D/16. */
+int64_t kvqo_nvfp4_region_bytes(int D, int block_size);
+
+/* Write T tokens of K and V (bf16, [T][Hkv][D], token stride `src_stride`
+ * elements) into the caches at slot_mapping[t]; slot < 0 skips the token.
+ * kv_dtype 0 = BF16 (bit copy, scales unused), 1 = FP8 E4M3 with the given
+ * per-layer scales.  Bytes not addressed are left unchanged. */
+void kvqo_cache_write(const uint16_t* k, const uint16_t* v, int64_t src_stride,
+                      const int64_t* slot_mapping, int T, int Hkv, int D,
+                      void* k_cache, void* v_cache, int block_size, int kv_dtype,
+                      float k_scale, float v_scale);
+
+/* NVFP4 write.  For each (token, head) row and each group of 16 consecutive
+ * dims: bamax = max |x| (fp32); bscale = E4M3(bamax / fp32(6 * gscale));
+ * e = fp32(value(bscale) * gscale); codes = E2M1(x / e) (fp32), or all zero
+ * when e == 0. */
+void kvqo_nvfp4_cache_write(const uint16_t* k, const uint16_t* v, int64_t src_stride,
+                            const int64_t* slot_mapping, int T, int Hkv, int D,
+                            uint8_t* k_cache, uint8_t* v_cache, int block_size,
+                            float k_gscale, float v_gscale);
+
+/* Dequantized value of element (slot, head g, dim d) of an NVFP4 K or V cache. */
+double kvqo_nvfp4_k_value(const uint8_t* k_cache, int64_t slot, int g, int d,
+                          int Hkv, int D, int block_size, float k_gscale);
+double kvqo_nvfp4_v_value(const uint8_t* v_cache, int64_t slot, int g, int d,
+                          int Hkv, int D, int block_size, float v_gscale);
+
+/* ---- attention ----------------------------------------------------------
+ * Single-token decode attention over a paged cache ([RUN26]: every generated
+ * token reads the whole cache).  For sequence b, query head h (KV head
+ * g = h / (Hq/Hkv)), L = seq_lens[b] tokens, token t at physical block
+ * block_tables[b*max_blocks + t/block_size], offset t % block_size:
+ *   k_t, v_t = dequantized cache values (fp64)
+ *   s_t = sm_scale * sum_d q[d] * k_t[d]
+ *   out = sum_t exp(s_t - max s) v_t / sum_t exp(s_t - max s)
+ * and out = 0 when L == 0.  q is bf16 [B][Hq][D]; out is fp64 [B][Hq][D].
+ * kv_dtype 0 = BF16 cache, 1 = FP8 cache (scales applied), 2 = NVFP4 cache
+ * (k_scale / v_scale are the global scales).  `nthreads` > 1 splits the
+ * independent (b, h) units over threads; results do not depend on it. */
+void kvqo_decode_attn(const uint16_t* q, const void* k_cache, const void* v_cache,
+                      int kv_dtype, const int32_t* block_tables, int max_blocks,
+                      const int32_t* seq_lens, int B, int Hq, int Hkv, int D,
+                      int block_size, float k_scale, float v_scale, float sm_scale,
+                      double* out, int nthreads);
+
+/* Same, for a chosen subset of (b, h) units: units[2*i] = b, units[2*i+1] = h;
+ * out is [n_units][D]. */
+void kvqo_decode_attn_units(const uint16_t* q, const void* k_cache, const void* v_cache,
+                            int kv_dtype, const int32_t* block_tables, int max_blocks,
+                            const int32_t* seq_lens, int B, int Hq, int Hkv, int D,
+                            int block_size, float k_scale, float v_scale, float sm_scale,
+                            const int32_t* units, int n_units, double* out, int nthreads);
+
+/* Reconstruction cosine similarity of n bf16 values against their FP8
+ * round trip value(E4M3(x / scale)) * scale, in fp64. */
+double kvqo_fp8_cos_sim(const uint16_t* x, int64_t n, float scale);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
