@@ -1,0 +1,257 @@
+"""Benchmark: FP8 paged decode attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gptoss65k]
+
+A step is one decode step of one full-attention layer of the gpt-oss-20b-shaped
+workload (64 query / 8 KV heads, head dim 64, one sequence of 65,536 tokens):
+kvq_cache_write of the newest token's K/V into the FP8 paged cache, then
+kvq_paged_decode_attn over all 65,536 tokens.  Steps rotate over 12 distinct
+layer caches (the model's 12 full-attention layers, 768 MiB of FP8 KV), so each
+step reads its cache from HBM rather than the 256 MB last-level cache.  Inputs
+are synthetic (seeded N(0,1) with 0.5% x10 outliers) and resident in HBM
+before timing starts.
+
+Prints one JSON line.  `value` is achieved HBM GB/s: algorithmic bytes of a
+step (KV bytes read once per KV head, block table, seq lens, q, out, the new
+token's K/V in and codes out) over the step time.  Also reported: KV tokens
+scanned/s, the BF16-KV step for comparison, the roofline of the dominant
+kernel (decode attention) and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "FP8 paged decode-attn achieved HBM GB/s (% of peak) + KV tokens scanned/s"
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["quantized_decode_attention_calibrate_amd/csrc/kvq_attn.hip",
+                  "quantized_decode_attention_calibrate_amd/csrc/kvq_device.h",
+                  "quantized_decode_attention_calibrate_amd/csrc/kvq_internal.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def step_bytes(B, Hq, Hkv, D, seq_lens, kv_elem_bytes, n_new):
+    """Algorithmic HBM bytes of one step: (decode attention, cache write)."""
+    tokens = sum(seq_lens)
+    kv = tokens * Hkv * 2 * D * kv_elem_bytes
+    table = sum((L + 15) // 16 for L in seq_lens) * 4 + B * 4
+    qo = 2 * B * Hq * D * 2
+    write = n_new * (Hkv * D * 2 * 2 + Hkv * D * 2 * kv_elem_bytes + 8)
+    return kv + table + qo, write
+
+
+class Layers:
+    """R layer caches of one workload, written by the library."""
+
+    def __init__(self, K, w, kv_dtype, R, dev):
+        import torch
+        self.K, self.w, self.kv_dtype, self.R = K, w, kv_dtype, R
+        self.q = w.q.to(dev)
+        k, v = w.k.to(dev), w.v.to(dev)
+        self.bt = w.block_tables.to(dev)
+        self.sl = torch.tensor(w.seq_lens, dtype=torch.int32, device=dev)
+        if kv_dtype == K.KVQ_KV_FP8_E4M3:
+            amax = torch.zeros(2, dtype=torch.float32, device=dev)
+            K.kvq_amax_bf16(k, amax[0:1])
+            K.kvq_amax_bf16(v, amax[1:2])
+            self.ks, self.vs = K.kvq_calibrate(amax.cpu().tolist())
+        else:
+            self.ks, self.vs = 1.0, 1.0
+        rows = w.last_token_rows()
+        rows = rows[rows >= 0].to(dev)
+        self.new_k = k[rows].contiguous()
+        self.new_v = v[rows].contiguous()
+        self.new_slots = w.slot_mapping.to(dev)[rows].contiguous()
+        self.caches = []
+        pre = w.prefill_slots().to(dev)
+        for _ in range(R):
+            kc, vc = K.new_caches(kv_dtype, w.num_blocks, w.Hkv, w.D, device=dev)
+            K.kvq_cache_write(k, v, pre, kc, vc, kv_dtype, self.ks, self.vs)
+            self.caches.append((kc, vc))
+        del k, v
+        self.out = torch.empty(w.B, w.Hq, w.D, dtype=torch.bfloat16, device=dev)
+        self.ws = K.new_workspace(w.B, w.Hq, w.Hkv, w.D, w.max_seq_len, device=dev)
+        self.sm = float(1.0 / math.sqrt(w.D))
+        torch.cuda.synchronize()
+
+    def write(self, i):
+        kc, vc = self.caches[i % self.R]
+        self.K.kvq_cache_write(self.new_k, self.new_v, self.new_slots, kc, vc, self.kv_dtype, self.ks, self.vs)
+
+    def attend(self, i, impl=0):
+        kc, vc = self.caches[i % self.R]
+        w = self.w
+        self.K.kvq_paged_decode_attn(self.q, kc, vc, self.kv_dtype, self.bt, self.sl, w.max_seq_len, w.Hkv,
+                                     self.ks, self.vs, self.sm, self.out, self.ws, impl=impl)
+
+
+def time_steps(torch, layers, steps, warmup, impl=0):
+    """Returns (ms per step, mean ms of the attention call alone), HIP events on the launch stream."""
+    for i in range(warmup):
+        layers.write(i)
+        layers.attend(i, impl)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(st)
+    for i in range(steps):
+        layers.write(i)
+        layers.attend(i, impl)
+    t1.record(st)
+    torch.cuda.synchronize()
+    step_ms = t0.elapsed_time(t1) / steps
+    # attention calls alone, bracketed one by one (dominant kernel's launch duration)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        layers.write(i)
+        evs[i][0].record(st)
+        layers.attend(i, impl)
+        evs[i][1].record(st)
+    torch.cuda.synchronize()
+    attn_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    return step_ms, sum(attn_ms) / len(attn_ms), attn_ms[len(attn_ms) // 2]
+
+
+def cpu_baseline(w, ks, vs, n_kv_heads=1):
+    """The oracle (fp64 C, brute-force codecs) timed on this host's cores over a
+    bounded sample: n_kv_heads KV heads (all their G query heads) of the
+    workload; scaled to the full step by the number of KV heads."""
+    import numpy as np
+    import oracle
+    import torch
+    G = w.Hq // w.Hkv
+    sub_k = w.k[:, :n_kv_heads, :].contiguous()
+    sub_v = w.v[:, :n_kv_heads, :].contiguous()
+    kc, vc = oracle.new_caches(oracle.KV_FP8, w.num_blocks, n_kv_heads, w.D, 16)
+    oracle.cache_write(sub_k, sub_v, w.slot_mapping, kc, vc, oracle.KV_FP8, ks, vs)
+    q = w.q[:, :n_kv_heads * G, :].contiguous()
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    cores = max(1, min(cores, 16))
+    t = time.perf_counter()
+    oracle.decode_attn(q, kc, vc, oracle.KV_FP8, w.block_tables, w.seq_lens, n_kv_heads, 16, ks, vs,
+                       float(np.float32(1.0 / math.sqrt(w.D))), nthreads=cores)
+    dt = time.perf_counter() - t
+    step_s = dt * w.Hkv / n_kv_heads
+    return step_s, cores, dt
+
+
+def read_traffic(kernel_hash):
+    """HBM traffic per launch from the committed PMC summary, if it was taken on this kernel source."""
+    path = os.path.join(PROFILES, "decode_fp8_gptoss65k_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_hash") != kernel_hash:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=600)
+    ap.add_argument("--warmup", type=int, default=60)
+    ap.add_argument("--workload", default="gptoss65k")
+    ap.add_argument("--layers", type=int, default=12)
+    ap.add_argument("--impl", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-compare", action="store_true", help="skip the BF16 and other-family runs")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this path has no multi-GPU "
+              "mode: the decode kernel shards by KV head or by sequence with no exchange.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from quantized_decode_attention_calibrate_amd import kvq as K
+    from quantized_decode_attention_calibrate_amd import workloads
+
+    dev = "cuda"
+    print(f"[bench] building {args.workload} on {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
+    w = workloads.make(args.workload, device=dev, seed=0)
+    w_cpu = None
+    fp8 = Layers(K, w, K.KVQ_KV_FP8_E4M3, args.layers, dev)
+    print("[bench] timing FP8", file=sys.stderr, flush=True)
+    step_ms, attn_ms, attn_med = time_steps(torch, fp8, args.steps, args.warmup, args.impl)
+    attn_b, write_b = step_bytes(w.B, w.Hq, w.Hkv, w.D, w.seq_lens, 1, w.B)
+    tokens = sum(w.seq_lens)
+    gbps = (attn_b + write_b) / (step_ms * 1e-3) / 1e9
+    achieved = attn_b / (attn_ms * 1e-3) / 1e9
+    khash = kernel_source_hash()
+    traffic = read_traffic(khash)
+    result = {
+        "metric": METRIC,
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 KV, f32 accumulate",
+        "data": "synthetic (seeded N(0,1), 0.5% of K/V x10)",
+        "config": {"workload": f"{args.workload}: B={w.B} x L={w.max_seq_len}, Hq={w.Hq}/Hkv={w.Hkv}, D={w.D}, "
+                               f"block 16, FP8 E4M3 paged KV, {args.layers} layer caches rotated; step = "
+                               "cache write of the new token + decode attention",
+                   "B": w.B, "seq_len": w.max_seq_len, "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.D,
+                   "kv_dtype": "fp8_e4m3", "layers_rotated": args.layers,
+                   "split_tokens": K.kvq_decode_plan_split_tokens(w.B, w.Hkv, w.max_seq_len)},
+        "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "kv_tokens_per_s": round(tokens / (step_ms * 1e-3), 1),
+        "step_bytes": attn_b + write_b,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": "kvq_paged_decode_attn (split-K decode + merge), bytes per launch = "
+                               f"{attn_b}", "attn_ms_mean": round(attn_ms, 6), "attn_ms_median": round(attn_med, 6),
+                     "kernel_source_hash": khash},
+    }
+    if not args.no_compare:
+        print("[bench] timing BF16 comparator", file=sys.stderr, flush=True)
+        fp8_caches = fp8.caches
+        del fp8
+        torch.cuda.empty_cache()
+        bf = Layers(K, w, K.KVQ_KV_BF16, args.layers, dev)
+        b_step, b_attn, _ = time_steps(torch, bf, args.steps, args.warmup, args.impl)
+        b_attn_b, _ = step_bytes(w.B, w.Hq, w.Hkv, w.D, w.seq_lens, 2, w.B)
+        result["bf16_kv"] = {"ms_per_step": round(b_step, 6), "attn_ms_mean": round(b_attn, 6),
+                             "attn_gbps": round(b_attn_b / (b_attn * 1e-3) / 1e9, 2)}
+        result["fp8_over_bf16_attn_time"] = round(attn_ms / b_attn, 4)
+        del bf, fp8_caches
+        torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        w_cpu = workloads.make(args.workload, device="cpu", seed=0)
+        amax_k = float(w_cpu.k.float().abs().max())
+        amax_v = float(w_cpu.v.float().abs().max())
+        ks, vs = K.kvq_calibrate([amax_k, amax_v])
+        step_s, cores, dt = cpu_baseline(w_cpu, ks, vs, n_kv_heads=1)
+        result["cpu_baseline"] = {
+            "value": round(attn_b / step_s / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"oracle decode attention (fp64) of 1 of {w.Hkv} KV heads (its {w.G} query heads) over "
+                      f"all {tokens} tokens, {dt:.2f} s on {cores} threads, scaled x{w.Hkv} to the full "
+                      "attention step; cache write excluded",
+            "kv_tokens_per_s": round(tokens / step_s, 1)}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,188 @@
+/*
+ * kvq.h -- C ABI of libkvq.so: FP8 (OCP E4M3) and block-scaled 4-bit KV-cache
+ * quantization with calibrated per-layer scales, paged KV-cache writes, and
+ * single-token split-K paged decode attention that dequantizes inside the
+ * kernel, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages, cited by title and the part of the page):
+ *   [CAL]   "FP8 KV calibration" guide for the Radiance vLLM fork on Radeon AI
+ *           PRO R9700: calibrator paragraph (observe BF16 K/V absolute maxima,
+ *           combine across ranks, scale = max(amax * 1.05 / 448, 1e-12), OCP
+ *           E4M3); storage paragraph (FP8 is one byte per element, half of BF16).
+ *   [RUN26] "I Tested NVFP4 vs FP8 KV Cache on Blackwell" video description
+ *           (Skildcore Run 26: KV Cache Precision), WHAT YOU'LL LEARN list and
+ *           CHAPTERS: every generated token reads the whole KV cache; E4M3 one
+ *           byte per number; block-scaled 4-bit float with FP8 scale factors,
+ *           4.5 bits per number; chapter "The Missing Fused Dequant Kernel";
+ *           "two-level FP32 accumulation".
+ *
+ * Conventions for every call:
+ *   - Pointers named *_dev are device pointers, *_host are host pointers.  The
+ *     caller owns every buffer; the library allocates nothing and keeps no
+ *     per-call state.
+ *   - `hip_stream` is a hipStream_t passed as void* (NULL = default stream).
+ *     Device calls are asynchronous: they validate arguments on the host,
+ *     enqueue kernels on the stream and return; they never synchronize.
+ *   - Return value: KVQ_OK or a negative kvq_status.  Host validation happens
+ *     before any HIP call, so an invalid call enqueues nothing.  A failed
+ *     launch returns KVQ_EHIP; kvq_last_hip_error() then gives the hipError_t
+ *     (per calling thread).  Nothing throws or aborts.
+ *   - Data that lives on the device (slot mappings, block tables, sequence
+ *     lengths) is the caller's contract: slots < num_blocks * block_size,
+ *     block ids < num_blocks, 0 <= seq_lens[b] <= max_seq_len.  The library
+ *     cannot check device data without a synchronization and does not.
+ *   - All tensors are dense row-major; device pointers to caches, q, out and
+ *     k/v sources must be 16-byte aligned and the k/v token stride a multiple
+ *     of 8 elements (KVQ_EINVAL otherwise).
+ *   - GQA: query head h reads KV head h / (Hq / Hkv).
+ *
+ * Paged cache layout (num_blocks physical blocks of block_size tokens):
+ *   BF16 / FP8 K cache  [num_blocks][Hkv][block_size][D]    (u16 / u8)
+ *   BF16 / FP8 V cache  [num_blocks][Hkv][D][block_size]    (u16 / u8, dim-major)
+ *   NVFP4 K and V cache [num_blocks][Hkv][kvq_nvfp4_region_bytes(D, bs)] bytes
+ *   A token's slot is physical_block * block_size + offset.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_ABI_VERSION 1
+
+enum kvq_status {
+    KVQ_OK = 0,
+    KVQ_EINVAL = -1,        /* bad pointer, size, alignment or argument combination */
+    KVQ_EUNSUPPORTED = -2,  /* valid but not implemented here (D, block_size, G) */
+    KVQ_EWORKSPACE = -3,    /* workspace smaller than kvq_decode_workspace_bytes() */
+    KVQ_EHIP = -4           /* a HIP launch failed; see kvq_last_hip_error() */
+};
+
+enum kvq_kv_dtype { KVQ_KV_BF16 = 0, KVQ_KV_FP8_E4M3 = 1 };
+
+/* F32 writes the fp32 epilogue unrounded (same kernels; only the final store
+ * differs); BF16 rounds it to nearest even. */
+enum kvq_out_dtype { KVQ_OUT_BF16 = 0, KVQ_OUT_F32 = 1 };
+
+/* Decode-attention kernel family (for comparisons; AUTO picks per shape). */
+enum kvq_attn_impl { KVQ_IMPL_AUTO = 0, KVQ_IMPL_VALU = 1, KVQ_IMPL_MFMA = 2 };
+
+/* Human-readable text of a kvq_status (static storage). */
+const char* kvq_strerror(int status);
+
+/* hipError_t of the last KVQ_EHIP returned on this thread (0 if none). */
+int kvq_last_hip_error(void);
+
+/* KVQ_ABI_VERSION of the loaded library. */
+int kvq_abi_version(void);
+
+/* ---- codec utilities (device) ---------------------------------------------
+ * The E4M3 codec used by every kernel, exposed for exhaustive checks.
+ * Encode: saturating round-to-nearest-even fp32 -> OCP E4M3 ([CAL]: OCP E4M3,
+ * maximum 448): |y| > 448 and +-Inf -> +-448 (0x7E/0xFE), NaN -> 0x7F with
+ * the NaN's sign, sign kept on underflow (-tiny -> 0x80).
+ * Decode: exact; out_kind 0 = fp32, 1 = fp16, 2 = bf16 (every finite E4M3
+ * value is exact in all three), through the conversion the attention kernels
+ * use for that type.  codes_dev: n bytes; y_dev / out_dev: n elements. */
+int kvq_e4m3_encode_f32(const float* y_dev, uint8_t* codes_dev, int64_t n, void* hip_stream);
+int kvq_e4m3_decode(const uint8_t* codes_dev, void* out_dev, int out_kind, int64_t n, void* hip_stream);
+
+/* ---- calibration ---------------------------------------------------------
+ * [CAL] calibrator paragraph: the calibrator observes BF16 K/V absolute
+ * maxima per layer, combines observations by maximum, and writes
+ * scale = max(observed_absolute_max * 1.05 / 448, 1e-12).
+ *
+ * kvq_amax_bf16: running maximum of |x| over a bf16 matrix of `rows` rows of
+ * `cols` elements with row stride `row_stride` elements (e.g. K as
+ * [T][Hkv*D]) into *amax_dev (fp32, device).  *amax_dev must be initialised by
+ * the caller (0 for a fresh observation); calling it again on more data, or on
+ * data from another rank, combines by maximum.  Exact.  A NaN anywhere makes
+ * the result NaN (kvq_calibrate then rejects it).  rows == 0 is a no-op. */
+int kvq_amax_bf16(const void* x_dev, int64_t rows, int64_t cols, int64_t row_stride,
+                  float* amax_dev, void* hip_stream);
+
+/* kvq_calibrate: host only.  scale_host[i] = fp32(max((double)amax_host[i] *
+ * 1.05 / 448, 1e-12)), evaluated left to right in fp64 and rounded once.
+ * KVQ_EINVAL (scale_host untouched) if any amax is negative, NaN or Inf. */
+int kvq_calibrate(const float* amax_host, float* scale_host, int n);
+
+/* ---- cache write ---------------------------------------------------------
+ * [CAL] storage paragraph: FP8 stores one byte per K or V element against two
+ * for BF16, so an FP8 block is half the size of a BF16 block.
+ *
+ * Quantize T tokens of K and V and scatter them into the paged caches.
+ *   k_dev, v_dev        bf16 [T][Hkv][D]; row t starts at t * src_token_stride
+ *                       elements (so K and V may be slices of a fused QKV
+ *                       projection output)
+ *   slot_mapping_dev    int64 [T]; slot < 0 skips the token
+ *   k_cache_dev, v_cache_dev  caches in the layouts above
+ *   kv_dtype            KVQ_KV_FP8_E4M3: code = E4M3(fp32(x) / scale) with an
+ *                       IEEE fp32 division (the scale multiplies a code value
+ *                       to give the real value, [CAL]); KVQ_KV_BF16: bit copy
+ *                       (scales ignored)
+ *   k_scale, v_scale    per-layer scales from kvq_calibrate (> 0, finite)
+ * Bytes of slots not written are left unchanged.  T == 0 is a no-op. */
+int kvq_cache_write(const void* k_dev, const void* v_dev, int64_t src_token_stride,
+                    const int64_t* slot_mapping_dev, int T, int Hkv, int D,
+                    void* k_cache_dev, void* v_cache_dev, int num_blocks, int block_size,
+                    int kv_dtype, float k_scale, float v_scale, void* hip_stream);
+
+/* ---- decode attention ----------------------------------------------------
+ * [RUN26]: each generated token reads the whole KV cache, so decode is a scan
+ * of the cache; the FP8 speed-up needs the dequantization fused into the
+ * attention kernel, and accuracy needs fp32 accumulation at both levels.
+ *
+ * For every sequence b and query head h (KV head g = h / (Hq / Hkv)), with
+ * L = seq_lens_dev[b] tokens, token t at physical block
+ * block_tables_dev[b * max_blocks_per_seq + t / block_size]:
+ *   s_t = sm_scale * sum_d q[b][h][d] * dequant(K[t][g][d])
+ *   out[b][h][:] = sum_t exp(s_t - max s) dequant(V[t][g][:]) / sum_t exp(s_t - max s)
+ * with dequant = code value * k_scale (v_scale) for FP8 and the bf16 value for
+ * BF16; out = 0 when L == 0.  Accumulation is fp32 throughout: per-split
+ * online softmax partials (m, l, acc[D]) and an fp32 log-sum-exp merge.
+ *   q_dev              bf16 [B][Hq][D]
+ *   block_tables_dev   int32 [B][max_blocks_per_seq]; entries past a sequence's
+ *                      last block are not read
+ *   seq_lens_dev       int32 [B]
+ *   max_seq_len        host upper bound of seq_lens (sizes the grid; no
+ *                      device-to-host copy happens); must be
+ *                      <= max_blocks_per_seq * block_size
+ *   out_dev            [B][Hq][D], bf16 or fp32 per out_dtype
+ *   workspace_dev      >= kvq_decode_workspace_bytes(...) bytes, 16-B aligned,
+ *                      contents on entry irrelevant
+ * Supported: D in {64, 128, 256}, block_size 16, 1 <= Hq / Hkv <= 16. */
+size_t kvq_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_seq_len, int block_size);
+
+int kvq_paged_decode_attn(const void* q_dev, const void* k_cache_dev, const void* v_cache_dev,
+                          int kv_dtype, const int32_t* block_tables_dev, int max_blocks_per_seq,
+                          const int32_t* seq_lens_dev, int max_seq_len,
+                          int B, int Hq, int Hkv, int D, int block_size, int num_blocks,
+                          float k_scale, float v_scale, float sm_scale,
+                          void* out_dev, int out_dtype,
+                          void* workspace_dev, size_t workspace_bytes, void* hip_stream);
+
+/* As kvq_paged_decode_attn with an explicit kernel family (kvq_attn_impl) and
+ * split length in tokens (a positive multiple of 64; 0 = automatic).  Used to
+ * compare kernels; results agree within fp32 summation order. */
+size_t kvq_decode_workspace_bytes_ex(int B, int Hq, int Hkv, int D, int max_seq_len, int block_size,
+                                     int split_tokens);
+int kvq_paged_decode_attn_ex(const void* q_dev, const void* k_cache_dev, const void* v_cache_dev,
+                             int kv_dtype, const int32_t* block_tables_dev, int max_blocks_per_seq,
+                             const int32_t* seq_lens_dev, int max_seq_len,
+                             int B, int Hq, int Hkv, int D, int block_size, int num_blocks,
+                             float k_scale, float v_scale, float sm_scale,
+                             void* out_dev, int out_dtype,
+                             void* workspace_dev, size_t workspace_bytes, void* hip_stream,
+                             int impl, int split_tokens);
+
+/* Split length (tokens) the automatic plan picks for this shape. */
+int kvq_decode_plan_split_tokens(int B, int Hkv, int max_seq_len, int block_size);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVQ_H */

@@ -47,6 +47,7 @@ def lib() -> ctypes.CDLL:
         sig = {
             "kvqo_e4m3_value": (D, [U8]),
             "kvqo_e4m3_encode": (U8, [F]),
+            "kvqo_e4m3_encode_array": (None, [P, P, I64]),
             "kvqo_bf16_to_float": (F, [U16]),
             "kvqo_e4m3_quantize": (U8, [U16, F]),
             "kvqo_e2m1_value": (D, [U8]),
@@ -98,6 +99,14 @@ def e4m3_table() -> np.ndarray:
 
 def e4m3_encode(y: float) -> int:
     return lib().kvqo_e4m3_encode(y)
+
+
+def e4m3_encode_array(y) -> np.ndarray:
+    """Brute-force encode of every element of a float32 array."""
+    a = np.ascontiguousarray(np.asarray(y, dtype=np.float32).reshape(-1))
+    out = np.zeros(a.size, dtype=np.uint8)
+    lib().kvqo_e4m3_encode_array(_ptr(a), _ptr(out), a.size)
+    return out
 
 
 def e4m3_quantize(x_bf16_bits: int, scale: float) -> int:

@@ -29,21 +29,33 @@ double kvqo_e4m3_value(uint8_t code) {
     return s ? -mag : mag;
 }
 
+/* values of the 127 non-negative finite codes 0x00..0x7E, filled once */
+static double g_e4m3_pos[0x7F];
+static pthread_once_t g_e4m3_once = PTHREAD_ONCE_INIT;
+static void fill_e4m3_pos(void) {
+    for (int c = 0; c <= 0x7E; ++c) g_e4m3_pos[c] = kvqo_e4m3_value((uint8_t)c);
+}
+
 uint8_t kvqo_e4m3_encode(float y) {
     uint8_t sign = signbit(y) ? 0x80 : 0x00;
     if (isnan(y)) return (uint8_t)(0x7F | sign);
     double a = fabs((double)y);
     if (a > 448.0) return (uint8_t)(0x7E | sign); /* saturate (Inf too) */
+    pthread_once(&g_e4m3_once, fill_e4m3_pos);
     int best = 0;
     double best_d = INFINITY;
     for (int c = 0; c <= 0x7E; ++c) {             /* all non-negative finite codes */
-        double d = fabs(kvqo_e4m3_value((uint8_t)c) - a);
+        double d = fabs(g_e4m3_pos[c] - a);
         if (d < best_d || (d == best_d && (c & 1) == 0)) {
             best = c;
             best_d = d;
         }
     }
     return (uint8_t)(best | sign);
+}
+
+void kvqo_e4m3_encode_array(const float* y, uint8_t* codes, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) codes[i] = kvqo_e4m3_encode(y[i]);
 }
 
 float kvqo_bf16_to_float(uint16_t bits) {

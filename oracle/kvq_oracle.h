@@ -51,6 +51,9 @@ double kvqo_e4m3_value(uint8_t code);
  * kept, so negative values that round to zero give 0x80. */
 uint8_t kvqo_e4m3_encode(float y);
 
+/* kvqo_e4m3_encode over an array. */
+void kvqo_e4m3_encode_array(const float* y, uint8_t* codes, int64_t n);
+
 /* bf16 bit pattern -> fp32 (exact). */
 float kvqo_bf16_to_float(uint16_t bits);
 

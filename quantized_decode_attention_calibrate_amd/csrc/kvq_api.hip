@@ -1,0 +1,211 @@
+// kvq_api.hip -- the C ABI of libkvq.so (declared in include/kvq.h).
+//
+// Every entry point validates its host arguments before touching HIP, so an
+// invalid call enqueues nothing and returns a status; device work is enqueued
+// asynchronously on the caller's stream.  The library allocates nothing.
+#include <math.h>
+#include <stdint.h>
+
+#include "kvq.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+
+// Work-groups one decode launch aims for: 4 per CU on MI355X's 256 CUs (16
+// waves per CU), enough in-flight loads to cover HBM latency.
+constexpr int kTargetWorkGroups = 1024;
+constexpr int kMinSplitTokens = 512;
+
+size_t decode_workspace_bytes(int B, int Hq, int D, int num_splits) {
+    return (size_t)B * Hq * num_splits * (size_t)(D + 2) * sizeof(float);
+}
+
+DecodePlan plan_decode(int B, int Hkv, int max_seq_len, int split_tokens_request) {
+    DecodePlan p;
+    int split = split_tokens_request;
+    if (split <= 0) {
+        const int64_t units = (int64_t)(B > 0 ? B : 1) * (Hkv > 0 ? Hkv : 1);
+        int64_t per_unit = (kTargetWorkGroups + units - 1) / units;
+        if (per_unit < 1) per_unit = 1;
+        int64_t s = ((int64_t)max_seq_len + per_unit - 1) / per_unit;
+        s = (s + kChunkTokens - 1) / kChunkTokens * kChunkTokens;
+        if (s < kMinSplitTokens) s = kMinSplitTokens;
+        if (s > kMaxSplitTokens) s = kMaxSplitTokens;
+        split = (int)s;
+    }
+    p.split_tokens = split;
+    int S = (max_seq_len + split - 1) / split;
+    p.num_splits = S < 1 ? 1 : S;
+    return p;
+}
+
+}  // namespace kvq
+
+using namespace kvq;
+
+static thread_local int g_last_hip_error = 0;
+
+static int hip_status(hipError_t e) {
+    if (e == hipSuccess) return KVQ_OK;
+    g_last_hip_error = (int)e;
+    return KVQ_EHIP;
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+static bool supported_d(int D) { return D == 64 || D == 128 || D == 256; }
+static bool good_scale(float s) { return isfinite(s) && s > 0.0f; }
+
+extern "C" {
+
+const char* kvq_strerror(int status) {
+    switch (status) {
+        case KVQ_OK: return "ok";
+        case KVQ_EINVAL: return "invalid argument";
+        case KVQ_EUNSUPPORTED: return "unsupported shape or option";
+        case KVQ_EWORKSPACE: return "workspace too small";
+        case KVQ_EHIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+int kvq_last_hip_error(void) { return g_last_hip_error; }
+
+int kvq_abi_version(void) { return KVQ_ABI_VERSION; }
+
+int kvq_e4m3_encode_f32(const float* y_dev, uint8_t* codes_dev, int64_t n, void* hip_stream) {
+    if (n < 0) return KVQ_EINVAL;
+    if (n == 0) return KVQ_OK;
+    if (!y_dev || !codes_dev) return KVQ_EINVAL;
+    return hip_status(launch_e4m3_encode(y_dev, codes_dev, n, (hipStream_t)hip_stream));
+}
+
+int kvq_e4m3_decode(const uint8_t* codes_dev, void* out_dev, int out_kind, int64_t n, void* hip_stream) {
+    if (n < 0 || out_kind < 0 || out_kind > 2) return KVQ_EINVAL;
+    if (n == 0) return KVQ_OK;
+    if (!codes_dev || !out_dev) return KVQ_EINVAL;
+    return hip_status(launch_e4m3_decode(codes_dev, out_dev, out_kind, n, (hipStream_t)hip_stream));
+}
+
+int kvq_amax_bf16(const void* x_dev, int64_t rows, int64_t cols, int64_t row_stride, float* amax_dev,
+                  void* hip_stream) {
+    if (rows < 0 || cols < 0 || !amax_dev) return KVQ_EINVAL;
+    if (rows == 0 || cols == 0) return KVQ_OK;
+    if (!x_dev || row_stride < cols) return KVQ_EINVAL;
+    if (((cols & 7) == 0 && (row_stride & 7) == 0) && !aligned16(x_dev)) return KVQ_EINVAL;
+    return hip_status(launch_amax_bf16(x_dev, rows, cols, row_stride, amax_dev, (hipStream_t)hip_stream));
+}
+
+int kvq_calibrate(const float* amax_host, float* scale_host, int n) {
+    if (n < 0 || (n > 0 && (!amax_host || !scale_host))) return KVQ_EINVAL;
+    for (int i = 0; i < n; ++i)
+        if (!(amax_host[i] >= 0.0f) || isinf(amax_host[i])) return KVQ_EINVAL;
+    for (int i = 0; i < n; ++i) {
+        double s = (double)amax_host[i] * 1.05 / 448.0;
+        scale_host[i] = (float)(s > 1e-12 ? s : 1e-12);
+    }
+    return KVQ_OK;
+}
+
+int kvq_cache_write(const void* k_dev, const void* v_dev, int64_t src_token_stride,
+                    const int64_t* slot_mapping_dev, int T, int Hkv, int D, void* k_cache_dev,
+                    void* v_cache_dev, int num_blocks, int block_size, int kv_dtype, float k_scale,
+                    float v_scale, void* hip_stream) {
+    if (T < 0 || Hkv <= 0 || num_blocks <= 0) return KVQ_EINVAL;
+    if (kv_dtype != KVQ_KV_BF16 && kv_dtype != KVQ_KV_FP8_E4M3) return KVQ_EINVAL;
+    if (!supported_d(D) || block_size != kBlockSize) return KVQ_EUNSUPPORTED;
+    if (kv_dtype == KVQ_KV_FP8_E4M3 && (!good_scale(k_scale) || !good_scale(v_scale))) return KVQ_EINVAL;
+    if (T == 0) return KVQ_OK;
+    if (!k_dev || !v_dev || !slot_mapping_dev || !k_cache_dev || !v_cache_dev) return KVQ_EINVAL;
+    if (src_token_stride < (int64_t)Hkv * D || (src_token_stride & 7) != 0) return KVQ_EINVAL;
+    if (!aligned16(k_dev) || !aligned16(v_dev) || !aligned16(k_cache_dev) || !aligned16(v_cache_dev))
+        return KVQ_EINVAL;
+    return hip_status(launch_cache_write(k_dev, v_dev, src_token_stride, slot_mapping_dev, T, Hkv, D,
+                                         k_cache_dev, v_cache_dev, block_size, kv_dtype, k_scale, v_scale,
+                                         (hipStream_t)hip_stream));
+}
+
+int kvq_decode_plan_split_tokens(int B, int Hkv, int max_seq_len, int block_size) {
+    (void)block_size;
+    if (B < 0 || Hkv <= 0 || max_seq_len < 0) return KVQ_EINVAL;
+    return plan_decode(B, Hkv, max_seq_len, 0).split_tokens;
+}
+
+size_t kvq_decode_workspace_bytes_ex(int B, int Hq, int Hkv, int D, int max_seq_len, int block_size,
+                                     int split_tokens) {
+    (void)block_size;
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || max_seq_len < 0) return 0;
+    if (split_tokens < 0 || split_tokens % kChunkTokens != 0 || split_tokens > kMaxSplitTokens) return 0;
+    DecodePlan p = plan_decode(B, Hkv, max_seq_len, split_tokens);
+    return decode_workspace_bytes(B, Hq, D, p.num_splits);
+}
+
+size_t kvq_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_seq_len, int block_size) {
+    return kvq_decode_workspace_bytes_ex(B, Hq, Hkv, D, max_seq_len, block_size, 0);
+}
+
+int kvq_paged_decode_attn_ex(const void* q_dev, const void* k_cache_dev, const void* v_cache_dev, int kv_dtype,
+                             const int32_t* block_tables_dev, int max_blocks_per_seq, const int32_t* seq_lens_dev,
+                             int max_seq_len, int B, int Hq, int Hkv, int D, int block_size, int num_blocks,
+                             float k_scale, float v_scale, float sm_scale, void* out_dev, int out_dtype,
+                             void* workspace_dev, size_t workspace_bytes, void* hip_stream, int impl,
+                             int split_tokens) {
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_seq_len < 0)
+        return KVQ_EINVAL;
+    if (Hq % Hkv != 0) return KVQ_EINVAL;
+    if (kv_dtype != KVQ_KV_BF16 && kv_dtype != KVQ_KV_FP8_E4M3) return KVQ_EINVAL;
+    if (out_dtype != KVQ_OUT_BF16 && out_dtype != KVQ_OUT_F32) return KVQ_EINVAL;
+    if (impl < KVQ_IMPL_AUTO || impl > KVQ_IMPL_MFMA) return KVQ_EINVAL;
+    if (split_tokens < 0 || split_tokens % kChunkTokens != 0 || split_tokens > kMaxSplitTokens)
+        return KVQ_EINVAL;
+    if (!supported_d(D) || block_size != kBlockSize) return KVQ_EUNSUPPORTED;
+    const int G = Hq / Hkv;
+    if (G > 16) return KVQ_EUNSUPPORTED;
+    if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * block_size) return KVQ_EINVAL;
+    if (!isfinite(sm_scale)) return KVQ_EINVAL;
+    if (kv_dtype == KVQ_KV_FP8_E4M3 && (!good_scale(k_scale) || !good_scale(v_scale))) return KVQ_EINVAL;
+    if (B == 0) return KVQ_OK;
+    if (!q_dev || !k_cache_dev || !v_cache_dev || !block_tables_dev || !seq_lens_dev || !out_dev ||
+        !workspace_dev)
+        return KVQ_EINVAL;
+    if (!aligned16(q_dev) || !aligned16(k_cache_dev) || !aligned16(v_cache_dev) || !aligned16(out_dev) ||
+        !aligned16(workspace_dev))
+        return KVQ_EINVAL;
+    const DecodePlan plan = plan_decode(B, Hkv, max_seq_len, split_tokens);
+    const size_t need = decode_workspace_bytes(B, Hq, D, plan.num_splits);
+    if (workspace_bytes < need) return KVQ_EWORKSPACE;
+    if (impl == KVQ_IMPL_AUTO) impl = KVQ_IMPL_MFMA;
+
+    const bool fp8 = kv_dtype == KVQ_KV_FP8_E4M3;
+    DecodeArgs a;
+    a.q = (const uint16_t*)q_dev;
+    a.k_cache = (const uint8_t*)k_cache_dev;
+    a.v_cache = (const uint8_t*)v_cache_dev;
+    a.block_tables = block_tables_dev;
+    a.seq_lens = seq_lens_dev;
+    a.ws_ml = (float*)workspace_dev;
+    a.ws_acc = (float*)workspace_dev + (size_t)B * Hq * plan.num_splits * 2;
+    a.out = out_dev;
+    a.max_blocks = max_blocks_per_seq;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = G;
+    a.split_tokens = plan.split_tokens;
+    a.num_splits = plan.num_splits;
+    a.qk_scale_log2 = (float)((double)sm_scale * (fp8 ? (double)k_scale : 1.0) * 1.4426950408889634);
+    a.v_scale = fp8 ? v_scale : 1.0f;
+    a.out_f32 = out_dtype == KVQ_OUT_F32;
+    return hip_status(launch_decode(a, B, D, fp8, impl, (hipStream_t)hip_stream));
+}
+
+int kvq_paged_decode_attn(const void* q_dev, const void* k_cache_dev, const void* v_cache_dev, int kv_dtype,
+                          const int32_t* block_tables_dev, int max_blocks_per_seq, const int32_t* seq_lens_dev,
+                          int max_seq_len, int B, int Hq, int Hkv, int D, int block_size, int num_blocks,
+                          float k_scale, float v_scale, float sm_scale, void* out_dev, int out_dtype,
+                          void* workspace_dev, size_t workspace_bytes, void* hip_stream) {
+    return kvq_paged_decode_attn_ex(q_dev, k_cache_dev, v_cache_dev, kv_dtype, block_tables_dev,
+                                    max_blocks_per_seq, seq_lens_dev, max_seq_len, B, Hq, Hkv, D, block_size,
+                                    num_blocks, k_scale, v_scale, sm_scale, out_dev, out_dtype, workspace_dev,
+                                    workspace_bytes, hip_stream, KVQ_IMPL_AUTO, 0);
+}
+
+}  // extern "C"

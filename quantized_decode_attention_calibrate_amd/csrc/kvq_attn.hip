@@ -1,0 +1,554 @@
+// kvq_attn.hip -- single-token split-K paged decode attention with the
+// dequantization fused into the attention kernel, and the cross-split merge.
+//
+// The Run 26 video description (Skildcore, "KV Cache Precision") states the
+// problem these kernels answer: each generated token reads the whole KV
+// cache, so decode is a bandwidth-bound scan; halving the bytes with FP8 gave
+// no speed-up on its hardware because no fused dequant kernel existed
+// (chapter "The Missing Fused Dequant Kernel"); accuracy needs fp32
+// accumulation at two levels ("two-level FP32 accumulation").  Here the
+// levels are the per-split online softmax (fp32 m, l, acc) and the fp32
+// log-sum-exp merge across splits.
+//
+// Work decomposition (MI355X: 256 CUs, wave64): one work-group of 4 waves per
+// (split s, KV head g, sequence b).  A split is a fixed range of logical
+// tokens (a multiple of 64), so results do not depend on physical block
+// placement.  Each wave walks 64-token chunks (4 blocks of 16) of the split
+// round-robin; the 4 waves merge through LDS and write one fp32 partial
+// (m, l, acc[G][D]) per head to the workspace; the merge kernel combines the
+// splits and applies v_scale.
+//
+// Two kernel families:
+//   MFMA: QK^T on v_mfma_f32_16x16x32_bf16 (E4M3 -> bf16 is exact; bf16 x
+//         bf16 products are exact in fp32) and PV on v_mfma_f32_16x16x32_f16
+//         (E4M3 -> f16 is exact; each fp32 softmax weight is split into f16
+//         hi + lo parts, two MFMAs on the same V operand).  The G query heads
+//         sharing a KV head are the 16-wide N dimension (padded), so each K/V
+//         byte is read once per KV head.
+//   VALU: plain fp32 FMAs with Q staged in LDS; the comparator.
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kMaxSplitBlocks = kMaxSplitTokens / kBlockSize;
+
+// LDS layout shared by both families (dynamic shared memory):
+//   int   blk[kMaxSplitBlocks]          physical block ids of this split
+//   float m[kWaves][16], l[kWaves][16]  per-wave softmax state per head
+//   float acc[kWaves][G][D]             per-wave unnormalised outputs
+//   (VALU only) float q[G][D], p[kWaves][16][16]
+__host__ __device__ constexpr int lds_merge_floats(int G, int D) { return kWaves * 32 + kWaves * G * D; }
+
+// Stage the physical block ids of logical blocks [lb0, lb0 + n) into LDS,
+// clamping logical blocks past the sequence to its last block (those tokens
+// are masked; the clamp only keeps every address inside the cache).
+__device__ __forceinline__ void stage_block_ids(int* s_blk, const int32_t* bt_row, int lb0, int n,
+                                                int last_lb) {
+    for (int i = threadIdx.x; i < n; i += kThreads) {
+        int lb = min(lb0 + i, last_lb);
+        s_blk[i] = bt_row[lb];
+    }
+}
+
+// Merge the 4 waves' (m, l, acc) held in LDS and write this split's partial.
+__device__ __forceinline__ void merge_waves_and_store(const DecodeArgs& a, const float* s_m, const float* s_l,
+                                                      const float* s_acc, int b, int g, int s, int D) {
+    const int G = a.G;
+    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+        const int h = idx / D, d = idx - h * D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w * 16 + h]);
+        float acc = 0.f, l = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float mw = s_m[w * 16 + h];
+            const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+            acc += f * s_acc[(w * G + h) * D + d];
+            l += f * s_l[w * 16 + h];
+        }
+        const int64_t hq = (int64_t)b * a.Hq + (int64_t)g * G + h;
+        a.ws_acc[(hq * a.num_splits + s) * D + d] = acc;
+        if (d == 0) {
+            a.ws_ml[(hq * a.num_splits + s) * 2 + 0] = M;
+            a.ws_ml[(hq * a.num_splits + s) * 2 + 1] = l;
+        }
+    }
+}
+
+// =============================================================================
+// MFMA family
+// =============================================================================
+//
+// Lane roles (lane = 16 * grp + n, grp = lane / 16, n = lane % 16); a chunk is
+// logical blocks c0 .. c0+3 of the split (chunk blocks 0..3).
+//   QK tile i (i = 0..3), MFMA C = K_tile x Q^T:
+//     A row m = n  <- token (chunk block n/4, offset 4i + n%4); the lane loads
+//                     16 contiguous K bytes (dims 64j + 16grp .. +15) per
+//                     64-dim slice j, i.e. two 8-wide k-steps
+//     B col n      <- query head g*G + n (zero when n >= G), same dims
+//     C            -> lane holds S[token (chunk block grp, offset 4i + r)][head n], r = 0..3
+//   so after the 4 tiles each lane holds all 16 scores of chunk block grp for
+//   head n, which is exactly the P^T operand layout PV needs.
+//   PV, dim tile dt (D/16 tiles), half hh (tokens 8hh..8hh+7), MFMA C = V^T x P^T:
+//     A row m = n  <- dim 16dt + n of chunk block grp: the V block is dim-major,
+//                     so the lane's 16 contiguous bytes are that dim's 16 tokens
+//     B col n      <- weights of head n for the same 8 tokens
+//     C            -> acc[dt]: lane holds out[dim 16dt + 4grp + r][head n]
+template <int D, bool FP8>
+__global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
+    constexpr int KJ = D / 64;   // 64-dim slices
+    constexpr int DT = D / 16;   // PV dim tiles
+    extern __shared__ float lds[];
+    int* s_blk = reinterpret_cast<int*>(lds);
+    float* s_m = lds + kMaxSplitBlocks;
+    float* s_l = s_m + kWaves * 16;
+    float* s_acc = s_l + kWaves * 16;
+
+    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int L = a.seq_lens[b];
+    const int tok_begin = s * a.split_tokens;
+    if (tok_begin >= L) return;
+    const int tok_end = min(L, tok_begin + a.split_tokens);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int n = lane & 15, grp = lane >> 4;
+    const int G = a.G;
+    const int Hkv = a.Hkv;
+
+    const int lb0 = tok_begin / kBlockSize;
+    const int n_chunks = (tok_end - tok_begin + kChunkTokens - 1) / kChunkTokens;
+    stage_block_ids(s_blk, a.block_tables + (int64_t)b * a.max_blocks, lb0, n_chunks * 4,
+                    (L + kBlockSize - 1) / kBlockSize - 1);
+
+    // Q^T operands: k-step (j, hh) covers dims 64j + 16grp + 8hh .. +7
+    bf16x8 qb[2 * KJ];
+    {
+        const int h = g * G + n;
+        const uint16_t* qrow = a.q + ((int64_t)b * a.Hq + h) * D;
+#pragma unroll
+        for (int j = 0; j < KJ; ++j)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                u32x4 w = {0u, 0u, 0u, 0u};
+                if (n < G) w = *reinterpret_cast<const u32x4*>(qrow + 64 * j + 16 * grp + 8 * hh);
+                qb[2 * j + hh] = __builtin_bit_cast(bf16x8, w);
+            }
+    }
+    __syncthreads();
+
+    f32x4 acc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+    const float c = a.qk_scale_log2;
+
+    for (int ch = wave; ch < n_chunks; ch += kWaves) {
+        const int chunk_tok = tok_begin + ch * kChunkTokens;
+        const int pk = s_blk[ch * 4 + (n >> 2)];   // block for this lane's K rows
+        const int pv = s_blk[ch * 4 + grp];        // block for this lane's V rows
+
+        // ---- loads: K rows for 4 tiles, V^T rows for DT dim tiles --------
+        constexpr int KW = FP8 ? 1 : 2;  // 16-byte words per (tile, slice)
+        u32x4 kw[4][KJ][KW];
+        u32x4 vw[DT][KW];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int off = 4 * i + (n & 3);
+            const int64_t row = (((int64_t)pk * Hkv + g) * kBlockSize + off) * D;
+#pragma unroll
+            for (int j = 0; j < KJ; ++j)
+#pragma unroll
+                for (int x = 0; x < KW; ++x) {
+                    if constexpr (FP8)
+                        kw[i][j][x] = *reinterpret_cast<const u32x4*>(a.k_cache + row + 64 * j + 16 * grp);
+                    else
+                        kw[i][j][x] = *reinterpret_cast<const u32x4*>(
+                            reinterpret_cast<const uint16_t*>(a.k_cache) + row + 64 * j + 16 * grp + 8 * x);
+                }
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const int64_t vrow = (((int64_t)pv * Hkv + g) * D + 16 * dt + n) * kBlockSize;
+#pragma unroll
+            for (int x = 0; x < KW; ++x) {
+                if constexpr (FP8)
+                    vw[dt][x] = *reinterpret_cast<const u32x4*>(a.v_cache + vrow);
+                else
+                    vw[dt][x] = *reinterpret_cast<const u32x4*>(
+                        reinterpret_cast<const uint16_t*>(a.v_cache) + vrow + 8 * x);
+            }
+        }
+
+        // ---- S = K Q^T ---------------------------------------------------
+        float sv[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f32x4 st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < KJ; ++j)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    bf16x8 ka;
+                    if constexpr (FP8)
+                        ka = e4m3x8_to_bf16(kw[i][j][0][2 * hh], kw[i][j][0][2 * hh + 1]);
+                    else
+                        ka = __builtin_bit_cast(bf16x8, kw[i][j][hh]);
+                    st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[2 * j + hh], st, 0, 0, 0);
+                }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sv[4 * i + r] = st[r] * c;
+        }
+
+        // ---- online softmax over this chunk (head n, chunk block grp) -----
+        const int valid = tok_end - (chunk_tok + 16 * grp);  // tokens of block grp in range
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {  // sv[4i + r] is token offset 4i + r of block grp
+            if (e >= valid) sv[e] = -INFINITY;
+            mloc = fmaxf(mloc, sv[e]);
+        }
+        mloc = fmaxf(mloc, shfl_xor(mloc, 16));
+        mloc = fmaxf(mloc, shfl_xor(mloc, 32));
+        const float m_new = fmaxf(m_run, mloc);
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+
+        // Weights in the PV operand layout (half hh = tokens 8hh..8hh+7).  They
+        // are scaled by 2^15 (exp2 offset) so they sit in f16's normal range,
+        // and split into hi + lo 16-bit parts so the two PV MFMAs on the same
+        // exact V operand reproduce the fp32 weight to ~2^-21.  The scale is
+        // common to acc and l and cancels in the final division.
+        const float m_off = m_new - 15.0f;
+        float psum = 0.f;
+        f16x8 pfh[2], pfl[2];
+        bf16x8 pbh[2], pbl[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const float p0 = fast_exp2(sv[8 * hh + 2 * e2] - m_off);
+                const float p1 = fast_exp2(sv[8 * hh + 2 * e2 + 1] - m_off);
+                psum += p0 + p1;
+                if constexpr (FP8) {
+                    const f16x2 h = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(p0, p1));
+                    const f16x2 l = __builtin_bit_cast(
+                        f16x2, __builtin_amdgcn_cvt_pkrtz(p0 - (float)h[0], p1 - (float)h[1]));
+                    pfh[hh][2 * e2] = h[0];
+                    pfh[hh][2 * e2 + 1] = h[1];
+                    pfl[hh][2 * e2] = l[0];
+                    pfl[hh][2 * e2 + 1] = l[1];
+                } else {
+                    const __bf16 h0 = (__bf16)p0, h1 = (__bf16)p1;
+                    pbh[hh][2 * e2] = h0;
+                    pbh[hh][2 * e2 + 1] = h1;
+                    pbl[hh][2 * e2] = (__bf16)(p0 - (float)h0);
+                    pbl[hh][2 * e2 + 1] = (__bf16)(p1 - (float)h1);
+                }
+            }
+        }
+        l_run = l_run * alpha + psum;
+
+        // zero V bytes of tokens past the end (their weight is 0, the bytes may be anything)
+        if (valid < 16) {
+            // word w of 16-byte word x holds tokens 4w.. (FP8) or 8x + 2w.. (BF16)
+            u32x4 keep[KW];
+#pragma unroll
+            for (int x = 0; x < KW; ++x)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    uint32_t mask = 0;
+                    if constexpr (FP8) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (4 * w + e < valid) mask |= 0xFFu << (8 * e);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 2; ++e)
+                            if (8 * x + 2 * w + e < valid) mask |= 0xFFFFu << (16 * e);
+                    }
+                    keep[x][w] = mask;
+                }
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int x = 0; x < KW; ++x) vw[dt][x] &= keep[x];
+        }
+
+        // ---- acc = alpha * acc + V^T P^T ------------------------------------
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            acc[dt] *= alpha;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                if constexpr (FP8) {
+                    f16x8 va = e4m3x8_to_f16(vw[dt][0][2 * hh], vw[dt][0][2 * hh + 1]);
+                    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pfh[hh], acc[dt], 0, 0, 0);
+                    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pfl[hh], acc[dt], 0, 0, 0);
+                } else {
+                    bf16x8 va = __builtin_bit_cast(bf16x8, vw[dt][hh]);
+                    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pbh[hh], acc[dt], 0, 0, 0);
+                    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pbl[hh], acc[dt], 0, 0, 0);
+                }
+            }
+        }
+    }
+
+    // ---- wave results -> LDS ---------------------------------------------------
+    l_run += shfl_xor(l_run, 16);
+    l_run += shfl_xor(l_run, 32);
+    if (grp == 0) {
+        s_m[wave * 16 + n] = m_run;
+        s_l[wave * 16 + n] = l_run;
+    }
+    if (n < G) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s_acc[(wave * G + n) * D + 16 * dt + 4 * grp + r] = acc[dt][r];
+    }
+    __syncthreads();
+    merge_waves_and_store(a, s_m, s_l, s_acc, b, g, s, D);
+}
+
+// =============================================================================
+// VALU family (comparator)
+// =============================================================================
+// Per wave iteration: one 16-token block.  QK: lane = (token off = lane/4,
+// quarter qq = lane%4 of D); partial dots over D/4 dims with Q from LDS, quad
+// reduction.  PV: lane = dim (D/64 dims per lane) over the dim-major V block,
+// weights broadcast through LDS.
+template <int D, bool FP8>
+__global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeArgs a) {
+    constexpr int QD = D / 4;    // dims per lane in QK
+    constexpr int VD = D / 64;   // dims per lane in PV
+    constexpr int MAXG = 16;
+    extern __shared__ float lds[];
+    int* s_blk = reinterpret_cast<int*>(lds);
+    float* s_m = lds + kMaxSplitBlocks;
+    float* s_l = s_m + kWaves * 16;
+    float* s_acc = s_l + kWaves * 16;
+    const int G = a.G;
+    float* s_q = s_acc + kWaves * G * D;         // [G][D]
+    float* s_p = s_q + G * D;                    // [kWaves][16 heads][16 tokens]
+
+    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int L = a.seq_lens[b];
+    const int tok_begin = s * a.split_tokens;
+    if (tok_begin >= L) return;
+    const int tok_end = min(L, tok_begin + a.split_tokens);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int Hkv = a.Hkv;
+
+    const int lb0 = tok_begin / kBlockSize;
+    const int n_blocks = (tok_end - tok_begin + kBlockSize - 1) / kBlockSize;
+    stage_block_ids(s_blk, a.block_tables + (int64_t)b * a.max_blocks, lb0, n_blocks,
+                    (L + kBlockSize - 1) / kBlockSize - 1);
+    for (int i = threadIdx.x; i < G * D; i += kThreads) {
+        const int h = i / D, d = i - h * D;
+        s_q[i] = bits_f32((uint32_t)a.q[((int64_t)b * a.Hq + g * G + h) * D + d] << 16);
+    }
+    __syncthreads();
+
+    const int off = lane >> 2, qq = lane & 3;
+    float* my_p = s_p + wave * 256;
+    float m_run[MAXG], l_run[MAXG], acc[MAXG][VD];
+#pragma unroll
+    for (int h = 0; h < MAXG; ++h) {
+        m_run[h] = -INFINITY;
+        l_run[h] = 0.f;
+#pragma unroll
+        for (int e = 0; e < VD; ++e) acc[h][e] = 0.f;
+    }
+    const float c = a.qk_scale_log2;
+
+    for (int blk = wave; blk < n_blocks; blk += kWaves) {
+        const int phys = s_blk[blk];
+        const int valid = tok_end - (tok_begin + blk * kBlockSize);
+        // K slice: QD elements of token `off`
+        float kf[QD];
+        {
+            const int64_t row = (((int64_t)phys * Hkv + g) * kBlockSize + off) * D + qq * QD;
+            if constexpr (FP8) {
+#pragma unroll
+                for (int x = 0; x < QD / 16; ++x) {
+                    u32x4 w = *reinterpret_cast<const u32x4*>(a.k_cache + row + 16 * x);
+#pragma unroll
+                    for (int y = 0; y < 4; ++y) {
+                        f32x2 lo = e4m3x2_to_f32(w[y], false), hi = e4m3x2_to_f32(w[y], true);
+                        kf[16 * x + 4 * y + 0] = lo[0];
+                        kf[16 * x + 4 * y + 1] = lo[1];
+                        kf[16 * x + 4 * y + 2] = hi[0];
+                        kf[16 * x + 4 * y + 3] = hi[1];
+                    }
+                }
+            } else {
+                const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.k_cache);
+#pragma unroll
+                for (int x = 0; x < QD / 8; ++x) {
+                    u32x4 w = *reinterpret_cast<const u32x4*>(kc + row + 8 * x);
+#pragma unroll
+                    for (int y = 0; y < 4; ++y) {
+                        kf[8 * x + 2 * y] = bf16_lo(w[y]);
+                        kf[8 * x + 2 * y + 1] = bf16_hi(w[y]);
+                    }
+                }
+            }
+        }
+        // V^T rows: dims lane + 64e, 16 tokens each
+        float vf[VD][16];
+#pragma unroll
+        for (int e = 0; e < VD; ++e) {
+            const int64_t vrow = (((int64_t)phys * Hkv + g) * D + lane + 64 * e) * kBlockSize;
+            if constexpr (FP8) {
+                u32x4 w = *reinterpret_cast<const u32x4*>(a.v_cache + vrow);
+#pragma unroll
+                for (int y = 0; y < 4; ++y) {
+                    f32x2 lo = e4m3x2_to_f32(w[y], false), hi = e4m3x2_to_f32(w[y], true);
+                    vf[e][4 * y + 0] = lo[0];
+                    vf[e][4 * y + 1] = lo[1];
+                    vf[e][4 * y + 2] = hi[0];
+                    vf[e][4 * y + 3] = hi[1];
+                }
+            } else {
+                const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.v_cache);
+#pragma unroll
+                for (int x = 0; x < 2; ++x) {
+                    u32x4 w = *reinterpret_cast<const u32x4*>(vc + vrow + 8 * x);
+#pragma unroll
+                    for (int y = 0; y < 4; ++y) {
+                        vf[e][8 * x + 2 * y] = bf16_lo(w[y]);
+                        vf[e][8 * x + 2 * y + 1] = bf16_hi(w[y]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < 16; ++t)
+                if (t >= valid) vf[e][t] = 0.f;
+        }
+
+#pragma unroll
+        for (int h = 0; h < MAXG; ++h) {
+            if (h >= G) break;
+            const float* qh = s_q + h * D + qq * QD;
+            float part = 0.f;
+#pragma unroll
+            for (int x = 0; x < QD; x += 4) {
+                const f32x4 qv = *reinterpret_cast<const f32x4*>(qh + x);
+                part += qv[0] * kf[x] + qv[1] * kf[x + 1] + qv[2] * kf[x + 2] + qv[3] * kf[x + 3];
+            }
+            part += shfl_xor(part, 1);
+            part += shfl_xor(part, 2);
+            float sh = (off < valid) ? part * c : -INFINITY;
+            float bm = sh;
+            bm = fmaxf(bm, shfl_xor(bm, 4));
+            bm = fmaxf(bm, shfl_xor(bm, 8));
+            bm = fmaxf(bm, shfl_xor(bm, 16));
+            bm = fmaxf(bm, shfl_xor(bm, 32));
+            const float m_new = fmaxf(m_run[h], bm);
+            const float alpha = fast_exp2(m_run[h] - m_new);
+            m_run[h] = m_new;
+            const float p = fast_exp2(sh - m_new);
+            l_run[h] = l_run[h] * alpha + (qq == 0 ? p : 0.f);
+            if (qq == 0) my_p[h * 16 + off] = p;
+#pragma unroll
+            for (int e = 0; e < VD; ++e) acc[h][e] *= alpha;
+        }
+        // weights written by this wave are read back by the same wave only
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int h = 0; h < MAXG; ++h) {
+            if (h >= G) break;
+            const float* ph = my_p + h * 16;
+#pragma unroll
+            for (int t = 0; t < 16; t += 4) {
+                const f32x4 pv4 = *reinterpret_cast<const f32x4*>(ph + t);
+#pragma unroll
+                for (int e = 0; e < VD; ++e)
+                    acc[h][e] += pv4[0] * vf[e][t] + pv4[1] * vf[e][t + 1] + pv4[2] * vf[e][t + 2] +
+                                 pv4[3] * vf[e][t + 3];
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+
+#pragma unroll
+    for (int h = 0; h < MAXG; ++h) {
+        if (h >= G) break;
+        float l = l_run[h];
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) l += shfl_xor(l, o);
+        if (lane == 0) {
+            s_m[wave * 16 + h] = m_run[h];
+            s_l[wave * 16 + h] = l;
+        }
+#pragma unroll
+        for (int e = 0; e < VD; ++e) s_acc[(wave * G + h) * D + lane + 64 * e] = acc[h][e];
+    }
+    __syncthreads();
+    merge_waves_and_store(a, s_m, s_l, s_acc, b, g, s, D);
+}
+
+// =============================================================================
+// cross-split merge: out = v_scale * sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s
+// =============================================================================
+template <int D>
+__global__ void __launch_bounds__(D) merge_splits_kernel(DecodeArgs a) {
+    const int hq = blockIdx.x;            // b * Hq + h
+    const int b = hq / a.Hq;
+    const int d = threadIdx.x;
+    const int L = a.seq_lens[b];
+    const int S = (L + a.split_tokens - 1) / a.split_tokens;  // splits with tokens
+    float result = 0.f;
+    if (S > 0) {
+        const float* ml = a.ws_ml + (int64_t)hq * a.num_splits * 2;
+        const float* ac = a.ws_acc + (int64_t)hq * a.num_splits * D + d;
+        float M = -INFINITY;
+        for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * s]);
+        float num = 0.f, den = 0.f;
+        for (int s = 0; s < S; ++s) {
+            const float f = fast_exp2(ml[2 * s] - M);
+            num += f * ac[(int64_t)s * D];
+            den += f * ml[2 * s + 1];
+        }
+        result = num / den * a.v_scale;
+    }
+    const int64_t o = (int64_t)hq * D + d;
+    if (a.out_f32)
+        reinterpret_cast<float*>(a.out)[o] = result;
+    else
+        reinterpret_cast<uint16_t*>(a.out)[o] = (uint16_t)f32_to_bf16_rne(result);
+}
+
+template <int D, bool FP8>
+static hipError_t launch_family(const DecodeArgs& a, int B, int impl, hipStream_t st) {
+    dim3 grid(a.num_splits, a.Hkv, B);
+    size_t lds = sizeof(float) * (kMaxSplitBlocks + lds_merge_floats(a.G, D));
+    if (impl == 2) {
+        hipLaunchKernelGGL((decode_mfma_kernel<D, FP8>), grid, dim3(kThreads), lds, st, a);
+    } else {
+        lds += sizeof(float) * (a.G * D + kWaves * 256);
+        hipLaunchKernelGGL((decode_valu_kernel<D, FP8>), grid, dim3(kThreads), lds, st, a);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((merge_splits_kernel<D>), dim3(B * a.Hq), dim3(D), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int B, int D, bool fp8, int impl, hipStream_t st) {
+    switch (D) {
+        case 64: return fp8 ? launch_family<64, true>(a, B, impl, st) : launch_family<64, false>(a, B, impl, st);
+        case 128: return fp8 ? launch_family<128, true>(a, B, impl, st) : launch_family<128, false>(a, B, impl, st);
+        case 256: return fp8 ? launch_family<256, true>(a, B, impl, st) : launch_family<256, false>(a, B, impl, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace kvq

@@ -1,0 +1,89 @@
+// kvq_device.h -- device-side building blocks shared by the libkvq kernels
+// (gfx950 only): the OCP E4M3 codec on the native conversion instructions,
+// vector types for MFMA operands, and wave-level helpers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kE4M3Max = 448.0f;   // OCP E4M3 largest finite magnitude
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ uint32_t f32_bits(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ float bits_f32(uint32_t x) { return __builtin_bit_cast(float, x); }
+
+// bf16 bit pattern -> fp32 (exact)
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return bits_f32(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return bits_f32(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet)
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
+    uint32_t u = f32_bits(x);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// ---- E4M3 encode: saturating round-to-nearest-even ---------------------
+// The native v_cvt_pk_fp8_f32 rounds to nearest even; clamping to +-448 first
+// makes overflow and Inf saturate instead of producing NaN.  NaN is mapped
+// explicitly to 0x7F carrying the input's sign.  The clamp keeps -0.0, so a
+// negative value that rounds to zero encodes as 0x80.
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+    float c = __builtin_fminf(__builtin_fmaxf(y, -kE4M3Max), kE4M3Max);
+    uint32_t code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xFFu;
+    if (__builtin_isnan(y)) code = 0x7Fu | ((f32_bits(y) >> 24) & 0x80u);
+    return code;
+}
+
+// Encode 4 floats into one little-endian word of E4M3 codes.
+__device__ __forceinline__ uint32_t e4m3_encode4(float a, float b, float c, float d) {
+    return e4m3_encode(a) | (e4m3_encode(b) << 8) | (e4m3_encode(c) << 16) | (e4m3_encode(d) << 24);
+}
+
+// ---- E4M3 decode (exact) -------------------------------------------------
+// Two codes from the low (hi = false) or high (hi = true) half of a word.
+__device__ __forceinline__ f32x2 e4m3x2_to_f32(uint32_t w, bool hi) {
+    return hi ? __builtin_amdgcn_cvt_pk_f32_fp8(w, true) : __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+}
+__device__ __forceinline__ f16x2 e4m3x2_to_f16(uint32_t w, bool hi) {
+    return hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true)
+              : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+}
+__device__ __forceinline__ bf16x2 e4m3x2_to_bf16(uint32_t w, bool hi) {
+    return hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+              : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+}
+
+// 8 codes (two words) -> 8 halves / 8 bf16 (MFMA operand order = byte order)
+__device__ __forceinline__ f16x8 e4m3x8_to_f16(uint32_t w0, uint32_t w1) {
+    f16x2 a = e4m3x2_to_f16(w0, false), b = e4m3x2_to_f16(w0, true);
+    f16x2 c = e4m3x2_to_f16(w1, false), d = e4m3x2_to_f16(w1, true);
+    return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
+    bf16x2 a = e4m3x2_to_bf16(w0, false), b = e4m3x2_to_bf16(w0, true);
+    bf16x2 c = e4m3x2_to_bf16(w1, false), d = e4m3x2_to_bf16(w1, true);
+    return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// ---- wave helpers ----------------------------------------------------------
+__device__ __forceinline__ float shfl_xor(float v, int mask) {
+    int lane = __lane_id();
+    return bits_f32((uint32_t)__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, (int)f32_bits(v)));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace kvq

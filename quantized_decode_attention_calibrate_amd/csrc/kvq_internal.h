@@ -1,0 +1,51 @@
+// kvq_internal.h -- host-side declarations shared by the libkvq translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvq {
+
+// Split-K plan for one decode call (host-computed from host-known bounds only).
+struct DecodePlan {
+    int split_tokens;  // tokens per work-group, multiple of 64
+    int num_splits;    // ceil(max_seq_len / split_tokens)
+};
+
+// Largest split the kernels stage block ids for (LDS table of 512 ids).
+constexpr int kMaxSplitTokens = 8192;
+constexpr int kChunkTokens = 64;   // tokens per wave iteration (4 blocks of 16)
+constexpr int kBlockSize = 16;
+
+struct DecodeArgs {
+    const uint16_t* q;           // bf16 [B][Hq][D]
+    const uint8_t* k_cache;      // FP8 or BF16 paged K cache (bytes)
+    const uint8_t* v_cache;      // FP8 or BF16 paged V cache (bytes, dim-major blocks)
+    const int32_t* block_tables; // [B][max_blocks]
+    const int32_t* seq_lens;     // [B]
+    float* ws_ml;                // [B][Hq][S][2] : running max (log2 units), sum of weights
+    float* ws_acc;               // [B][Hq][S][D] : unnormalised weighted sum of V codes
+    void* out;                   // [B][Hq][D]
+    int max_blocks;
+    int Hq, Hkv, G;
+    int split_tokens, num_splits;
+    float qk_scale_log2;         // sm_scale * k_scale * log2(e)
+    float v_scale;               // applied once in the merge
+    int out_f32;
+};
+
+size_t decode_workspace_bytes(int B, int Hq, int D, int num_splits);
+DecodePlan plan_decode(int B, int Hkv, int max_seq_len, int split_tokens_request);
+
+hipError_t launch_amax_bf16(const void* x, int64_t rows, int64_t cols, int64_t stride, float* amax,
+                            hipStream_t st);
+hipError_t launch_e4m3_encode(const float* y, uint8_t* codes, int64_t n, hipStream_t st);
+hipError_t launch_e4m3_decode(const uint8_t* codes, void* out, int kind, int64_t n, hipStream_t st);
+hipError_t launch_cache_write(const void* k, const void* v, int64_t src_stride, const int64_t* slots, int T,
+                              int Hkv, int D, void* k_cache, void* v_cache, int bs, int kv_dtype,
+                              float k_scale, float v_scale, hipStream_t st);
+// impl: 1 = VALU, 2 = MFMA.  B is the grid's z extent.
+hipError_t launch_decode(const DecodeArgs& a, int B, int D, bool fp8, int impl, hipStream_t st);
+
+}  // namespace kvq

@@ -1,0 +1,174 @@
+"""ctypes binding of libkvq.so (include/kvq.h): same names, argument
+marshalling only.  Every computation runs in the library's HIP kernels; torch
+supplies device memory and the current stream.  There is no fallback: if the
+library is missing or fails to load, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # must be loaded first: libkvq binds to the HIP runtime torch ships
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkvq.so")
+
+KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_EWORKSPACE, KVQ_EHIP = 0, -1, -2, -3, -4
+KVQ_KV_BF16, KVQ_KV_FP8_E4M3 = 0, 1
+KVQ_OUT_BF16, KVQ_OUT_F32 = 0, 1
+KVQ_IMPL_AUTO, KVQ_IMPL_VALU, KVQ_IMPL_MFMA = 0, 1, 2
+BLOCK_SIZE = 16
+
+
+class KvqError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = f"{fn}: {kvq_strerror(status)} ({status})"
+        if status == KVQ_EHIP:
+            msg += f", hipError {_lib.kvq_last_hip_error()}"
+        super().__init__(msg)
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m quantized_decode_attention_calibrate_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, I64, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    sig = {
+        "kvq_strerror": (ctypes.c_char_p, [I]),
+        "kvq_last_hip_error": (I, []),
+        "kvq_abi_version": (I, []),
+        "kvq_e4m3_encode_f32": (I, [P, P, I64, P]),
+        "kvq_e4m3_decode": (I, [P, P, I, I64, P]),
+        "kvq_amax_bf16": (I, [P, I64, I64, I64, P, P]),
+        "kvq_calibrate": (I, [P, P, I]),
+        "kvq_cache_write": (I, [P, P, I64, P, I, I, I, P, P, I, I, I, F, F, P]),
+        "kvq_decode_workspace_bytes": (SZ, [I, I, I, I, I, I]),
+        "kvq_decode_workspace_bytes_ex": (SZ, [I, I, I, I, I, I, I]),
+        "kvq_decode_plan_split_tokens": (I, [I, I, I, I]),
+        "kvq_paged_decode_attn": (I, [P, P, P, I, P, I, P, I, I, I, I, I, I, I, F, F, F, P, I, P, SZ, P]),
+        "kvq_paged_decode_attn_ex": (I, [P, P, P, I, P, I, P, I, I, I, I, I, I, I, F, F, F, P, I, P, SZ, P,
+                                         I, I]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    return L
+
+
+_lib = _load()
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(fn: str, status: int) -> None:
+    if status != KVQ_OK:
+        raise KvqError(fn, status)
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def kvq_strerror(status: int) -> str:
+    return _lib.kvq_strerror(status).decode()
+
+
+def kvq_abi_version() -> int:
+    return _lib.kvq_abi_version()
+
+
+def kvq_e4m3_encode_f32(y: torch.Tensor, codes: torch.Tensor, stream=None) -> None:
+    assert y.dtype == torch.float32 and codes.dtype == torch.uint8 and y.is_contiguous() and codes.is_contiguous()
+    assert codes.numel() >= y.numel()
+    _check("kvq_e4m3_encode_f32", _lib.kvq_e4m3_encode_f32(_ptr(y), _ptr(codes), y.numel(), _stream(stream)))
+
+
+def kvq_e4m3_decode(codes: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    kind = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}[out.dtype]
+    assert codes.dtype == torch.uint8 and codes.is_contiguous() and out.is_contiguous()
+    assert out.numel() >= codes.numel()
+    _check("kvq_e4m3_decode", _lib.kvq_e4m3_decode(_ptr(codes), _ptr(out), kind, codes.numel(), _stream(stream)))
+
+
+def kvq_amax_bf16(x: torch.Tensor, amax: torch.Tensor, stream=None) -> None:
+    """Running max |x| into amax (fp32 device scalar, caller-initialised).
+    x: bf16, viewed as rows of its last-but-flattened layout: a 2-D or 3-D
+    tensor whose last dims are contiguous and whose first dim may be strided."""
+    assert x.dtype == torch.bfloat16 and amax.dtype == torch.float32
+    x2 = x.reshape(x.shape[0], -1) if x.dim() > 2 else x
+    assert x2.stride(1) == 1
+    _check("kvq_amax_bf16", _lib.kvq_amax_bf16(_ptr(x2), x2.shape[0], x2.shape[1], x2.stride(0), _ptr(amax),
+                                                _stream(stream)))
+
+
+def kvq_calibrate(amax) -> list:
+    """Host-only: per-layer scales from observed maxima (list of floats)."""
+    vals = [float(a) for a in amax]
+    n = len(vals)
+    src = (ctypes.c_float * n)(*vals)
+    dst = (ctypes.c_float * n)()
+    _check("kvq_calibrate", _lib.kvq_calibrate(ctypes.addressof(src), ctypes.addressof(dst), n))
+    return list(dst)
+
+
+def new_caches(kv_dtype: int, num_blocks: int, Hkv: int, D: int, device="cuda"):
+    """Uninitialised K and V caches in the library's layouts."""
+    dt = torch.uint8 if kv_dtype == KVQ_KV_FP8_E4M3 else torch.bfloat16
+    k = torch.empty((num_blocks, Hkv, BLOCK_SIZE, D), dtype=dt, device=device)
+    v = torch.empty((num_blocks, Hkv, D, BLOCK_SIZE), dtype=dt, device=device)
+    return k, v
+
+
+def kvq_cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, k_cache: torch.Tensor,
+                    v_cache: torch.Tensor, kv_dtype: int, k_scale: float = 1.0, v_scale: float = 1.0,
+                    stream=None) -> None:
+    """k, v: bf16 [T][Hkv][D] (token dim may be strided); slot_mapping int64 [T]."""
+    assert k.dtype == torch.bfloat16 and v.dtype == torch.bfloat16 and slot_mapping.dtype == torch.int64
+    T, Hkv, D = k.shape
+    assert v.shape == k.shape and k.stride(0) == v.stride(0) and k.stride(2) == 1 and k.stride(1) == D
+    assert slot_mapping.shape == (T,) and slot_mapping.is_contiguous()
+    num_blocks = k_cache.shape[0]
+    _check("kvq_cache_write", _lib.kvq_cache_write(
+        _ptr(k), _ptr(v), k.stride(0), _ptr(slot_mapping), T, Hkv, D, _ptr(k_cache), _ptr(v_cache),
+        num_blocks, BLOCK_SIZE, kv_dtype, k_scale, v_scale, _stream(stream)))
+
+
+def kvq_decode_workspace_bytes(B: int, Hq: int, Hkv: int, D: int, max_seq_len: int, split_tokens: int = 0) -> int:
+    return _lib.kvq_decode_workspace_bytes_ex(B, Hq, Hkv, D, max_seq_len, BLOCK_SIZE, split_tokens)
+
+
+def kvq_decode_plan_split_tokens(B: int, Hkv: int, max_seq_len: int) -> int:
+    return _lib.kvq_decode_plan_split_tokens(B, Hkv, max_seq_len, BLOCK_SIZE)
+
+
+def new_workspace(B: int, Hq: int, Hkv: int, D: int, max_seq_len: int, split_tokens: int = 0, device="cuda"):
+    n = kvq_decode_workspace_bytes(B, Hq, Hkv, D, max_seq_len, split_tokens)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def kvq_paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_dtype: int,
+                          block_tables: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, Hkv: int,
+                          k_scale: float, v_scale: float, sm_scale: float, out: torch.Tensor,
+                          workspace: torch.Tensor, impl: int = KVQ_IMPL_AUTO, split_tokens: int = 0,
+                          stream=None) -> None:
+    """q bf16 [B][Hq][D]; out bf16 or fp32 [B][Hq][D]; block_tables int32 [B][max_blocks]; seq_lens int32 [B]."""
+    B, Hq, D = q.shape
+    assert q.dtype == torch.bfloat16 and q.is_contiguous() and out.is_contiguous() and out.shape == q.shape
+    assert block_tables.dtype == torch.int32 and block_tables.is_contiguous() and block_tables.shape[0] == B
+    assert seq_lens.dtype == torch.int32 and seq_lens.shape == (B,)
+    out_dtype = {torch.bfloat16: KVQ_OUT_BF16, torch.float32: KVQ_OUT_F32}[out.dtype]
+    _check("kvq_paged_decode_attn", _lib.kvq_paged_decode_attn_ex(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), kv_dtype, _ptr(block_tables), block_tables.shape[1],
+        _ptr(seq_lens), max_seq_len, B, Hq, Hkv, D, BLOCK_SIZE, k_cache.shape[0], k_scale, v_scale, sm_scale,
+        _ptr(out), out_dtype, _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream),
+        impl, split_tokens))

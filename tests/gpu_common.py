@@ -1,0 +1,121 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI and
+the oracle on the same seeded inputs.  Nothing here computes an expected value:
+expected values come only from ``oracle``."""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from quantized_decode_attention_calibrate_amd import workloads
+
+# Attention tolerance against the oracle's fp64 attention over the same
+# dequantized values, applied to the fp32 epilogue (out_dtype F32).
+MAX_ABS = 2e-3
+REL_L2 = 1e-3
+
+
+def gpu_or_skip():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def kvq():
+    from quantized_decode_attention_calibrate_amd import kvq as K  # raises if the library is missing
+    return K
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def bits_u8(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.uint8).numpy()
+
+
+def gpu_calibrate(K, x: torch.Tensor) -> float:
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    K.kvq_amax_bf16(x, amax)
+    return K.kvq_calibrate([float(amax.item())])[0]
+
+
+class Setup:
+    """A workload on the GPU with its caches written by kvq_cache_write: the
+    prefill (all tokens but each sequence's newest) in one call, then the
+    decode-step write of the newest token per sequence."""
+
+    def __init__(self, w: workloads.Workload, kv_dtype: int, sentinel: int = 0xFF, scales=None):
+        K = kvq()
+        self.K, self.w, self.kv_dtype = K, w, kv_dtype
+        dev = "cuda"
+        self.q = w.q.to(dev)
+        self.k = w.k.to(dev)
+        self.v = w.v.to(dev)
+        self.bt = w.block_tables.to(dev)
+        self.sl = torch.tensor(w.seq_lens, dtype=torch.int32, device=dev)
+        if scales is not None:
+            self.ks, self.vs = scales
+        elif kv_dtype == K.KVQ_KV_FP8_E4M3:
+            src_k = w.calib_k.to(dev) if w.calib_k is not None else self.k
+            src_v = w.calib_v.to(dev) if w.calib_v is not None else self.v
+            self.ks, self.vs = gpu_calibrate(K, src_k), gpu_calibrate(K, src_v)
+        else:
+            self.ks, self.vs = 1.0, 1.0
+        self.kc, self.vc = K.new_caches(kv_dtype, w.num_blocks, w.Hkv, w.D, device=dev)
+        # unwritten slots hold the sentinel byte (0xFF: an FP8 and a bf16 NaN)
+        self.kc.view(torch.uint8).fill_(sentinel)
+        self.vc.view(torch.uint8).fill_(sentinel)
+        slots = w.slot_mapping.to(dev)
+        pre = w.prefill_slots().to(dev)
+        if w.T:
+            K.kvq_cache_write(self.k, self.v, pre, self.kc, self.vc, kv_dtype, self.ks, self.vs)
+            rows = w.last_token_rows()
+            rows = rows[rows >= 0].to(dev)
+            if rows.numel():
+                K.kvq_cache_write(self.k[rows], self.v[rows], slots[rows].contiguous(), self.kc, self.vc,
+                                  kv_dtype, self.ks, self.vs)
+        self.sm_scale = float(np.float32(1.0 / math.sqrt(w.D)))
+
+    def attend(self, out_dtype=torch.float32, impl=0, split_tokens=0, q=None):
+        K, w = self.K, self.w
+        q = self.q if q is None else q
+        out = torch.empty(w.B, w.Hq, w.D, dtype=out_dtype, device="cuda")
+        ws = K.new_workspace(w.B, w.Hq, w.Hkv, w.D, w.max_seq_len, split_tokens)
+        K.kvq_paged_decode_attn(q, self.kc, self.vc, self.kv_dtype, self.bt, self.sl, w.max_seq_len, w.Hkv,
+                                self.ks, self.vs, self.sm_scale, out, ws, impl=impl, split_tokens=split_tokens)
+        torch.cuda.synchronize()
+        return out
+
+    def oracle_caches(self, sentinel: int = 0xFF):
+        w = self.w
+        kvd = oracle.KV_FP8 if self.kv_dtype == 1 else oracle.KV_BF16
+        fill = sentinel if kvd == oracle.KV_FP8 else (sentinel | (sentinel << 8))
+        kc, vc = oracle.new_caches(kvd, w.num_blocks, w.Hkv, w.D, w.block_size, fill=fill)
+        oracle.cache_write(w.k, w.v, w.slot_mapping, kc, vc, kvd, self.ks, self.vs)
+        return kc, vc
+
+    def oracle_attention(self, kc, vc, units=None, nthreads=8):
+        w = self.w
+        kvd = oracle.KV_FP8 if self.kv_dtype == 1 else oracle.KV_BF16
+        return oracle.decode_attn(w.q, kc, vc, kvd, w.block_tables, w.seq_lens, w.Hkv, w.block_size,
+                                  self.ks, self.vs, self.sm_scale, units=units, nthreads=nthreads)
+
+
+def attention_errors(got: np.ndarray, ref: np.ndarray):
+    diff = got.astype(np.float64) - ref
+    max_abs = float(np.abs(diff).max()) if diff.size else 0.0
+    den = float(np.sqrt((ref ** 2).sum()))
+    rel = float(np.sqrt((diff ** 2).sum()) / den) if den > 0 else float(np.sqrt((diff ** 2).sum()))
+    return max_abs, rel
+
+
+def assert_attention_close(got: np.ndarray, ref: np.ndarray, what: str = ""):
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    max_abs, rel = attention_errors(got, ref)
+    say(f"  {what}: max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    assert max_abs <= MAX_ABS and rel <= REL_L2, (what, max_abs, rel)

@@ -1,0 +1,140 @@
+"""GPU parity for the codec, amax and cache write: bit-exact against the oracle.
+
+- decode of all 256 E4M3 codes through each conversion the kernels use
+  (fp32, f16, bf16) equals the oracle's table;
+- the device encoder equals the oracle's brute-force encoder on every bf16
+  bit pattern, every rounding midpoint +-2 ulp, specials, and 2M random fp32
+  patterns;
+- amax equals the oracle's max |x| (running max, strided rows, NaN);
+- kvq_cache_write (FP8 and BF16) produces byte-identical caches to the
+  oracle's cache write, including unwritten bytes, skipped slots, a strided
+  source, and every bf16 pattern quantized at several scales.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from quantized_decode_attention_calibrate_amd import workloads
+
+from gpu_common import Setup, bits_u8, gpu_or_skip, kvq, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def K():
+    gpu_or_skip()
+    return kvq()
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16, torch.bfloat16])
+def test_decode_all_codes(K, dtype):
+    say(f"decode all codes -> {dtype}")
+    codes = torch.arange(256, dtype=torch.uint8, device="cuda")
+    out = torch.empty(256, dtype=dtype, device="cuda")
+    K.kvq_e4m3_decode(codes, out)
+    got = out.float().cpu().double().numpy()
+    want = oracle.e4m3_table()
+    nan = np.isnan(want)
+    assert (np.isnan(got) == nan).all()
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))  # -0 for 0x80
+
+
+def encode_inputs():
+    rng = np.random.default_rng(1234)
+    bf = (np.arange(65536, dtype=np.uint32) << 16).view(np.float32)
+    t = oracle.e4m3_table()[:0x7F]
+    mids = ((t[:-1] + t[1:]) / 2).astype(np.float32)
+    near = [mids]
+    for k in (1, 2):
+        up, dn = mids.copy(), mids.copy()
+        for _ in range(k):
+            up = np.nextafter(up, np.float32(np.inf), dtype=np.float32)
+            dn = np.nextafter(dn, np.float32(-np.inf), dtype=np.float32)
+        near += [up, dn]
+    near = np.concatenate(near)
+    special = np.array([0.0, -0.0, np.inf, -np.inf, np.nan, 448.0, 464.0, 465.0, 1e30, 1e-45, -1e-45,
+                        2 ** -10, 1.5 * 2 ** -9], dtype=np.float32)
+    rnd = rng.integers(0, 2 ** 32, size=2_000_000, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    return np.concatenate([bf, near, -near, special, rnd]).astype(np.float32)
+
+
+def test_encode_matches_oracle(K):
+    y = encode_inputs()
+    say(f"encode {y.size} values")
+    codes = torch.empty(y.size, dtype=torch.uint8, device="cuda")
+    K.kvq_e4m3_encode_f32(torch.from_numpy(y).cuda(), codes)
+    got = codes.cpu().numpy()
+    want = oracle.e4m3_encode_array(y)
+    bad = np.where(got != want)[0]
+    assert bad.size == 0, [(float(y[i]), hex(int(got[i])), hex(int(want[i]))) for i in bad[:10]]
+
+
+def test_amax(K):
+    w = workloads.make("tiny", seed=0)
+    k = w.k.cuda()
+    amax = torch.zeros(1, device="cuda")
+    K.kvq_amax_bf16(k, amax)
+    assert amax.item() == oracle.amax_bf16(w.k)
+    # running max over a second call, strided rows (a slice of a fused [T][2*Hkv*D] buffer)
+    fused = torch.cat([w.v, w.k * 3], dim=1).cuda()   # [T][2*Hkv][D]
+    vk = fused[:, w.Hkv:, :]
+    K.kvq_amax_bf16(vk, amax)
+    assert amax.item() == max(oracle.amax_bf16(w.k), oracle.amax_bf16((w.k * 3)))
+    # odd sizes take the scalar path
+    odd = w.k.reshape(-1)[:1001].reshape(7, 143).cuda()
+    a2 = torch.zeros(1, device="cuda")
+    K.kvq_amax_bf16(odd, a2)
+    assert a2.item() == oracle.amax_bf16(odd.cpu())
+    nanx = k.clone()
+    nanx[5, 1, 3] = float("nan")
+    a3 = torch.zeros(1, device="cuda")
+    K.kvq_amax_bf16(nanx, a3)
+    assert np.isnan(a3.item())
+
+
+@pytest.mark.parametrize("kv", [0, 1])
+@pytest.mark.parametrize("name,seed,lens,shape", [
+    ("tiny", 0, None, None),
+    ("mixed64", 3, [1, 17, 300, 0, 65], dict(Hq=8, Hkv=2, D=128)),
+    ("agents126k", 4, [100, 33], dict(Hq=12, Hkv=2, D=256, calib_tokens=64)),
+])
+def test_cache_write_matches_oracle(K, kv, name, seed, lens, shape):
+    say(f"cache write {name} kv={kv}")
+    w = workloads.make(name, seed=seed, seq_lens=lens, shape=shape)
+    s = Setup(w, kv)
+    kc, vc = s.oracle_caches()
+    assert np.array_equal(bits_u8(s.kc), kc.view(np.uint8))
+    assert np.array_equal(bits_u8(s.vc), vc.view(np.uint8))
+
+
+def test_cache_write_skips_and_strided_source(K):
+    w = workloads.make("tiny", seed=9, seq_lens=[50, 31])
+    fused = torch.cat([w.k, w.v, w.k], dim=1)                  # [T][3*Hkv][D]
+    k_view, v_view = fused[:, :w.Hkv, :], fused[:, w.Hkv:2 * w.Hkv, :]
+    sm = w.slot_mapping.clone()
+    sm[::4] = -1
+    ks, vs = 0.03125, 0.0117
+    kc, vc = K.new_caches(1, w.num_blocks, w.Hkv, w.D)
+    kc.fill_(0x5A)
+    vc.fill_(0x5A)
+    K.kvq_cache_write(k_view.cuda(), v_view.cuda(), sm.cuda(), kc, vc, 1, ks, vs)
+    okc, ovc = oracle.new_caches(oracle.KV_FP8, w.num_blocks, w.Hkv, w.D, 16, fill=0x5A)
+    oracle.cache_write(w.k, w.v, sm, okc, ovc, oracle.KV_FP8, ks, vs)
+    assert np.array_equal(bits_u8(kc), okc) and np.array_equal(bits_u8(vc), ovc)
+
+
+@pytest.mark.parametrize("scale", [1.0, 2.0 ** -7, 0.0117, 3.3, 1e-12, 448.0])
+def test_cache_write_every_bf16_pattern(K, scale):
+    # 65536 bf16 patterns as K (and reversed as V) of 512 tokens x 2 heads x 64 dims
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    k = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).reshape(512, 2, 64)
+    v = torch.from_numpy(bits[::-1].view(np.int16).copy()).view(torch.bfloat16).reshape(512, 2, 64)
+    slots = torch.randperm(512, generator=torch.Generator().manual_seed(5))
+    kc, vc = K.new_caches(1, 32, 2, 64)
+    K.kvq_cache_write(k.cuda(), v.cuda(), slots.cuda(), kc, vc, 1, scale, scale)
+    okc, ovc = oracle.new_caches(oracle.KV_FP8, 32, 2, 64, 16)
+    oracle.cache_write(k, v, slots, okc, ovc, oracle.KV_FP8, scale, scale)
+    assert np.array_equal(bits_u8(kc), okc) and np.array_equal(bits_u8(vc), ovc)
