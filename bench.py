@@ -56,6 +56,13 @@ def step_bytes(B, Hq, Hkv, D, seq_lens, kv_elem_bytes, n_new):
     return kv + table + qo, write
 
 
+def layers_for(w, kv_elem_bytes, cap=12):
+    """Enough distinct layer caches that one rotation exceeds 1 GiB (beyond the
+    256 MB last-level cache), at most `cap`."""
+    per_layer = sum(w.seq_lens) * w.Hkv * w.D * 2 * kv_elem_bytes
+    return max(2, min(cap, -(-(1 << 30) // max(per_layer, 1))))
+
+
 class Layers:
     """R layer caches of one workload, written by the library."""
 
@@ -128,10 +135,33 @@ def time_steps(torch, layers, steps, warmup, impl=0):
     return step_ms, sum(attn_ms) / len(attn_ms), attn_ms[len(attn_ms) // 2]
 
 
-def cpu_baseline(w, ks, vs, n_kv_heads=1):
+def measure_workload(torch, K, name, steps, warmup):
+    """FP8 and BF16 attention-call time for one workload (compact record)."""
+    from quantized_decode_attention_calibrate_amd import workloads
+    w = workloads.make(name, device="cuda", seed=0)
+    rec = {"B": w.B, "max_seq_len": w.max_seq_len, "kv_tokens": sum(w.seq_lens), "Hq": w.Hq, "Hkv": w.Hkv,
+           "D": w.D, "split_tokens": K.kvq_decode_plan_split_tokens(w.B, w.Hkv, w.max_seq_len)}
+    for kv, tag, eb in ((K.KVQ_KV_FP8_E4M3, "fp8", 1), (K.KVQ_KV_BF16, "bf16", 2)):
+        L = Layers(K, w, kv, layers_for(w, eb), "cuda")
+        step_ms, attn_ms, _ = time_steps(torch, L, steps, warmup)
+        attn_b, write_b = step_bytes(w.B, w.Hq, w.Hkv, w.D, w.seq_lens, eb, w.B)
+        rec[tag] = {"attn_us": round(attn_ms * 1e3, 2), "attn_gbps": round(attn_b / (attn_ms * 1e-3) / 1e9, 1),
+                    "pct_of_hbm_peak": round(100 * attn_b / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1),
+                    "step_us": round(step_ms * 1e3, 2), "layers_rotated": L.R}
+        del L
+        torch.cuda.empty_cache()
+    rec["fp8_over_bf16_attn_time"] = round(rec["fp8"]["attn_us"] / rec["bf16"]["attn_us"], 3)
+    rec["fp8_kv_tokens_per_s"] = round(rec["kv_tokens"] / (rec["fp8"]["attn_us"] * 1e-6), 1)
+    del w
+    torch.cuda.empty_cache()
+    return rec
+
+
+def cpu_baseline(w, ks, vs, n_kv_heads):
     """The oracle (fp64 C, brute-force codecs) timed on this host's cores over a
     bounded sample: n_kv_heads KV heads (all their G query heads) of the
-    workload; scaled to the full step by the number of KV heads."""
+    workload's decode attention; scaled to the full step by Hkv / n_kv_heads.
+    The oracle's own cache write (untimed) supplies its FP8 cache."""
     import numpy as np
     import oracle
     import torch
@@ -172,7 +202,9 @@ def main():
     ap.add_argument("--layers", type=int, default=12)
     ap.add_argument("--impl", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-compare", action="store_true", help="skip the BF16 and other-family runs")
+    ap.add_argument("--no-compare", action="store_true", help="skip the BF16 comparator")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the per-workload table (agents126k, mixed64, nvfp4_131k)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this path has no multi-GPU "
@@ -237,18 +269,26 @@ def main():
         result["fp8_over_bf16_attn_time"] = round(attn_ms / b_attn, 4)
         del bf, fp8_caches
         torch.cuda.empty_cache()
+    del w
+    torch.cuda.empty_cache()
+    if not args.no_other_workloads:
+        result["workloads"] = {}
+        for name in ("agents126k", "mixed64", "nvfp4_131k"):
+            print(f"[bench] workload {name}", file=sys.stderr, flush=True)
+            result["workloads"][name] = measure_workload(torch, K, name, 60, 10)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         w_cpu = workloads.make(args.workload, device="cpu", seed=0)
         amax_k = float(w_cpu.k.float().abs().max())
         amax_v = float(w_cpu.v.float().abs().max())
         ks, vs = K.kvq_calibrate([amax_k, amax_v])
-        step_s, cores, dt = cpu_baseline(w_cpu, ks, vs, n_kv_heads=1)
+        nh = w_cpu.Hkv
+        step_s, cores, dt = cpu_baseline(w_cpu, ks, vs, n_kv_heads=nh)
         result["cpu_baseline"] = {
             "value": round(attn_b / step_s / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"oracle decode attention (fp64) of 1 of {w.Hkv} KV heads (its {w.G} query heads) over "
-                      f"all {tokens} tokens, {dt:.2f} s on {cores} threads, scaled x{w.Hkv} to the full "
-                      "attention step; cache write excluded",
+            "sample": f"oracle decode attention (fp64 C) over all {w_cpu.Hkv} KV heads ({w_cpu.Hq} query heads) "
+                      f"x {tokens} tokens of one layer: {dt:.2f} s wall on {cores} threads (the step's "
+                      "attention; the cache write is excluded)",
             "kv_tokens_per_s": round(tokens / step_s, 1)}
     print(json.dumps(result), flush=True)
 

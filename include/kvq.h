@@ -152,9 +152,14 @@ int kvq_cache_write(const void* k_dev, const void* v_dev, int64_t src_token_stri
  *                      device-to-host copy happens); must be
  *                      <= max_blocks_per_seq * block_size
  *   out_dev            [B][Hq][D], bf16 or fp32 per out_dtype
- *   workspace_dev      >= kvq_decode_workspace_bytes(...) bytes, 16-B aligned,
- *                      contents on entry irrelevant
- * Supported: D in {64, 128, 256}, block_size 16, 1 <= Hq / Hkv <= 16. */
+ *   workspace_dev      >= kvq_decode_workspace_bytes(...) bytes, 16-B aligned;
+ *                      contents on entry irrelevant.  Calls that share a
+ *                      workspace must not run concurrently.
+ * Launches: the split kernel (each work-group reduces its 4 waves through LDS;
+ * a split that holds a whole sequence writes `out` directly) and, when any
+ * sequence spans two or more splits, the merge kernel for those sequences.
+ * Supported: D in {64, 128, 256}, block_size 16, 1 <= Hq / Hkv <= 16, at most
+ * 16384 splits (KVQ_EUNSUPPORTED otherwise). */
 size_t kvq_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_seq_len, int block_size);
 
 int kvq_paged_decode_attn(const void* q_dev, const void* k_cache_dev, const void* v_cache_dev,

@@ -11,13 +11,21 @@
 
 namespace kvq {
 
-// Work-groups one decode launch aims for: 4 per CU on MI355X's 256 CUs (16
-// waves per CU), enough in-flight loads to cover HBM latency.
-constexpr int kTargetWorkGroups = 1024;
+// Work-groups one decode launch aims for: one per CU on MI355X's 256 CUs.
+// Each wave keeps two 64-token chunks in flight, so 4 waves per CU cover HBM
+// latency, and fewer, longer splits keep the cross-split merge cheap (measured
+// on gfx950: 16-32 splits per sequence beat 64-128 at 65k-131k tokens).
+constexpr int kTargetWorkGroups = 256;
 constexpr int kMinSplitTokens = 512;
 
+static size_t pad256(size_t n) { return (n + 255) / 256 * 256; }
+
+size_t decode_ml_bytes(int B, int Hq, int num_splits) {
+    return pad256((size_t)B * Hq * num_splits * 2 * sizeof(float));
+}
+
 size_t decode_workspace_bytes(int B, int Hq, int D, int num_splits) {
-    return (size_t)B * Hq * num_splits * (size_t)(D + 2) * sizeof(float);
+    return decode_ml_bytes(B, Hq, num_splits) + (size_t)B * Hq * num_splits * (size_t)D * sizeof(float);
 }
 
 DecodePlan plan_decode(int B, int Hkv, int max_seq_len, int split_tokens_request) {
@@ -136,6 +144,7 @@ size_t kvq_decode_workspace_bytes_ex(int B, int Hq, int Hkv, int D, int max_seq_
     if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || max_seq_len < 0) return 0;
     if (split_tokens < 0 || split_tokens % kChunkTokens != 0 || split_tokens > kMaxSplitTokens) return 0;
     DecodePlan p = plan_decode(B, Hkv, max_seq_len, split_tokens);
+    if (p.num_splits > kMaxSplits) return 0;
     return decode_workspace_bytes(B, Hq, D, p.num_splits);
 }
 
@@ -171,6 +180,7 @@ int kvq_paged_decode_attn_ex(const void* q_dev, const void* k_cache_dev, const v
         !aligned16(workspace_dev))
         return KVQ_EINVAL;
     const DecodePlan plan = plan_decode(B, Hkv, max_seq_len, split_tokens);
+    if (plan.num_splits > kMaxSplits) return KVQ_EUNSUPPORTED;
     const size_t need = decode_workspace_bytes(B, Hq, D, plan.num_splits);
     if (workspace_bytes < need) return KVQ_EWORKSPACE;
     if (impl == KVQ_IMPL_AUTO) impl = KVQ_IMPL_MFMA;
@@ -183,7 +193,7 @@ int kvq_paged_decode_attn_ex(const void* q_dev, const void* k_cache_dev, const v
     a.block_tables = block_tables_dev;
     a.seq_lens = seq_lens_dev;
     a.ws_ml = (float*)workspace_dev;
-    a.ws_acc = (float*)workspace_dev + (size_t)B * Hq * plan.num_splits * 2;
+    a.ws_acc = (float*)((char*)a.ws_ml + decode_ml_bytes(B, Hq, plan.num_splits));
     a.out = out_dev;
     a.max_blocks = max_blocks_per_seq;
     a.Hq = Hq;

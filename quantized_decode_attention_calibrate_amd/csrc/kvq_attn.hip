@@ -53,10 +53,20 @@ __device__ __forceinline__ void stage_block_ids(int* s_blk, const int32_t* bt_ro
     }
 }
 
-// Merge the 4 waves' (m, l, acc) held in LDS and write this split's partial.
-__device__ __forceinline__ void merge_waves_and_store(const DecodeArgs& a, const float* s_m, const float* s_l,
-                                                      const float* s_acc, int b, int g, int s, int D) {
+// Merge the 4 waves' (m, l, acc) held in LDS into this split's result.  If the
+// split holds the whole sequence the result is final and goes to `out`
+// directly; otherwise it is stored as an fp32 partial for merge_splits_kernel.
+__device__ __forceinline__ void store_out(const DecodeArgs& a, int64_t o, float v) {
+    if (a.out_f32)
+        reinterpret_cast<float*>(a.out)[o] = v;
+    else
+        reinterpret_cast<uint16_t*>(a.out)[o] = (uint16_t)f32_to_bf16_rne(v);
+}
+
+__device__ __forceinline__ void finish_split(const DecodeArgs& a, const float* s_m, const float* s_l,
+                                             const float* s_acc, int b, int g, int s, int S, int D) {
     const int G = a.G;
+    const int64_t hq0 = (int64_t)b * a.Hq + (int64_t)g * G;
     for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
         const int h = idx / D, d = idx - h * D;
         float M = -INFINITY;
@@ -70,13 +80,22 @@ __device__ __forceinline__ void merge_waves_and_store(const DecodeArgs& a, const
             acc += f * s_acc[(w * G + h) * D + d];
             l += f * s_l[w * 16 + h];
         }
-        const int64_t hq = (int64_t)b * a.Hq + (int64_t)g * G + h;
-        a.ws_acc[(hq * a.num_splits + s) * D + d] = acc;
-        if (d == 0) {
-            a.ws_ml[(hq * a.num_splits + s) * 2 + 0] = M;
-            a.ws_ml[(hq * a.num_splits + s) * 2 + 1] = l;
+        if (S == 1) {
+            store_out(a, (hq0 + h) * D + d, acc * (a.v_scale / l));
+        } else {
+            a.ws_acc[((hq0 + h) * a.num_splits + s) * D + d] = acc;
+            if (d == 0) {
+                a.ws_ml[((hq0 + h) * a.num_splits + s) * 2 + 0] = M;
+                a.ws_ml[((hq0 + h) * a.num_splits + s) * 2 + 1] = l;
+            }
         }
     }
+}
+
+// A sequence with no tokens: work-group (split 0) writes zeros for its heads.
+__device__ __forceinline__ void write_empty(const DecodeArgs& a, int b, int g, int D) {
+    const int64_t hq0 = (int64_t)b * a.Hq + (int64_t)g * a.G;
+    for (int idx = threadIdx.x; idx < a.G * D; idx += kThreads) store_out(a, hq0 * D + idx, 0.f);
 }
 
 // =============================================================================
@@ -98,10 +117,186 @@ __device__ __forceinline__ void merge_waves_and_store(const DecodeArgs& a, const
 //                     so the lane's 16 contiguous bytes are that dim's 16 tokens
 //     B col n      <- weights of head n for the same 8 tokens
 //     C            -> acc[dt]: lane holds out[dim 16dt + 4grp + r][head n]
+#ifndef KVQ_MFMA_PREFETCH
+#define KVQ_MFMA_PREFETCH 1
+#endif
+
+// Raw bytes of one 64-token chunk as this lane needs them.
+template <int D, bool FP8>
+struct MfmaChunk {
+    static constexpr int KJ = D / 64;        // 64-dim slices of a K row
+    static constexpr int DT = D / 16;        // PV dim tiles
+    static constexpr int KW = FP8 ? 1 : 2;   // 16-byte words per (tile, slice) / per V row
+    u32x4 kw[4][KJ][KW];
+    u32x4 vw[DT][KW];
+};
+
+// Per-wave running softmax state of head n (lane % 16).
+template <int D>
+struct MfmaState {
+    f32x4 acc[D / 16];
+    float m_run, l_run;
+};
+
+template <int D, bool FP8>
+__device__ __forceinline__ void mfma_load(MfmaChunk<D, FP8>& c, const DecodeArgs& a, const int* s_blk, int ch,
+                                          int g, int n, int grp) {
+    using C = MfmaChunk<D, FP8>;
+    const int pk = s_blk[ch * 4 + (n >> 2)];   // block of this lane's K rows
+    const int pv = s_blk[ch * 4 + grp];        // block of this lane's V rows
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int off = 4 * i + (n & 3);
+        const int64_t row = (((int64_t)pk * a.Hkv + g) * kBlockSize + off) * D;
+#pragma unroll
+        for (int j = 0; j < C::KJ; ++j)
+#pragma unroll
+            for (int x = 0; x < C::KW; ++x) {
+                if constexpr (FP8)
+                    c.kw[i][j][x] = *reinterpret_cast<const u32x4*>(a.k_cache + row + 64 * j + 16 * grp);
+                else
+                    c.kw[i][j][x] = *reinterpret_cast<const u32x4*>(
+                        reinterpret_cast<const uint16_t*>(a.k_cache) + row + 64 * j + 16 * grp + 8 * x);
+            }
+    }
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+        const int64_t vrow = (((int64_t)pv * a.Hkv + g) * D + 16 * dt + n) * kBlockSize;
+#pragma unroll
+        for (int x = 0; x < C::KW; ++x) {
+            if constexpr (FP8)
+                c.vw[dt][x] = *reinterpret_cast<const u32x4*>(a.v_cache + vrow);
+            else
+                c.vw[dt][x] = *reinterpret_cast<const u32x4*>(
+                    reinterpret_cast<const uint16_t*>(a.v_cache) + vrow + 8 * x);
+        }
+    }
+}
+
+template <int D, bool FP8>
+__device__ __forceinline__ void mfma_process(MfmaState<D>& st, MfmaChunk<D, FP8>& c, const bf16x8* qb, float cs,
+                                             int chunk_tok, int tok_end, int grp) {
+    using C = MfmaChunk<D, FP8>;
+    // ---- S = K Q^T ---------------------------------------------------------
+    float sv[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < C::KJ; ++j)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                bf16x8 ka;
+                if constexpr (FP8)
+                    ka = e4m3x8_to_bf16(c.kw[i][j][0][2 * hh], c.kw[i][j][0][2 * hh + 1]);
+                else
+                    ka = __builtin_bit_cast(bf16x8, c.kw[i][j][hh]);
+                t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[2 * j + hh], t, 0, 0, 0);
+            }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sv[4 * i + r] = t[r] * cs;
+    }
+
+    // ---- online softmax over this chunk (head n, chunk block grp) -----------
+    const int valid = tok_end - (chunk_tok + 16 * grp);  // tokens of block grp in range
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {  // sv[4i + r] is token offset 4i + r of block grp
+        if (e >= valid) sv[e] = -INFINITY;
+        mloc = fmaxf(mloc, sv[e]);
+    }
+    mloc = fmaxf(mloc, shfl_xor(mloc, 16));
+    mloc = fmaxf(mloc, shfl_xor(mloc, 32));
+    const float m_new = fmaxf(st.m_run, mloc);
+    const float alpha = fast_exp2(st.m_run - m_new);
+    st.m_run = m_new;
+
+    // Weights in the PV operand layout (half hh = tokens 8hh..8hh+7).  They are
+    // scaled by 2^15 (exp2 offset) so they sit in f16's normal range, and split
+    // into hi + lo 16-bit parts so the two PV MFMAs on the same exact V operand
+    // reproduce the fp32 weight to ~2^-21.  The scale is common to acc and l and
+    // cancels in the final division.
+    const float m_off = m_new - 15.0f;
+    float psum = 0.f;
+    f16x8 pfh[2], pfl[2];
+    bf16x8 pbh[2], pbl[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+            const float p0 = fast_exp2(sv[8 * hh + 2 * e2] - m_off);
+            const float p1 = fast_exp2(sv[8 * hh + 2 * e2 + 1] - m_off);
+            psum += p0 + p1;
+            if constexpr (FP8) {
+                const f16x2 h = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(p0, p1));
+                const f16x2 l =
+                    __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(p0 - (float)h[0], p1 - (float)h[1]));
+                pfh[hh][2 * e2] = h[0];
+                pfh[hh][2 * e2 + 1] = h[1];
+                pfl[hh][2 * e2] = l[0];
+                pfl[hh][2 * e2 + 1] = l[1];
+            } else {
+                const __bf16 h0 = (__bf16)p0, h1 = (__bf16)p1;
+                pbh[hh][2 * e2] = h0;
+                pbh[hh][2 * e2 + 1] = h1;
+                pbl[hh][2 * e2] = (__bf16)(p0 - (float)h0);
+                pbl[hh][2 * e2 + 1] = (__bf16)(p1 - (float)h1);
+            }
+        }
+    }
+    st.l_run = st.l_run * alpha + psum;
+
+    // zero V bytes of tokens past the end (their weight is 0, the bytes may be anything)
+    if (valid < 16) {
+        // word w of 16-byte word x holds tokens 4w.. (FP8) or 8x + 2w.. (BF16)
+        u32x4 keep[C::KW];
+#pragma unroll
+        for (int x = 0; x < C::KW; ++x)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                uint32_t mask = 0;
+                if constexpr (FP8) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (4 * w + e < valid) mask |= 0xFFu << (8 * e);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 2; ++e)
+                        if (8 * x + 2 * w + e < valid) mask |= 0xFFFFu << (16 * e);
+                }
+                keep[x][w] = mask;
+            }
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+            for (int x = 0; x < C::KW; ++x) c.vw[dt][x] &= keep[x];
+    }
+
+    // ---- acc = alpha * acc + V^T P^T ----------------------------------------
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+        st.acc[dt] *= alpha;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            if constexpr (FP8) {
+                f16x8 va = e4m3x8_to_f16(c.vw[dt][0][2 * hh], c.vw[dt][0][2 * hh + 1]);
+                st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pfh[hh], st.acc[dt], 0, 0, 0);
+                st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pfl[hh], st.acc[dt], 0, 0, 0);
+            } else {
+                bf16x8 va = __builtin_bit_cast(bf16x8, c.vw[dt][hh]);
+                st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pbh[hh], st.acc[dt], 0, 0, 0);
+                st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pbl[hh], st.acc[dt], 0, 0, 0);
+            }
+        }
+    }
+}
+
 template <int D, bool FP8>
 __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
-    constexpr int KJ = D / 64;   // 64-dim slices
-    constexpr int DT = D / 16;   // PV dim tiles
+    constexpr int KJ = D / 64;
+    constexpr int DT = D / 16;
+    // two chunks in flight per wave where the registers allow it
+    constexpr bool kPrefetch = KVQ_MFMA_PREFETCH && D <= 128;
     extern __shared__ float lds[];
     int* s_blk = reinterpret_cast<int*>(lds);
     float* s_m = lds + kMaxSplitBlocks;
@@ -111,12 +306,15 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
     const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int L = a.seq_lens[b];
     const int tok_begin = s * a.split_tokens;
-    if (tok_begin >= L) return;
+    if (tok_begin >= L) {
+        if (L <= 0 && s == 0) write_empty(a, b, g, D);
+        return;
+    }
     const int tok_end = min(L, tok_begin + a.split_tokens);
+    const int S = (L + a.split_tokens - 1) / a.split_tokens;   // splits holding tokens
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n = lane & 15, grp = lane >> 4;
     const int G = a.G;
-    const int Hkv = a.Hkv;
 
     const int lb0 = tok_begin / kBlockSize;
     const int n_chunks = (tok_end - tok_begin + kChunkTokens - 1) / kChunkTokens;
@@ -139,178 +337,68 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
     }
     __syncthreads();
 
-    f32x4 acc[DT];
+    MfmaState<D> st;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
-    const float c = a.qk_scale_log2;
+    for (int dt = 0; dt < DT; ++dt) st.acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.m_run = -INFINITY;
+    st.l_run = 0.f;
+    const float cs = a.qk_scale_log2;
+    // this wave's chunks: wave, wave + 4, ...
+    const int my = wave < n_chunks ? (n_chunks - wave + kWaves - 1) / kWaves : 0;
 
-    for (int ch = wave; ch < n_chunks; ch += kWaves) {
-        const int chunk_tok = tok_begin + ch * kChunkTokens;
-        const int pk = s_blk[ch * 4 + (n >> 2)];   // block for this lane's K rows
-        const int pv = s_blk[ch * 4 + grp];        // block for this lane's V rows
-
-        // ---- loads: K rows for 4 tiles, V^T rows for DT dim tiles --------
-        constexpr int KW = FP8 ? 1 : 2;  // 16-byte words per (tile, slice)
-        u32x4 kw[4][KJ][KW];
-        u32x4 vw[DT][KW];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int off = 4 * i + (n & 3);
-            const int64_t row = (((int64_t)pk * Hkv + g) * kBlockSize + off) * D;
-#pragma unroll
-            for (int j = 0; j < KJ; ++j)
-#pragma unroll
-                for (int x = 0; x < KW; ++x) {
-                    if constexpr (FP8)
-                        kw[i][j][x] = *reinterpret_cast<const u32x4*>(a.k_cache + row + 64 * j + 16 * grp);
-                    else
-                        kw[i][j][x] = *reinterpret_cast<const u32x4*>(
-                            reinterpret_cast<const uint16_t*>(a.k_cache) + row + 64 * j + 16 * grp + 8 * x);
-                }
-        }
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const int64_t vrow = (((int64_t)pv * Hkv + g) * D + 16 * dt + n) * kBlockSize;
-#pragma unroll
-            for (int x = 0; x < KW; ++x) {
-                if constexpr (FP8)
-                    vw[dt][x] = *reinterpret_cast<const u32x4*>(a.v_cache + vrow);
-                else
-                    vw[dt][x] = *reinterpret_cast<const u32x4*>(
-                        reinterpret_cast<const uint16_t*>(a.v_cache) + vrow + 8 * x);
-            }
-        }
-
-        // ---- S = K Q^T ---------------------------------------------------
-        float sv[16];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f32x4 st = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int j = 0; j < KJ; ++j)
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    bf16x8 ka;
-                    if constexpr (FP8)
-                        ka = e4m3x8_to_bf16(kw[i][j][0][2 * hh], kw[i][j][0][2 * hh + 1]);
-                    else
-                        ka = __builtin_bit_cast(bf16x8, kw[i][j][hh]);
-                    st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[2 * j + hh], st, 0, 0, 0);
-                }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sv[4 * i + r] = st[r] * c;
-        }
-
-        // ---- online softmax over this chunk (head n, chunk block grp) -----
-        const int valid = tok_end - (chunk_tok + 16 * grp);  // tokens of block grp in range
-        float mloc = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {  // sv[4i + r] is token offset 4i + r of block grp
-            if (e >= valid) sv[e] = -INFINITY;
-            mloc = fmaxf(mloc, sv[e]);
-        }
-        mloc = fmaxf(mloc, shfl_xor(mloc, 16));
-        mloc = fmaxf(mloc, shfl_xor(mloc, 32));
-        const float m_new = fmaxf(m_run, mloc);
-        const float alpha = fast_exp2(m_run - m_new);
-        m_run = m_new;
-
-        // Weights in the PV operand layout (half hh = tokens 8hh..8hh+7).  They
-        // are scaled by 2^15 (exp2 offset) so they sit in f16's normal range,
-        // and split into hi + lo 16-bit parts so the two PV MFMAs on the same
-        // exact V operand reproduce the fp32 weight to ~2^-21.  The scale is
-        // common to acc and l and cancels in the final division.
-        const float m_off = m_new - 15.0f;
-        float psum = 0.f;
-        f16x8 pfh[2], pfl[2];
-        bf16x8 pbh[2], pbl[2];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-                const float p0 = fast_exp2(sv[8 * hh + 2 * e2] - m_off);
-                const float p1 = fast_exp2(sv[8 * hh + 2 * e2 + 1] - m_off);
-                psum += p0 + p1;
-                if constexpr (FP8) {
-                    const f16x2 h = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(p0, p1));
-                    const f16x2 l = __builtin_bit_cast(
-                        f16x2, __builtin_amdgcn_cvt_pkrtz(p0 - (float)h[0], p1 - (float)h[1]));
-                    pfh[hh][2 * e2] = h[0];
-                    pfh[hh][2 * e2 + 1] = h[1];
-                    pfl[hh][2 * e2] = l[0];
-                    pfl[hh][2 * e2 + 1] = l[1];
+    if constexpr (kPrefetch) {
+        // software pipeline: the next chunk's loads are in flight while the
+        // current one is computed; loads are issued only for chunks that exist
+        MfmaChunk<D, FP8> A, Bc;
+        if (my > 0) {
+            mfma_load(A, a, s_blk, wave, g, n, grp);
+            int i = 0;
+            for (;;) {
+                const int ch = wave + i * kWaves;
+                if (i + 1 < my) {
+                    mfma_load(Bc, a, s_blk, ch + kWaves, g, n, grp);
+                    mfma_process(st, A, qb, cs, tok_begin + ch * kChunkTokens, tok_end, grp);
+                    ++i;
                 } else {
-                    const __bf16 h0 = (__bf16)p0, h1 = (__bf16)p1;
-                    pbh[hh][2 * e2] = h0;
-                    pbh[hh][2 * e2 + 1] = h1;
-                    pbl[hh][2 * e2] = (__bf16)(p0 - (float)h0);
-                    pbl[hh][2 * e2 + 1] = (__bf16)(p1 - (float)h1);
+                    mfma_process(st, A, qb, cs, tok_begin + ch * kChunkTokens, tok_end, grp);
+                    break;
                 }
-            }
-        }
-        l_run = l_run * alpha + psum;
-
-        // zero V bytes of tokens past the end (their weight is 0, the bytes may be anything)
-        if (valid < 16) {
-            // word w of 16-byte word x holds tokens 4w.. (FP8) or 8x + 2w.. (BF16)
-            u32x4 keep[KW];
-#pragma unroll
-            for (int x = 0; x < KW; ++x)
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    uint32_t mask = 0;
-                    if constexpr (FP8) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (4 * w + e < valid) mask |= 0xFFu << (8 * e);
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 2; ++e)
-                            if (8 * x + 2 * w + e < valid) mask |= 0xFFFFu << (16 * e);
-                    }
-                    keep[x][w] = mask;
-                }
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                for (int x = 0; x < KW; ++x) vw[dt][x] &= keep[x];
-        }
-
-        // ---- acc = alpha * acc + V^T P^T ------------------------------------
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            acc[dt] *= alpha;
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                if constexpr (FP8) {
-                    f16x8 va = e4m3x8_to_f16(vw[dt][0][2 * hh], vw[dt][0][2 * hh + 1]);
-                    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pfh[hh], acc[dt], 0, 0, 0);
-                    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pfl[hh], acc[dt], 0, 0, 0);
+                const int ch2 = wave + i * kWaves;
+                if (i + 1 < my) {
+                    mfma_load(A, a, s_blk, ch2 + kWaves, g, n, grp);
+                    mfma_process(st, Bc, qb, cs, tok_begin + ch2 * kChunkTokens, tok_end, grp);
+                    ++i;
                 } else {
-                    bf16x8 va = __builtin_bit_cast(bf16x8, vw[dt][hh]);
-                    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pbh[hh], acc[dt], 0, 0, 0);
-                    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pbl[hh], acc[dt], 0, 0, 0);
+                    mfma_process(st, Bc, qb, cs, tok_begin + ch2 * kChunkTokens, tok_end, grp);
+                    break;
                 }
             }
+        }
+    } else {
+        for (int i = 0; i < my; ++i) {
+            const int ch = wave + i * kWaves;
+            MfmaChunk<D, FP8> A;
+            mfma_load(A, a, s_blk, ch, g, n, grp);
+            mfma_process(st, A, qb, cs, tok_begin + ch * kChunkTokens, tok_end, grp);
         }
     }
 
     // ---- wave results -> LDS ---------------------------------------------------
+    float l_run = st.l_run;
     l_run += shfl_xor(l_run, 16);
     l_run += shfl_xor(l_run, 32);
     if (grp == 0) {
-        s_m[wave * 16 + n] = m_run;
+        s_m[wave * 16 + n] = st.m_run;
         s_l[wave * 16 + n] = l_run;
     }
     if (n < G) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) s_acc[(wave * G + n) * D + 16 * dt + 4 * grp + r] = acc[dt][r];
+            for (int r = 0; r < 4; ++r) s_acc[(wave * G + n) * D + 16 * dt + 4 * grp + r] = st.acc[dt][r];
     }
     __syncthreads();
-    merge_waves_and_store(a, s_m, s_l, s_acc, b, g, s, D);
+    finish_split(a, s_m, s_l, s_acc, b, g, s, S, D);
 }
 
 // =============================================================================
@@ -337,8 +425,12 @@ __global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeArgs a) {
     const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int L = a.seq_lens[b];
     const int tok_begin = s * a.split_tokens;
-    if (tok_begin >= L) return;
+    if (tok_begin >= L) {
+        if (L <= 0 && s == 0) write_empty(a, b, g, D);
+        return;
+    }
     const int tok_end = min(L, tok_begin + a.split_tokens);
+    const int S = (L + a.split_tokens - 1) / a.split_tokens;   // splits holding tokens
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int Hkv = a.Hkv;
 
@@ -492,38 +584,84 @@ __global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeArgs a) {
         for (int e = 0; e < VD; ++e) s_acc[(wave * G + h) * D + lane + 64 * e] = acc[h][e];
     }
     __syncthreads();
-    merge_waves_and_store(a, s_m, s_l, s_acc, b, g, s, D);
+    finish_split(a, s_m, s_l, s_acc, b, g, s, S, D);
 }
 
 // =============================================================================
 // cross-split merge: out = v_scale * sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s
 // =============================================================================
-template <int D>
-__global__ void __launch_bounds__(D) merge_splits_kernel(DecodeArgs a) {
-    const int hq = blockIdx.x;            // b * Hq + h
-    const int b = hq / a.Hq;
-    const int d = threadIdx.x;
-    const int L = a.seq_lens[b];
-    const int S = (L + a.split_tokens - 1) / a.split_tokens;  // splits with tokens
-    float result = 0.f;
-    if (S > 0) {
-        const float* ml = a.ws_ml + (int64_t)hq * a.num_splits * 2;
-        const float* ac = a.ws_acc + (int64_t)hq * a.num_splits * D + d;
-        float M = -INFINITY;
-        for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * s]);
-        float num = 0.f, den = 0.f;
-        for (int s = 0; s < S; ++s) {
-            const float f = fast_exp2(ml[2 * s] - M);
-            num += f * ac[(int64_t)s * D];
-            den += f * ml[2 * s + 1];
-        }
-        result = num / den * a.v_scale;
+// One work-group per (sequence, query head) whose sequence has two or more
+// splits.  Every load is issued up front (the first 4 partial rows per thread
+// and all (m, l) pairs), so the merge costs about one memory round trip: the
+// split weights go to LDS, and P = 256 / (D/4) thread groups each sum every
+// P-th split of one 4-dim column before an LDS reduction.
+constexpr int kMergeThreads = 256;
+
+__device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const float t = shfl_xor(v, o);
+        v = is_max ? fmaxf(v, t) : v + t;
     }
-    const int64_t o = (int64_t)hq * D + d;
-    if (a.out_f32)
-        reinterpret_cast<float*>(a.out)[o] = result;
-    else
-        reinterpret_cast<uint16_t*>(a.out)[o] = (uint16_t)f32_to_bf16_rne(result);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int w = 1; w < kMergeThreads / 64; ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
+    return r;
+}
+
+template <int D>
+__global__ void __launch_bounds__(kMergeThreads) merge_splits_kernel(DecodeArgs a) {
+    constexpr int C4 = D / 4;                 // float4 columns of a partial row
+    constexpr int P = kMergeThreads / C4;     // split groups: 16, 8, 4 for D = 64, 128, 256
+    constexpr int PRE = 4;                    // partial rows loaded up front per thread
+    extern __shared__ float s_w[];            // [num_splits] split weights
+    __shared__ float red[kMergeThreads / 64];
+    __shared__ f32x4 part[P][C4];
+    const int hq = blockIdx.x;                // b * Hq + h
+    const int b = hq / a.Hq;
+    const int L = a.seq_lens[b];
+    const int S = (L + a.split_tokens - 1) / a.split_tokens;
+    if (S <= 1) return;                       // written by the decode kernel
+    const int t = threadIdx.x;
+    const int d4 = t % C4, p = t / C4;
+    const float* ml = a.ws_ml + (int64_t)hq * a.num_splits * 2;
+    const f32x4* col = reinterpret_cast<const f32x4*>(a.ws_acc + (int64_t)hq * a.num_splits * D) + d4;
+    f32x4 pre[PRE];
+#pragma unroll
+    for (int k = 0; k < PRE; ++k) {
+        const int s = p + k * P;
+        pre[k] = s < S ? col[(int64_t)s * C4] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float m = -INFINITY;
+    for (int s = t; s < S; s += kMergeThreads) m = fmaxf(m, ml[2 * s]);
+    const float M = block_reduce(m, red, true);
+    float den = 0.f;
+    for (int s = t; s < S; s += kMergeThreads) {
+        const float w = fast_exp2(ml[2 * s] - M);
+        s_w[s] = w;
+        den += w * ml[2 * s + 1];
+    }
+    den = block_reduce(den, red, false);       // its barriers also publish s_w
+    f32x4 num = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < PRE; ++k) {
+        const int s = p + k * P;
+        if (s < S) num += s_w[s] * pre[k];
+    }
+    for (int s = p + PRE * P; s < S; s += P) num += s_w[s] * col[(int64_t)s * C4];
+    part[p][d4] = num;
+    __syncthreads();
+    if (p == 0) {
+#pragma unroll
+        for (int q = 1; q < P; ++q) num += part[q][d4];
+        const float scale = a.v_scale / den;
+        const int64_t o = (int64_t)hq * D + 4 * d4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) store_out(a, o + e, num[e] * scale);
+    }
 }
 
 template <int D, bool FP8>
@@ -537,8 +675,9 @@ static hipError_t launch_family(const DecodeArgs& a, int B, int impl, hipStream_
         hipLaunchKernelGGL((decode_valu_kernel<D, FP8>), grid, dim3(kThreads), lds, st, a);
     }
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((merge_splits_kernel<D>), dim3(B * a.Hq), dim3(D), 0, st, a);
+    if (e != hipSuccess || a.num_splits <= 1) return e;
+    hipLaunchKernelGGL((merge_splits_kernel<D>), dim3(B * a.Hq), dim3(kMergeThreads),
+                       sizeof(float) * a.num_splits, st, a);
     return hipGetLastError();
 }
 

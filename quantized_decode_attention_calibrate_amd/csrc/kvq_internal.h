@@ -15,6 +15,8 @@ struct DecodePlan {
 
 // Largest split the kernels stage block ids for (LDS table of 512 ids).
 constexpr int kMaxSplitTokens = 8192;
+// Most splits one call may have (the merge keeps one weight per split in LDS).
+constexpr int kMaxSplits = 16384;
 constexpr int kChunkTokens = 64;   // tokens per wave iteration (4 blocks of 16)
 constexpr int kBlockSize = 16;
 
@@ -35,6 +37,9 @@ struct DecodeArgs {
     int out_f32;
 };
 
+// Workspace: [ml: B*Hq*S*2 f32][acc: B*Hq*S*D f32], the second region starting
+// on a 256-byte boundary.
+size_t decode_ml_bytes(int B, int Hq, int num_splits);
 size_t decode_workspace_bytes(int B, int Hq, int D, int num_splits);
 DecodePlan plan_decode(int B, int Hkv, int max_seq_len, int split_tokens_request);
 

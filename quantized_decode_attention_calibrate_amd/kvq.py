@@ -11,7 +11,7 @@ import os
 import torch  # must be loaded first: libkvq binds to the HIP runtime torch ships
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libkvq.so")
+LIB_PATH = os.environ.get("KVQ_LIBRARY") or os.path.join(_PKG, "libkvq.so")
 
 KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_EWORKSPACE, KVQ_EHIP = 0, -1, -2, -3, -4
 KVQ_KV_BF16, KVQ_KV_FP8_E4M3 = 0, 1
@@ -152,8 +152,9 @@ def kvq_decode_plan_split_tokens(B: int, Hkv: int, max_seq_len: int) -> int:
 
 
 def new_workspace(B: int, Hq: int, Hkv: int, D: int, max_seq_len: int, split_tokens: int = 0, device="cuda"):
+    """Workspace for kvq_paged_decode_attn."""
     n = kvq_decode_workspace_bytes(B, Hq, Hkv, D, max_seq_len, split_tokens)
-    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
 def kvq_paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_dtype: int,

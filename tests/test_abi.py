@@ -60,7 +60,7 @@ def attn(K, **over):
     (dict(D=96), -2), (dict(bs=32), -2), (dict(Hq=34, Hkv=2), -2), (dict(msl=8 * 16 + 1), -1),
     (dict(ks=0.0), -1), (dict(vs=float("nan")), -1), (dict(sm=float("inf")), -1), (dict(wsb=64), -3),
     (dict(q=FAKE + 8), -1), (dict(impl=3), -1), (dict(split=100), -1), (dict(split=16384), -1),
-    (dict(B=-1), -1), (dict(nb=0), -1),
+    (dict(B=-1), -1), (dict(nb=0), -1), (dict(msl=64 * 16385, mb=70000, split=64), -2),
 ])
 def test_decode_validation(K, over, status):
     assert attn(K, **over) == status
@@ -120,6 +120,8 @@ def test_plan_and_workspace(K):
         split = K.kvq_decode_plan_split_tokens(B, Hkv, L)
         assert split % 64 == 0 and 512 <= split <= 8192
         S = max(1, math.ceil(L / split))
-        assert K.kvq_decode_workspace_bytes(B, Hq, Hkv, D, L) == B * Hq * S * (D + 2) * 4
-        assert K.kvq_decode_workspace_bytes(B, Hq, Hkv, D, L, 128) == B * Hq * max(1, math.ceil(L / 128)) * (D + 2) * 4
+        pad = lambda n: (n + 255) // 256 * 256
+        for sp, SS in ((0, S), (128, max(1, math.ceil(L / 128)))):
+            want = pad(B * Hq * SS * 8) + B * Hq * SS * D * 4
+            assert K.kvq_decode_workspace_bytes(B, Hq, Hkv, D, L, sp) == want
     assert K.kvq_decode_workspace_bytes(1, 8, 2, 64, 100, 100) == 0   # not a multiple of 64
