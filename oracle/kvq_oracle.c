@@ -231,7 +231,7 @@ void kvqo_nvfp4_cache_write(const uint16_t* k, const uint16_t* v, int64_t src_st
                 nvfp4_group(xv, v_gscale, codes, &sc);
                 for (int i = 0; i < 16; ++i)
                     set_nibble(vr, (int64_t)(grp * 16 + i) * block_size + off, codes[i]); /* [D][bs] nibbles */
-                vr[codes_bytes + off * (D / 16) + grp] = sc;
+                vr[codes_bytes + (int64_t)grp * block_size + off] = sc;                  /* [D/16][bs] */
             }
         }
     }
@@ -253,7 +253,7 @@ double kvqo_nvfp4_v_value(const uint8_t* v_cache, int64_t slot, int g, int d,
     int64_t blk = slot / block_size, off = slot % block_size;
     const uint8_t* r = v_cache + (blk * Hkv + g) * region;
     uint8_t code = get_nibble(r, (int64_t)d * block_size + off);
-    uint8_t sc = r[(int64_t)block_size * D / 2 + off * (D / 16) + d / 16];
+    uint8_t sc = r[(int64_t)block_size * D / 2 + (int64_t)(d / 16) * block_size + off];
     return kvqo_e2m1_value(code) * kvqo_e4m3_value(sc) * (double)v_gscale;
 }
 

@@ -98,7 +98,8 @@ int kvqo_nvfp4_calibrate(const float* amax, float* gscale, int n);
  *   K: codes [block_size][D/2] (element 2i low nibble, 2i+1 high nibble)
  *      then block scales [block_size][D/16] (E4M3 codes)
  *   V: codes [D][block_size/2] (token 2j low nibble, 2j+1 high nibble)
- *      then block scales [block_size][D/16]
+ *      then block scales [D/16][block_size] (group-major: one dim group's
+ *      scales for all tokens of the block are contiguous)
  *   region bytes = block_size*D/2 + block_size*D/16. */
 int64_t kvqo_nvfp4_region_bytes(int D, int block_size);
 
