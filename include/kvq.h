@@ -40,6 +40,7 @@
  *   BF16 / FP8 K cache  [num_blocks][Hkv][block_size][D]    (u16 / u8)
  *   BF16 / FP8 V cache  [num_blocks][Hkv][D][block_size]    (u16 / u8, dim-major)
  *   NVFP4 K and V cache [num_blocks][Hkv][kvq_nvfp4_region_bytes(D, bs)] bytes
+ *                       (layout inside a region: see the NVFP4 section)
  *   A token's slot is physical_block * block_size + offset.
  */
 #ifndef KVQ_H
@@ -186,6 +187,61 @@ int kvq_paged_decode_attn_ex(const void* q_dev, const void* k_cache_dev, const v
 
 /* Split length (tokens) the automatic plan picks for this shape. */
 int kvq_decode_plan_split_tokens(int B, int Hkv, int max_seq_len, int block_size);
+
+/* ---- block-scaled 4-bit (NVFP4-style) KV cache -------------------------------
+ * [RUN26]: a block-scaled 4-bit float with FP8 scale factors, 4.5 bits per
+ * number, 1.8x smaller than FP8.  The pages give the format's name and size
+ * only; the recipe here is this library's reading:
+ *   - element E2M1 (values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and sign), one E4M3
+ *     block scale per 16 consecutive elements along D of a (token, head) row,
+ *     and one fp32 global scale per tensor;
+ *   - gscale = fp32(max(amax * 1.05 / (6 * 448), 1e-12)) (the [CAL] formula
+ *     with the E2M1 * E4M3 range);
+ *   - per 16-element group: bscale = E4M3(bamax / fp32(6 * gscale)),
+ *     e = fp32(value(bscale) * gscale), code_i = E2M1(x_i / e) (fp32 division,
+ *     round to nearest even, saturating at 6), all-zero codes when e == 0;
+ *   - value = E2M1(code) * value(bscale) * gscale.
+ * Cache region per (block, head), kvq_nvfp4_region_bytes(D, 16) = 9*D bytes:
+ *   K: codes [16][D/2] (element 2i in the low nibble), scales [16][D/16];
+ *   V: codes [D][8] (token 2j in the low nibble), scales [D/16][16].
+ * A V code byte holds two tokens, so writes merge nibbles atomically; bytes of
+ * other tokens are preserved. */
+int kvq_nvfp4_calibrate(const float* amax_host, float* gscale_host, int n);
+size_t kvq_nvfp4_region_bytes(int D, int block_size);
+
+/* As kvq_cache_write, into NVFP4 caches [num_blocks][Hkv][region] bytes, with
+ * the per-tensor global scales k_gscale, v_gscale (> 0, finite). */
+int kvq_nvfp4_cache_write(const void* k_dev, const void* v_dev, int64_t src_token_stride,
+                          const int64_t* slot_mapping_dev, int T, int Hkv, int D,
+                          void* k_cache_dev, void* v_cache_dev, int num_blocks, int block_size,
+                          float k_gscale, float v_gscale, void* hip_stream);
+
+/* As kvq_paged_decode_attn over NVFP4 caches (MFMA family; the block scales
+ * are applied while converting codes to MFMA operands, the global scales are
+ * folded into the softmax exponent and the final division).  Same workspace
+ * sizing (kvq_decode_workspace_bytes[_ex]). */
+int kvq_nvfp4_paged_decode_attn(const void* q_dev, const void* k_cache_dev, const void* v_cache_dev,
+                                const int32_t* block_tables_dev, int max_blocks_per_seq,
+                                const int32_t* seq_lens_dev, int max_seq_len,
+                                int B, int Hq, int Hkv, int D, int block_size, int num_blocks,
+                                float k_gscale, float v_gscale, float sm_scale,
+                                void* out_dev, int out_dtype,
+                                void* workspace_dev, size_t workspace_bytes, void* hip_stream);
+int kvq_nvfp4_paged_decode_attn_ex(const void* q_dev, const void* k_cache_dev, const void* v_cache_dev,
+                                   const int32_t* block_tables_dev, int max_blocks_per_seq,
+                                   const int32_t* seq_lens_dev, int max_seq_len,
+                                   int B, int Hq, int Hkv, int D, int block_size, int num_blocks,
+                                   float k_gscale, float v_gscale, float sm_scale,
+                                   void* out_dev, int out_dtype,
+                                   void* workspace_dev, size_t workspace_bytes, void* hip_stream,
+                                   int split_tokens);
+
+/* E2M1 codec utility: byte i of codes_dev holds two codes (low nibble first);
+ * out_dev[2i], out_dev[2i+1] = value(code) * value(scale_code) as f16, where
+ * scale_code is an E4M3 block-scale code -- computed exactly as the NVFP4
+ * decode kernel builds its operands.  out_dev: 2 * n_bytes f16, 4-byte aligned. */
+int kvq_e2m1_decode(const uint8_t* codes_dev, uint8_t scale_code, void* out_dev, int64_t n_bytes,
+                    void* hip_stream);
 
 #ifdef __cplusplus
 }

@@ -103,15 +103,52 @@ int kvq_amax_bf16(const void* x_dev, int64_t rows, int64_t cols, int64_t row_str
     return hip_status(launch_amax_bf16(x_dev, rows, cols, row_stride, amax_dev, (hipStream_t)hip_stream));
 }
 
-int kvq_calibrate(const float* amax_host, float* scale_host, int n) {
+static int scales_from_amax(const float* amax_host, float* scale_host, int n, double top) {
     if (n < 0 || (n > 0 && (!amax_host || !scale_host))) return KVQ_EINVAL;
     for (int i = 0; i < n; ++i)
         if (!(amax_host[i] >= 0.0f) || isinf(amax_host[i])) return KVQ_EINVAL;
     for (int i = 0; i < n; ++i) {
-        double s = (double)amax_host[i] * 1.05 / 448.0;
+        double s = (double)amax_host[i] * 1.05 / top;
         scale_host[i] = (float)(s > 1e-12 ? s : 1e-12);
     }
     return KVQ_OK;
+}
+
+int kvq_calibrate(const float* amax_host, float* scale_host, int n) {
+    return scales_from_amax(amax_host, scale_host, n, 448.0);
+}
+
+int kvq_nvfp4_calibrate(const float* amax_host, float* gscale_host, int n) {
+    return scales_from_amax(amax_host, gscale_host, n, 6.0 * 448.0);
+}
+
+size_t kvq_nvfp4_region_bytes(int D, int block_size) {
+    if (D <= 0 || D % 16 != 0 || block_size <= 0 || block_size % 2 != 0) return 0;
+    return (size_t)block_size * D / 2 + (size_t)block_size * D / 16;
+}
+
+int kvq_e2m1_decode(const uint8_t* codes_dev, uint8_t scale_code, void* out_dev, int64_t n_bytes, void* hip_stream) {
+    if (n_bytes < 0) return KVQ_EINVAL;
+    if (n_bytes == 0) return KVQ_OK;
+    if (!codes_dev || !out_dev || ((uintptr_t)out_dev & 3u) != 0) return KVQ_EINVAL;
+    return hip_status(launch_e2m1_decode(codes_dev, scale_code, out_dev, n_bytes, (hipStream_t)hip_stream));
+}
+
+int kvq_nvfp4_cache_write(const void* k_dev, const void* v_dev, int64_t src_token_stride,
+                          const int64_t* slot_mapping_dev, int T, int Hkv, int D, void* k_cache_dev,
+                          void* v_cache_dev, int num_blocks, int block_size, float k_gscale, float v_gscale,
+                          void* hip_stream) {
+    if (T < 0 || Hkv <= 0 || num_blocks <= 0) return KVQ_EINVAL;
+    if (!supported_d(D) || block_size != kBlockSize) return KVQ_EUNSUPPORTED;
+    if (!good_scale(k_gscale) || !good_scale(v_gscale)) return KVQ_EINVAL;
+    if (T == 0) return KVQ_OK;
+    if (!k_dev || !v_dev || !slot_mapping_dev || !k_cache_dev || !v_cache_dev) return KVQ_EINVAL;
+    if (src_token_stride < (int64_t)Hkv * D || (src_token_stride & 7) != 0) return KVQ_EINVAL;
+    if (!aligned16(k_dev) || !aligned16(v_dev) || !aligned16(k_cache_dev) || !aligned16(v_cache_dev))
+        return KVQ_EINVAL;
+    return hip_status(launch_nvfp4_cache_write(k_dev, v_dev, src_token_stride, slot_mapping_dev, T, Hkv, D,
+                                               k_cache_dev, v_cache_dev, k_gscale, v_gscale,
+                                               (hipStream_t)hip_stream));
 }
 
 int kvq_cache_write(const void* k_dev, const void* v_dev, int64_t src_token_stride,
@@ -152,16 +189,14 @@ size_t kvq_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_seq_len
     return kvq_decode_workspace_bytes_ex(B, Hq, Hkv, D, max_seq_len, block_size, 0);
 }
 
-int kvq_paged_decode_attn_ex(const void* q_dev, const void* k_cache_dev, const void* v_cache_dev, int kv_dtype,
-                             const int32_t* block_tables_dev, int max_blocks_per_seq, const int32_t* seq_lens_dev,
-                             int max_seq_len, int B, int Hq, int Hkv, int D, int block_size, int num_blocks,
-                             float k_scale, float v_scale, float sm_scale, void* out_dev, int out_dtype,
-                             void* workspace_dev, size_t workspace_bytes, void* hip_stream, int impl,
-                             int split_tokens) {
+static int decode_common(int fmt, const void* q_dev, const void* k_cache_dev, const void* v_cache_dev,
+                         const int32_t* block_tables_dev, int max_blocks_per_seq, const int32_t* seq_lens_dev,
+                         int max_seq_len, int B, int Hq, int Hkv, int D, int block_size, int num_blocks,
+                         float k_scale, float v_scale, float sm_scale, void* out_dev, int out_dtype,
+                         void* workspace_dev, size_t workspace_bytes, void* hip_stream, int impl, int split_tokens) {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_seq_len < 0)
         return KVQ_EINVAL;
     if (Hq % Hkv != 0) return KVQ_EINVAL;
-    if (kv_dtype != KVQ_KV_BF16 && kv_dtype != KVQ_KV_FP8_E4M3) return KVQ_EINVAL;
     if (out_dtype != KVQ_OUT_BF16 && out_dtype != KVQ_OUT_F32) return KVQ_EINVAL;
     if (impl < KVQ_IMPL_AUTO || impl > KVQ_IMPL_MFMA) return KVQ_EINVAL;
     if (split_tokens < 0 || split_tokens % kChunkTokens != 0 || split_tokens > kMaxSplitTokens)
@@ -171,7 +206,7 @@ int kvq_paged_decode_attn_ex(const void* q_dev, const void* k_cache_dev, const v
     if (G > 16) return KVQ_EUNSUPPORTED;
     if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * block_size) return KVQ_EINVAL;
     if (!isfinite(sm_scale)) return KVQ_EINVAL;
-    if (kv_dtype == KVQ_KV_FP8_E4M3 && (!good_scale(k_scale) || !good_scale(v_scale))) return KVQ_EINVAL;
+    if (fmt != kFmtBF16 && (!good_scale(k_scale) || !good_scale(v_scale))) return KVQ_EINVAL;
     if (B == 0) return KVQ_OK;
     if (!q_dev || !k_cache_dev || !v_cache_dev || !block_tables_dev || !seq_lens_dev || !out_dev ||
         !workspace_dev)
@@ -183,9 +218,9 @@ int kvq_paged_decode_attn_ex(const void* q_dev, const void* k_cache_dev, const v
     if (plan.num_splits > kMaxSplits) return KVQ_EUNSUPPORTED;
     const size_t need = decode_workspace_bytes(B, Hq, D, plan.num_splits);
     if (workspace_bytes < need) return KVQ_EWORKSPACE;
-    if (impl == KVQ_IMPL_AUTO) impl = KVQ_IMPL_MFMA;
+    if (impl == KVQ_IMPL_AUTO || fmt == kFmtNVFP4) impl = KVQ_IMPL_MFMA;
 
-    const bool fp8 = kv_dtype == KVQ_KV_FP8_E4M3;
+    const bool scaled = fmt != kFmtBF16;
     DecodeArgs a;
     a.q = (const uint16_t*)q_dev;
     a.k_cache = (const uint8_t*)k_cache_dev;
@@ -201,10 +236,46 @@ int kvq_paged_decode_attn_ex(const void* q_dev, const void* k_cache_dev, const v
     a.G = G;
     a.split_tokens = plan.split_tokens;
     a.num_splits = plan.num_splits;
-    a.qk_scale_log2 = (float)((double)sm_scale * (fp8 ? (double)k_scale : 1.0) * 1.4426950408889634);
-    a.v_scale = fp8 ? v_scale : 1.0f;
+    a.qk_scale_log2 = (float)((double)sm_scale * (scaled ? (double)k_scale : 1.0) * 1.4426950408889634);
+    a.v_scale = scaled ? v_scale : 1.0f;
     a.out_f32 = out_dtype == KVQ_OUT_F32;
-    return hip_status(launch_decode(a, B, D, fp8, impl, (hipStream_t)hip_stream));
+    return hip_status(launch_decode(a, B, D, fmt, impl, (hipStream_t)hip_stream));
+}
+
+int kvq_paged_decode_attn_ex(const void* q_dev, const void* k_cache_dev, const void* v_cache_dev, int kv_dtype,
+                             const int32_t* block_tables_dev, int max_blocks_per_seq, const int32_t* seq_lens_dev,
+                             int max_seq_len, int B, int Hq, int Hkv, int D, int block_size, int num_blocks,
+                             float k_scale, float v_scale, float sm_scale, void* out_dev, int out_dtype,
+                             void* workspace_dev, size_t workspace_bytes, void* hip_stream, int impl,
+                             int split_tokens) {
+    if (kv_dtype != KVQ_KV_BF16 && kv_dtype != KVQ_KV_FP8_E4M3) return KVQ_EINVAL;
+    return decode_common(kv_dtype == KVQ_KV_FP8_E4M3 ? kFmtFP8 : kFmtBF16, q_dev, k_cache_dev, v_cache_dev,
+                         block_tables_dev, max_blocks_per_seq, seq_lens_dev, max_seq_len, B, Hq, Hkv, D,
+                         block_size, num_blocks, k_scale, v_scale, sm_scale, out_dev, out_dtype, workspace_dev,
+                         workspace_bytes, hip_stream, impl, split_tokens);
+}
+
+int kvq_nvfp4_paged_decode_attn_ex(const void* q_dev, const void* k_cache_dev, const void* v_cache_dev,
+                                   const int32_t* block_tables_dev, int max_blocks_per_seq,
+                                   const int32_t* seq_lens_dev, int max_seq_len, int B, int Hq, int Hkv, int D,
+                                   int block_size, int num_blocks, float k_gscale, float v_gscale, float sm_scale,
+                                   void* out_dev, int out_dtype, void* workspace_dev, size_t workspace_bytes,
+                                   void* hip_stream, int split_tokens) {
+    return decode_common(kFmtNVFP4, q_dev, k_cache_dev, v_cache_dev, block_tables_dev, max_blocks_per_seq,
+                         seq_lens_dev, max_seq_len, B, Hq, Hkv, D, block_size, num_blocks, k_gscale, v_gscale,
+                         sm_scale, out_dev, out_dtype, workspace_dev, workspace_bytes, hip_stream, KVQ_IMPL_MFMA,
+                         split_tokens);
+}
+
+int kvq_nvfp4_paged_decode_attn(const void* q_dev, const void* k_cache_dev, const void* v_cache_dev,
+                                const int32_t* block_tables_dev, int max_blocks_per_seq, const int32_t* seq_lens_dev,
+                                int max_seq_len, int B, int Hq, int Hkv, int D, int block_size, int num_blocks,
+                                float k_gscale, float v_gscale, float sm_scale, void* out_dev, int out_dtype,
+                                void* workspace_dev, size_t workspace_bytes, void* hip_stream) {
+    return kvq_nvfp4_paged_decode_attn_ex(q_dev, k_cache_dev, v_cache_dev, block_tables_dev, max_blocks_per_seq,
+                                          seq_lens_dev, max_seq_len, B, Hq, Hkv, D, block_size, num_blocks,
+                                          k_gscale, v_gscale, sm_scale, out_dev, out_dtype, workspace_dev,
+                                          workspace_bytes, hip_stream, 0);
 }
 
 int kvq_paged_decode_attn(const void* q_dev, const void* k_cache_dev, const void* v_cache_dev, int kv_dtype,

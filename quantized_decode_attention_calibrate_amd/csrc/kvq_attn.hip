@@ -26,6 +26,8 @@
 //         sharing a KV head are the 16-wide N dimension (padded), so each K/V
 //         byte is read once per KV head.
 //   VALU: plain fp32 FMAs with Q staged in LDS; the comparator.
+#include <type_traits>
+
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -121,14 +123,25 @@ __device__ __forceinline__ void write_empty(const DecodeArgs& a, int b, int g, i
 #define KVQ_MFMA_PREFETCH 1
 #endif
 
-// Raw bytes of one 64-token chunk as this lane needs them.
-template <int D, bool FP8>
-struct MfmaChunk {
-    static constexpr int KJ = D / 64;        // 64-dim slices of a K row
-    static constexpr int DT = D / 16;        // PV dim tiles
-    static constexpr int KW = FP8 ? 1 : 2;   // 16-byte words per (tile, slice) / per V row
-    u32x4 kw[4][KJ][KW];
-    u32x4 vw[DT][KW];
+// Raw bytes of one 64-token chunk as this lane needs them, per cache format.
+template <int D, int FMT>
+struct MfmaChunk;
+template <int D>
+struct MfmaChunk<D, kFmtFP8> {        // 16 K bytes per (tile, slice); 16 tokens of one V dim
+    u32x4 kw[4][D / 64];
+    u32x4 vw[D / 16];
+};
+template <int D>
+struct MfmaChunk<D, kFmtBF16> {       // the same elements at two bytes each
+    u32x4 kw[4][D / 64][2];
+    u32x4 vw[D / 16][2];
+};
+template <int D>
+struct MfmaChunk<D, kFmtNVFP4> {      // 16 E2M1 codes + 1 scale per (tile, slice); V dim row + 16 token scales
+    u32x2 kc[4][D / 64];
+    uint32_t ks[4][D / 64];
+    u32x2 vc[D / 16];
+    u32x4 vs[D / 16];
 };
 
 // Per-wave running softmax state of head n (lane % 16).
@@ -138,60 +151,113 @@ struct MfmaState {
     float m_run, l_run;
 };
 
-template <int D, bool FP8>
-__device__ __forceinline__ void mfma_load(MfmaChunk<D, FP8>& c, const DecodeArgs& a, const int* s_blk, int ch,
+template <int D, int FMT>
+__device__ __forceinline__ void mfma_load(MfmaChunk<D, FMT>& c, const DecodeArgs& a, const int* s_blk, int ch,
                                           int g, int n, int grp) {
-    using C = MfmaChunk<D, FP8>;
+    constexpr int KJ = D / 64, DT = D / 16;
     const int pk = s_blk[ch * 4 + (n >> 2)];   // block of this lane's K rows
     const int pv = s_blk[ch * 4 + grp];        // block of this lane's V rows
+    if constexpr (FMT == kFmtNVFP4) {
+        constexpr int64_t region = 9 * D;              // 16*D/2 code bytes + 16*D/16 scale bytes
+        constexpr int64_t codes = 8 * D;
+        const uint8_t* kr = a.k_cache + ((int64_t)pk * a.Hkv + g) * region;
+        const uint8_t* vr = a.v_cache + ((int64_t)pv * a.Hkv + g) * region;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int off = 4 * i + (n & 3);
-        const int64_t row = (((int64_t)pk * a.Hkv + g) * kBlockSize + off) * D;
+        for (int i = 0; i < 4; ++i) {
+            const int off = 4 * i + (n & 3);
 #pragma unroll
-        for (int j = 0; j < C::KJ; ++j)
-#pragma unroll
-            for (int x = 0; x < C::KW; ++x) {
-                if constexpr (FP8)
-                    c.kw[i][j][x] = *reinterpret_cast<const u32x4*>(a.k_cache + row + 64 * j + 16 * grp);
-                else
-                    c.kw[i][j][x] = *reinterpret_cast<const u32x4*>(
-                        reinterpret_cast<const uint16_t*>(a.k_cache) + row + 64 * j + 16 * grp + 8 * x);
+            for (int j = 0; j < KJ; ++j) {
+                c.kc[i][j] = *reinterpret_cast<const u32x2*>(kr + off * (D / 2) + 32 * j + 8 * grp);
+                c.ks[i][j] = kr[codes + off * (D / 16) + 4 * j + grp];
             }
-    }
+        }
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) {
-        const int64_t vrow = (((int64_t)pv * a.Hkv + g) * D + 16 * dt + n) * kBlockSize;
+        for (int dt = 0; dt < DT; ++dt) {
+            c.vc[dt] = *reinterpret_cast<const u32x2*>(vr + (16 * dt + n) * 8);
+            c.vs[dt] = *reinterpret_cast<const u32x4*>(vr + codes + 16 * dt);
+        }
+    } else {
 #pragma unroll
-        for (int x = 0; x < C::KW; ++x) {
-            if constexpr (FP8)
-                c.vw[dt][x] = *reinterpret_cast<const u32x4*>(a.v_cache + vrow);
-            else
-                c.vw[dt][x] = *reinterpret_cast<const u32x4*>(
-                    reinterpret_cast<const uint16_t*>(a.v_cache) + vrow + 8 * x);
+        for (int i = 0; i < 4; ++i) {
+            const int off = 4 * i + (n & 3);
+            const int64_t row = (((int64_t)pk * a.Hkv + g) * kBlockSize + off) * D;
+#pragma unroll
+            for (int j = 0; j < KJ; ++j) {
+                if constexpr (FMT == kFmtFP8) {
+                    c.kw[i][j] = *reinterpret_cast<const u32x4*>(a.k_cache + row + 64 * j + 16 * grp);
+                } else {
+                    const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.k_cache) + row + 64 * j + 16 * grp;
+                    c.kw[i][j][0] = *reinterpret_cast<const u32x4*>(kc);
+                    c.kw[i][j][1] = *reinterpret_cast<const u32x4*>(kc + 8);
+                }
+            }
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const int64_t vrow = (((int64_t)pv * a.Hkv + g) * D + 16 * dt + n) * kBlockSize;
+            if constexpr (FMT == kFmtFP8) {
+                c.vw[dt] = *reinterpret_cast<const u32x4*>(a.v_cache + vrow);
+            } else {
+                const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.v_cache) + vrow;
+                c.vw[dt][0] = *reinterpret_cast<const u32x4*>(vc);
+                c.vw[dt][1] = *reinterpret_cast<const u32x4*>(vc + 8);
+            }
         }
     }
 }
 
-template <int D, bool FP8>
-__device__ __forceinline__ void mfma_process(MfmaState<D>& st, MfmaChunk<D, FP8>& c, const bf16x8* qb, float cs,
-                                             int chunk_tok, int tok_end, int grp) {
-    using C = MfmaChunk<D, FP8>;
+// K operand of k-step (tile i, slice j, half hh): dims 64j + 16grp + 8hh .. +7
+// of the tile's token row; bf16 for FP8 / BF16 caches, f16 for NVFP4 (codes
+// times the group's E4M3 block scale, exact in f16).
+template <int FMT>
+using QkOperand = typename std::conditional<FMT == kFmtNVFP4, f16x8, bf16x8>::type;
+
+template <int D, int FMT>
+__device__ __forceinline__ QkOperand<FMT> k_operand(const MfmaChunk<D, FMT>& c, int i, int j, int hh) {
+    if constexpr (FMT == kFmtFP8) {
+        return e4m3x8_to_bf16(c.kw[i][j][2 * hh], c.kw[i][j][2 * hh + 1]);
+    } else if constexpr (FMT == kFmtBF16) {
+        return __builtin_bit_cast(bf16x8, c.kw[i][j][hh]);
+    } else {
+        return e2m1x8_scaled_f16(c.kc[i][j][hh], e4m3x2_to_f16(c.ks[i][j], false)[0]);
+    }
+}
+
+// V operand of (dim tile dt, half hh) as f16: tokens 8hh .. 8hh+7 of the lane's dim.
+template <int D, int FMT>
+__device__ __forceinline__ f16x8 v_operand_f16(const MfmaChunk<D, FMT>& c, int dt, int hh) {
+    if constexpr (FMT == kFmtFP8) {
+        return e4m3x8_to_f16(c.vw[dt][2 * hh], c.vw[dt][2 * hh + 1]);
+    } else {
+        // E2M1 codes times each token's own block scale (exact in f16)
+        const uint32_t w = c.vc[dt][hh];
+        const f16x2 v0 = e2m1x2_to_f16<0>(w), v1 = e2m1x2_to_f16<1>(w);
+        const f16x2 v2 = e2m1x2_to_f16<2>(w), v3 = e2m1x2_to_f16<3>(w);
+        const f16x2 s0 = e4m3x2_to_f16(c.vs[dt][2 * hh], false), s1 = e4m3x2_to_f16(c.vs[dt][2 * hh], true);
+        const f16x2 s2 = e4m3x2_to_f16(c.vs[dt][2 * hh + 1], false), s3 = e4m3x2_to_f16(c.vs[dt][2 * hh + 1], true);
+        const f16x2 p0 = v0 * s0, p1 = v1 * s1, p2 = v2 * s2, p3 = v3 * s3;
+        return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+    }
+}
+
+template <int D, int FMT>
+__device__ __forceinline__ void mfma_process(MfmaState<D>& st, MfmaChunk<D, FMT>& c, const QkOperand<FMT>* qb,
+                                             float cs, int chunk_tok, int tok_end, int grp) {
+    constexpr int KJ = D / 64, DT = D / 16;
+    constexpr bool kF16V = FMT != kFmtBF16;   // V operand in f16 (FP8, NVFP4) or bf16
     // ---- S = K Q^T ---------------------------------------------------------
     float sv[16];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < C::KJ; ++j)
+        for (int j = 0; j < KJ; ++j)
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
-                bf16x8 ka;
-                if constexpr (FP8)
-                    ka = e4m3x8_to_bf16(c.kw[i][j][0][2 * hh], c.kw[i][j][0][2 * hh + 1]);
+                if constexpr (FMT == kFmtNVFP4)
+                    t = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand(c, i, j, hh), qb[2 * j + hh], t, 0, 0, 0);
                 else
-                    ka = __builtin_bit_cast(bf16x8, c.kw[i][j][hh]);
-                t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[2 * j + hh], t, 0, 0, 0);
+                    t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(c, i, j, hh), qb[2 * j + hh], t, 0, 0, 0);
             }
 #pragma unroll
         for (int r = 0; r < 4; ++r) sv[4 * i + r] = t[r] * cs;
@@ -227,7 +293,7 @@ __device__ __forceinline__ void mfma_process(MfmaState<D>& st, MfmaChunk<D, FP8>
             const float p0 = fast_exp2(sv[8 * hh + 2 * e2] - m_off);
             const float p1 = fast_exp2(sv[8 * hh + 2 * e2 + 1] - m_off);
             psum += p0 + p1;
-            if constexpr (FP8) {
+            if constexpr (kF16V) {
                 const f16x2 h = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(p0, p1));
                 const f16x2 l =
                     __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(p0 - (float)h[0], p1 - (float)h[1]));
@@ -246,44 +312,59 @@ __device__ __forceinline__ void mfma_process(MfmaState<D>& st, MfmaChunk<D, FP8>
     }
     st.l_run = st.l_run * alpha + psum;
 
-    // zero V bytes of tokens past the end (their weight is 0, the bytes may be anything)
+    // Zero V data of tokens past the end: their weight is 0 but the bytes may be
+    // anything (NaN codes).  FP8: V bytes; NVFP4: the tokens' block scales (the
+    // E2M1 codes are always finite); BF16: V halfwords.
     if (valid < 16) {
-        // word w of 16-byte word x holds tokens 4w.. (FP8) or 8x + 2w.. (BF16)
-        u32x4 keep[C::KW];
+        if constexpr (FMT == kFmtBF16) {
+            u32x4 keep[2];
 #pragma unroll
-        for (int x = 0; x < C::KW; ++x)
+            for (int x = 0; x < 2; ++x)
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                uint32_t mask = 0;
-                if constexpr (FP8) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (4 * w + e < valid) mask |= 0xFFu << (8 * e);
-                } else {
+                for (int w = 0; w < 4; ++w) {
+                    uint32_t mask = 0;
 #pragma unroll
                     for (int e = 0; e < 2; ++e)
                         if (8 * x + 2 * w + e < valid) mask |= 0xFFFFu << (16 * e);
+                    keep[x][w] = mask;
                 }
-                keep[x][w] = mask;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                c.vw[dt][0] &= keep[0];
+                c.vw[dt][1] &= keep[1];
+            }
+        } else {
+            u32x4 keep;   // word w holds tokens 4w .. 4w+3, one byte each
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                uint32_t mask = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (4 * w + e < valid) mask |= 0xFFu << (8 * e);
+                keep[w] = mask;
             }
 #pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-            for (int x = 0; x < C::KW; ++x) c.vw[dt][x] &= keep[x];
+            for (int dt = 0; dt < DT; ++dt) {
+                if constexpr (FMT == kFmtFP8)
+                    c.vw[dt] &= keep;
+                else
+                    c.vs[dt] &= keep;
+            }
+        }
     }
 
     // ---- acc = alpha * acc + V^T P^T ----------------------------------------
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) {
+    for (int dt = 0; dt < DT; ++dt) {
         st.acc[dt] *= alpha;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-            if constexpr (FP8) {
-                f16x8 va = e4m3x8_to_f16(c.vw[dt][0][2 * hh], c.vw[dt][0][2 * hh + 1]);
+            if constexpr (kF16V) {
+                const f16x8 va = v_operand_f16(c, dt, hh);
                 st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pfh[hh], st.acc[dt], 0, 0, 0);
                 st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pfl[hh], st.acc[dt], 0, 0, 0);
             } else {
-                bf16x8 va = __builtin_bit_cast(bf16x8, c.vw[dt][hh]);
+                const bf16x8 va = __builtin_bit_cast(bf16x8, c.vw[dt][hh]);
                 st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pbh[hh], st.acc[dt], 0, 0, 0);
                 st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pbl[hh], st.acc[dt], 0, 0, 0);
             }
@@ -291,7 +372,7 @@ __device__ __forceinline__ void mfma_process(MfmaState<D>& st, MfmaChunk<D, FP8>
     }
 }
 
-template <int D, bool FP8>
+template <int D, int FMT>
 __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
     constexpr int KJ = D / 64;
     constexpr int DT = D / 16;
@@ -321,19 +402,53 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
     stage_block_ids(s_blk, a.block_tables + (int64_t)b * a.max_blocks, lb0, n_chunks * 4,
                     (L + kBlockSize - 1) / kBlockSize - 1);
 
-    // Q^T operands: k-step (j, hh) covers dims 64j + 16grp + 8hh .. +7
-    bf16x8 qb[2 * KJ];
+    // Q^T operands: k-step (j, hh) covers dims 64j + 16grp + 8hh .. +7.  For
+    // NVFP4 the QK product runs in f16: head n's q is scaled by a power of two
+    // 2^qs (max |q| lands in [2^13, 2^14), far inside f16's range; the
+    // conversion is exact for every element within 2^27 of the max) and the
+    // score scale is divided by the same power of two.
+    QkOperand<FMT> qb[2 * KJ];
+    float cs = a.qk_scale_log2;
     {
         const int h = g * G + n;
         const uint16_t* qrow = a.q + ((int64_t)b * a.Hq + h) * D;
+        u32x4 qw[2 * KJ];
 #pragma unroll
         for (int j = 0; j < KJ; ++j)
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 u32x4 w = {0u, 0u, 0u, 0u};
                 if (n < G) w = *reinterpret_cast<const u32x4*>(qrow + 64 * j + 16 * grp + 8 * hh);
-                qb[2 * j + hh] = __builtin_bit_cast(bf16x8, w);
+                qw[2 * j + hh] = w;
             }
+        if constexpr (FMT == kFmtNVFP4) {
+            float qmax = 0.f;
+#pragma unroll
+            for (int k = 0; k < 2 * KJ; ++k)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    qmax = fmaxf(qmax, fmaxf(__builtin_fabsf(bf16_lo(qw[k][e])), __builtin_fabsf(bf16_hi(qw[k][e]))));
+            qmax = fmaxf(qmax, shfl_xor(qmax, 16));
+            qmax = fmaxf(qmax, shfl_xor(qmax, 32));
+            // exponent of qmax: qmax = m * 2^ex with m in [0.5, 1)
+            const int ex = qmax > 0.f ? __builtin_amdgcn_frexp_expf(qmax) : 0;
+            const int qs = min(14 - ex, 100);   // denormal-only rows stay finite
+            const float up = __builtin_ldexpf(1.0f, qs);
+            cs = __builtin_ldexpf(cs, -qs);
+#pragma unroll
+            for (int k = 0; k < 2 * KJ; ++k) {
+                f16x8 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[2 * e] = (_Float16)(bf16_lo(qw[k][e]) * up);
+                    v[2 * e + 1] = (_Float16)(bf16_hi(qw[k][e]) * up);
+                }
+                qb[k] = v;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 2 * KJ; ++k) qb[k] = __builtin_bit_cast(bf16x8, qw[k]);
+        }
     }
     __syncthreads();
 
@@ -342,14 +457,13 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
     for (int dt = 0; dt < DT; ++dt) st.acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     st.m_run = -INFINITY;
     st.l_run = 0.f;
-    const float cs = a.qk_scale_log2;
     // this wave's chunks: wave, wave + 4, ...
     const int my = wave < n_chunks ? (n_chunks - wave + kWaves - 1) / kWaves : 0;
 
     if constexpr (kPrefetch) {
         // software pipeline: the next chunk's loads are in flight while the
         // current one is computed; loads are issued only for chunks that exist
-        MfmaChunk<D, FP8> A, Bc;
+        MfmaChunk<D, FMT> A, Bc;
         if (my > 0) {
             mfma_load(A, a, s_blk, wave, g, n, grp);
             int i = 0;
@@ -377,7 +491,7 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
     } else {
         for (int i = 0; i < my; ++i) {
             const int ch = wave + i * kWaves;
-            MfmaChunk<D, FP8> A;
+            MfmaChunk<D, FMT> A;
             mfma_load(A, a, s_blk, ch, g, n, grp);
             mfma_process(st, A, qb, cs, tok_begin + ch * kChunkTokens, tok_end, grp);
         }
@@ -664,15 +778,19 @@ __global__ void __launch_bounds__(kMergeThreads) merge_splits_kernel(DecodeArgs 
     }
 }
 
-template <int D, bool FP8>
+template <int D, int FMT>
 static hipError_t launch_family(const DecodeArgs& a, int B, int impl, hipStream_t st) {
     dim3 grid(a.num_splits, a.Hkv, B);
     size_t lds = sizeof(float) * (kMaxSplitBlocks + lds_merge_floats(a.G, D));
-    if (impl == 2) {
-        hipLaunchKernelGGL((decode_mfma_kernel<D, FP8>), grid, dim3(kThreads), lds, st, a);
+    if constexpr (FMT == kFmtNVFP4) {
+        hipLaunchKernelGGL((decode_mfma_kernel<D, FMT>), grid, dim3(kThreads), lds, st, a);
     } else {
-        lds += sizeof(float) * (a.G * D + kWaves * 256);
-        hipLaunchKernelGGL((decode_valu_kernel<D, FP8>), grid, dim3(kThreads), lds, st, a);
+        if (impl == 2) {
+            hipLaunchKernelGGL((decode_mfma_kernel<D, FMT>), grid, dim3(kThreads), lds, st, a);
+        } else {
+            lds += sizeof(float) * (a.G * D + kWaves * 256);
+            hipLaunchKernelGGL((decode_valu_kernel<D, FMT == kFmtFP8>), grid, dim3(kThreads), lds, st, a);
+        }
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.num_splits <= 1) return e;
@@ -681,11 +799,21 @@ static hipError_t launch_family(const DecodeArgs& a, int B, int impl, hipStream_
     return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int B, int D, bool fp8, int impl, hipStream_t st) {
+template <int FMT>
+static hipError_t launch_d(const DecodeArgs& a, int B, int D, int impl, hipStream_t st) {
     switch (D) {
-        case 64: return fp8 ? launch_family<64, true>(a, B, impl, st) : launch_family<64, false>(a, B, impl, st);
-        case 128: return fp8 ? launch_family<128, true>(a, B, impl, st) : launch_family<128, false>(a, B, impl, st);
-        case 256: return fp8 ? launch_family<256, true>(a, B, impl, st) : launch_family<256, false>(a, B, impl, st);
+        case 64: return launch_family<64, FMT>(a, B, impl, st);
+        case 128: return launch_family<128, FMT>(a, B, impl, st);
+        case 256: return launch_family<256, FMT>(a, B, impl, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int B, int D, int fmt, int impl, hipStream_t st) {
+    switch (fmt) {
+        case kFmtBF16: return launch_d<kFmtBF16>(a, B, D, impl, st);
+        case kFmtFP8: return launch_d<kFmtFP8>(a, B, D, impl, st);
+        case kFmtNVFP4: return launch_d<kFmtNVFP4>(a, B, D, impl, st);
         default: return hipErrorInvalidValue;
     }
 }

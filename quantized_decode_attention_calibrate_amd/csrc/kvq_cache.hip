@@ -168,4 +168,111 @@ hipError_t launch_cache_write(const void* k, const void* v, int64_t src_stride, 
     return hipGetLastError();
 }
 
+// ---- NVFP4 (block-scaled E2M1) cache write --------------------------------
+// The Run 26 video description names the format: a block-scaled 4-bit float
+// with FP8 scale factors, 4.5 bits per number.  Per (token, head) row, each
+// group of 16 consecutive dims gets one E4M3 block scale:
+//   bscale = E4M3(bamax / fp32(6 * gscale)), e = fp32(value(bscale) * gscale),
+//   code_i = E2M1(x_i / e)  (all zero when e == 0).
+// Region per (block, head): K codes [16][D/2], K scales [16][D/16];
+// V codes [D][8] (token 2j in the low nibble), V scales [D/16][16].
+// One thread per (token, head, group).  K bytes and all scale bytes belong to
+// one token; a V code byte holds two tokens, so V nibbles are merged into
+// their 32-bit word with atomicAnd / atomicOr on disjoint bits.
+__global__ void __launch_bounds__(256) nvfp4_cache_write_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t src_stride,
+    const int64_t* __restrict__ slot_mapping, int T, int Hkv, int D, uint8_t* __restrict__ k_cache,
+    uint8_t* __restrict__ v_cache, float k_gscale, float v_gscale) {
+#pragma clang fp contract(off)
+    const int groups = D >> 4;
+    const int64_t per_tok = (int64_t)Hkv * groups;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)T * per_tok) return;
+    const int t = (int)(i / per_tok);
+    const int rem = (int)(i - (int64_t)t * per_tok);
+    const int g = rem / groups;
+    const int grp = rem - g * groups;
+    const int64_t slot = slot_mapping[t];
+    if (slot < 0) return;
+    const int64_t blk = slot / kBlockSize;
+    const int off = (int)(slot - blk * kBlockSize);
+    const int64_t region = (int64_t)kBlockSize * D / 2 + (int64_t)kBlockSize * D / 16;
+    const int64_t codes_bytes = (int64_t)kBlockSize * D / 2;
+    const int64_t src = (int64_t)t * src_stride + (int64_t)g * D + grp * 16;
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+        const uint16_t* x = which == 0 ? k : v;
+        const float gscale = which == 0 ? k_gscale : v_gscale;
+        const u32x4 w0 = *reinterpret_cast<const u32x4*>(x + src);
+        const u32x4 w1 = *reinterpret_cast<const u32x4*>(x + src + 8);
+        float xf[16];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            xf[2 * j] = bf16_lo(w0[j]);
+            xf[2 * j + 1] = bf16_hi(w0[j]);
+            xf[8 + 2 * j] = bf16_lo(w1[j]);
+            xf[8 + 2 * j + 1] = bf16_hi(w1[j]);
+        }
+        float bamax = 0.f;
+        bool nan = false;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const float a = __builtin_fabsf(xf[j]);
+            nan |= __builtin_isnan(a);
+            bamax = a > bamax ? a : bamax;
+        }
+        if (nan) bamax = __builtin_nanf("");
+        const float top = 6.0f * gscale;
+        const uint32_t bcode = e4m3_encode(bamax / top);
+        const float e = e4m3x2_to_f32(bcode, false)[0] * gscale;
+        uint32_t codes[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) codes[j] = e == 0.0f ? 0u : e2m1_encode(xf[j] / e);
+        uint8_t* region_base = (which == 0 ? k_cache : v_cache) + (blk * Hkv + g) * region;
+        if (which == 0) {
+            u32x2 packed = {0u, 0u};
+#pragma unroll
+            for (int j = 0; j < 16; ++j) packed[j >> 3] |= codes[j] << (4 * (j & 7));
+            *reinterpret_cast<u32x2*>(region_base + (int64_t)off * (D / 2) + grp * 8) = packed;
+            region_base[codes_bytes + (int64_t)off * groups + grp] = (uint8_t)bcode;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int64_t byte = (int64_t)(grp * 16 + j) * (kBlockSize / 2) + (off >> 1);
+                const unsigned shift = 8u * (unsigned)(byte & 3) + 4u * (unsigned)(off & 1);
+                unsigned* word = reinterpret_cast<unsigned*>(region_base + (byte & ~(int64_t)3));
+                atomicAnd(word, ~(0xFu << shift));
+                atomicOr(word, codes[j] << shift);
+            }
+            region_base[codes_bytes + (int64_t)grp * kBlockSize + off] = (uint8_t)bcode;
+        }
+    }
+}
+
+hipError_t launch_nvfp4_cache_write(const void* k, const void* v, int64_t src_stride, const int64_t* slots, int T,
+                                    int Hkv, int D, void* k_cache, void* v_cache, float k_gscale, float v_gscale,
+                                    hipStream_t st) {
+    const int64_t threads = (int64_t)T * Hkv * (D >> 4);
+    const unsigned blocks = (unsigned)((threads + 255) / 256);
+    hipLaunchKernelGGL(nvfp4_cache_write_kernel, dim3(blocks), dim3(256), 0, st, (const uint16_t*)k,
+                       (const uint16_t*)v, src_stride, slots, T, Hkv, D, (uint8_t*)k_cache, (uint8_t*)v_cache,
+                       k_gscale, v_gscale);
+    return hipGetLastError();
+}
+
+// ---- E2M1 decode utility: out[2i], out[2i+1] = the two codes of byte i times
+// the E4M3 value of scale_code, computed as the NVFP4 decode kernel does (f16).
+__global__ void __launch_bounds__(256) e2m1_decode_kernel(const uint8_t* __restrict__ codes, uint32_t scale_code,
+                                                          f16x2* __restrict__ out, int64_t n) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const _Float16 sc = e4m3x2_to_f16(scale_code, false)[0];
+    for (; i < n; i += stride) out[i] = e2m1x2_to_f16<0>(codes[i]) * f16x2{sc, sc};
+}
+
+hipError_t launch_e2m1_decode(const uint8_t* codes, uint32_t scale_code, void* out, int64_t n, hipStream_t st) {
+    hipLaunchKernelGGL(e2m1_decode_kernel, dim3(grid_for(n)), dim3(256), 0, st, codes, scale_code, (f16x2*)out, n);
+    return hipGetLastError();
+}
+
 }  // namespace kvq

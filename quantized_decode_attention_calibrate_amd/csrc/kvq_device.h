@@ -78,6 +78,38 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
     return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// ---- E2M1 (4-bit) codec ----------------------------------------------------
+// Values of codes 0..7: 0, 0.5, 1, 1.5, 2, 3, 4, 6 (bit 3 = sign).  Encode:
+// round to nearest, ties to the even code, saturate above 6 (Inf too), NaN ->
+// 7 with its sign.  Each comparison is one rounding boundary; `>` at a tie
+// rounds down to the even code below, `>=` rounds up to the even code above.
+__device__ __forceinline__ uint32_t e2m1_encode(float y) {
+    const float a = __builtin_fabsf(y);
+    const uint32_t s = (f32_bits(y) >> 28) & 0x8u;
+    if (__builtin_isnan(y)) return 0x7u | s;
+    const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                       (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+    return c | s;
+}
+
+// Two E2M1 codes (byte `SEL` of w, low nibble first) as exact f16 values.  The
+// conversion's scale operand is applied as a power of two only (it is meant
+// for power-of-two microscaling), so E4M3 block scales are applied separately
+// with an f16 multiply: a 2-bit E2M1 significand times a 4-bit E4M3 scale has
+// at most 6 significant bits and lies in [2^-10, 2688], exact in f16.
+template <int SEL>
+__device__ __forceinline__ f16x2 e2m1x2_to_f16(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
+}
+
+// 8 codes (one word, element order = nibble order) times one f16 scale.
+__device__ __forceinline__ f16x8 e2m1x8_scaled_f16(uint32_t w, _Float16 scale) {
+    const f16x2 s = {scale, scale};
+    const f16x2 a = e2m1x2_to_f16<0>(w) * s, b = e2m1x2_to_f16<1>(w) * s;
+    const f16x2 c = e2m1x2_to_f16<2>(w) * s, d = e2m1x2_to_f16<3>(w) * s;
+    return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
 // ---- wave helpers ----------------------------------------------------------
 __device__ __forceinline__ float shfl_xor(float v, int mask) {
     int lane = __lane_id();

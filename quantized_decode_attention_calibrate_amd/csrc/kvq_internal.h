@@ -18,6 +18,8 @@ constexpr int kMaxSplitTokens = 8192;
 // Most splits one call may have (the merge keeps one weight per split in LDS).
 constexpr int kMaxSplits = 16384;
 constexpr int kChunkTokens = 64;   // tokens per wave iteration (4 blocks of 16)
+// KV cache formats of the decode kernels
+enum : int { kFmtBF16 = 0, kFmtFP8 = 1, kFmtNVFP4 = 2 };
 constexpr int kBlockSize = 16;
 
 struct DecodeArgs {
@@ -50,7 +52,12 @@ hipError_t launch_e4m3_decode(const uint8_t* codes, void* out, int kind, int64_t
 hipError_t launch_cache_write(const void* k, const void* v, int64_t src_stride, const int64_t* slots, int T,
                               int Hkv, int D, void* k_cache, void* v_cache, int bs, int kv_dtype,
                               float k_scale, float v_scale, hipStream_t st);
+hipError_t launch_nvfp4_cache_write(const void* k, const void* v, int64_t src_stride, const int64_t* slots, int T,
+                                    int Hkv, int D, void* k_cache, void* v_cache, float k_gscale, float v_gscale,
+                                    hipStream_t st);
+hipError_t launch_e2m1_decode(const uint8_t* codes, uint32_t scale_code, void* out, int64_t n, hipStream_t st);
 // impl: 1 = VALU, 2 = MFMA.  B is the grid's z extent.
-hipError_t launch_decode(const DecodeArgs& a, int B, int D, bool fp8, int impl, hipStream_t st);
+// fmt: kFmtBF16 / kFmtFP8 / kFmtNVFP4 (NVFP4 has the MFMA family only)
+hipError_t launch_decode(const DecodeArgs& a, int B, int D, int fmt, int impl, hipStream_t st);
 
 }  // namespace kvq

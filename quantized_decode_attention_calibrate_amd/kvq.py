@@ -49,6 +49,13 @@ def _load() -> ctypes.CDLL:
         "kvq_paged_decode_attn": (I, [P, P, P, I, P, I, P, I, I, I, I, I, I, I, F, F, F, P, I, P, SZ, P]),
         "kvq_paged_decode_attn_ex": (I, [P, P, P, I, P, I, P, I, I, I, I, I, I, I, F, F, F, P, I, P, SZ, P,
                                          I, I]),
+        "kvq_nvfp4_calibrate": (I, [P, P, I]),
+        "kvq_nvfp4_region_bytes": (SZ, [I, I]),
+        "kvq_nvfp4_cache_write": (I, [P, P, I64, P, I, I, I, P, P, I, I, F, F, P]),
+        "kvq_nvfp4_paged_decode_attn": (I, [P, P, P, P, I, P, I, I, I, I, I, I, I, F, F, F, P, I, P, SZ, P]),
+        "kvq_nvfp4_paged_decode_attn_ex": (I, [P, P, P, P, I, P, I, I, I, I, I, I, I, F, F, F, P, I, P, SZ, P,
+                                               I]),
+        "kvq_e2m1_decode": (I, [P, ctypes.c_uint8, P, I64, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -111,14 +118,68 @@ def kvq_amax_bf16(x: torch.Tensor, amax: torch.Tensor, stream=None) -> None:
                                                 _stream(stream)))
 
 
-def kvq_calibrate(amax) -> list:
-    """Host-only: per-layer scales from observed maxima (list of floats)."""
+def _host_scales(fn_name: str, amax) -> list:
     vals = [float(a) for a in amax]
     n = len(vals)
     src = (ctypes.c_float * n)(*vals)
     dst = (ctypes.c_float * n)()
-    _check("kvq_calibrate", _lib.kvq_calibrate(ctypes.addressof(src), ctypes.addressof(dst), n))
+    _check(fn_name, getattr(_lib, fn_name)(ctypes.addressof(src), ctypes.addressof(dst), n))
     return list(dst)
+
+
+def kvq_nvfp4_calibrate(amax) -> list:
+    """Host-only: per-tensor NVFP4 global scales from observed maxima."""
+    return _host_scales("kvq_nvfp4_calibrate", amax)
+
+
+def kvq_nvfp4_region_bytes(D: int) -> int:
+    return _lib.kvq_nvfp4_region_bytes(D, BLOCK_SIZE)
+
+
+def new_nvfp4_caches(num_blocks: int, Hkv: int, D: int, device="cuda"):
+    """Uninitialised NVFP4 K and V caches [num_blocks][Hkv][region] bytes."""
+    r = kvq_nvfp4_region_bytes(D)
+    return (torch.empty((num_blocks, Hkv, r), dtype=torch.uint8, device=device),
+            torch.empty((num_blocks, Hkv, r), dtype=torch.uint8, device=device))
+
+
+def kvq_nvfp4_cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, k_cache: torch.Tensor,
+                          v_cache: torch.Tensor, k_gscale: float, v_gscale: float, stream=None) -> None:
+    assert k.dtype == torch.bfloat16 and v.dtype == torch.bfloat16 and slot_mapping.dtype == torch.int64
+    T, Hkv, D = k.shape
+    assert v.shape == k.shape and k.stride(0) == v.stride(0) and k.stride(2) == 1 and k.stride(1) == D
+    assert slot_mapping.shape == (T,) and slot_mapping.is_contiguous()
+    _check("kvq_nvfp4_cache_write", _lib.kvq_nvfp4_cache_write(
+        _ptr(k), _ptr(v), k.stride(0), _ptr(slot_mapping), T, Hkv, D, _ptr(k_cache), _ptr(v_cache),
+        k_cache.shape[0], BLOCK_SIZE, k_gscale, v_gscale, _stream(stream)))
+
+
+def kvq_nvfp4_paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                block_tables: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, Hkv: int,
+                                k_gscale: float, v_gscale: float, sm_scale: float, out: torch.Tensor,
+                                workspace: torch.Tensor, split_tokens: int = 0, stream=None) -> None:
+    B, Hq, D = q.shape
+    assert q.dtype == torch.bfloat16 and q.is_contiguous() and out.is_contiguous() and out.shape == q.shape
+    assert block_tables.dtype == torch.int32 and block_tables.is_contiguous() and block_tables.shape[0] == B
+    assert seq_lens.dtype == torch.int32 and seq_lens.shape == (B,)
+    out_dtype = {torch.bfloat16: KVQ_OUT_BF16, torch.float32: KVQ_OUT_F32}[out.dtype]
+    _check("kvq_nvfp4_paged_decode_attn", _lib.kvq_nvfp4_paged_decode_attn_ex(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens),
+        max_seq_len, B, Hq, Hkv, D, BLOCK_SIZE, k_cache.shape[0], k_gscale, v_gscale, sm_scale, _ptr(out),
+        out_dtype, _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream), split_tokens))
+
+
+def kvq_e2m1_decode(codes: torch.Tensor, scale_code: int, out: torch.Tensor, stream=None) -> None:
+    """out (f16, 2 per byte) = E2M1 codes times the E4M3 value of scale_code."""
+    assert codes.dtype == torch.uint8 and codes.is_contiguous() and out.is_contiguous()
+    assert out.dtype == torch.float16 and out.numel() >= 2 * codes.numel()
+    _check("kvq_e2m1_decode", _lib.kvq_e2m1_decode(_ptr(codes), scale_code, _ptr(out), codes.numel(),
+                                                    _stream(stream)))
+
+
+def kvq_calibrate(amax) -> list:
+    """Host-only: per-layer scales from observed maxima (list of floats)."""
+    return _host_scales("kvq_calibrate", amax)
 
 
 def new_caches(kv_dtype: int, num_blocks: int, Hkv: int, D: int, device="cuda"):

@@ -125,3 +125,26 @@ def test_plan_and_workspace(K):
             want = pad(B * Hq * SS * 8) + B * Hq * SS * D * 4
             assert K.kvq_decode_workspace_bytes(B, Hq, Hkv, D, L, sp) == want
     assert K.kvq_decode_workspace_bytes(1, 8, 2, 64, 100, 100) == 0   # not a multiple of 64
+
+
+def test_nvfp4_host_calls(K):
+    rng = np.random.default_rng(5)
+    amax = np.concatenate([rng.uniform(0, 50, 300), 10.0 ** rng.uniform(-15, 5, 300), [0.0]]).astype(np.float32)
+    ours = np.array(K.kvq_nvfp4_calibrate(amax.tolist()), dtype=np.float32)
+    assert np.array_equal(ours.view(np.uint32), oracle.nvfp4_calibrate(amax).view(np.uint32))
+    with pytest.raises(K.KvqError):
+        K.kvq_nvfp4_calibrate([float("nan")])
+    for D in (64, 128, 256):
+        assert K.kvq_nvfp4_region_bytes(D) == oracle.nvfp4_region_bytes(D, 16) == 9 * D
+    L = K.lib()
+    args = [FAKE, FAKE, 128, FAKE, 5, 2, 64, FAKE, FAKE, 4, 16, 0.5, 0.5, None]
+    assert L.kvq_nvfp4_cache_write(*args[:11], 0.0, 0.5, None) == -1
+    assert L.kvq_nvfp4_cache_write(*args[:6], 96, *args[7:]) == -2
+    assert L.kvq_nvfp4_cache_write(None, *args[1:]) == -1
+    a = [FAKE, FAKE, FAKE, FAKE, 8, FAKE, 100, 2, 8, 2, 64, 16, 10, 0.5, 0.5, 0.125, FAKE, 0, FAKE, 1 << 30, None, 0]
+    assert L.kvq_nvfp4_paged_decode_attn_ex(*a[:13], -1.0, *a[14:]) == -1
+    assert L.kvq_nvfp4_paged_decode_attn_ex(*a[:19], 64, None, 0) == -3
+    assert L.kvq_nvfp4_paged_decode_attn_ex(*a[:10], 80, *a[11:]) == -2
+    assert L.kvq_e2m1_decode(FAKE, 0x38, FAKE, -1, None) == -1
+    assert L.kvq_e2m1_decode(FAKE, 0x38, FAKE + 2, 4, None) == -1
+    assert L.kvq_e2m1_decode(None, 0x38, None, 0, None) == 0
