@@ -31,6 +31,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+NVFP4 = 2            # cache format tag for Layers (the C ABI has separate NVFP4 calls)
+NVFP4_BYTES = 0.5625  # 4.5 bits per element: E2M1 code + one E4M3 scale per 16
 METRIC = "FP8 paged decode-attn achieved HBM GB/s (% of peak) + KV tokens scanned/s"
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["quantized_decode_attention_calibrate_amd/csrc/kvq_attn.hip",
@@ -53,13 +55,13 @@ def step_bytes(B, Hq, Hkv, D, seq_lens, kv_elem_bytes, n_new):
     table = sum((L + 15) // 16 for L in seq_lens) * 4 + B * 4
     qo = 2 * B * Hq * D * 2
     write = n_new * (Hkv * D * 2 * 2 + Hkv * D * 2 * kv_elem_bytes + 8)
-    return kv + table + qo, write
+    return int(kv + table + qo), int(write)
 
 
 def layers_for(w, kv_elem_bytes, cap=12):
     """Enough distinct layer caches that one rotation exceeds 1 GiB (beyond the
     256 MB last-level cache), at most `cap`."""
-    per_layer = sum(w.seq_lens) * w.Hkv * w.D * 2 * kv_elem_bytes
+    per_layer = int(sum(w.seq_lens) * w.Hkv * w.D * 2 * kv_elem_bytes)
     return max(2, min(cap, -(-(1 << 30) // max(per_layer, 1))))
 
 
@@ -73,11 +75,13 @@ class Layers:
         k, v = w.k.to(dev), w.v.to(dev)
         self.bt = w.block_tables.to(dev)
         self.sl = torch.tensor(w.seq_lens, dtype=torch.int32, device=dev)
-        if kv_dtype == K.KVQ_KV_FP8_E4M3:
+        self.nvfp4 = kv_dtype == NVFP4
+        if kv_dtype != K.KVQ_KV_BF16:
             amax = torch.zeros(2, dtype=torch.float32, device=dev)
             K.kvq_amax_bf16(k, amax[0:1])
             K.kvq_amax_bf16(v, amax[1:2])
-            self.ks, self.vs = K.kvq_calibrate(amax.cpu().tolist())
+            cal = K.kvq_nvfp4_calibrate if self.nvfp4 else K.kvq_calibrate
+            self.ks, self.vs = cal(amax.cpu().tolist())
         else:
             self.ks, self.vs = 1.0, 1.0
         rows = w.last_token_rows()
@@ -88,8 +92,12 @@ class Layers:
         self.caches = []
         pre = w.prefill_slots().to(dev)
         for _ in range(R):
-            kc, vc = K.new_caches(kv_dtype, w.num_blocks, w.Hkv, w.D, device=dev)
-            K.kvq_cache_write(k, v, pre, kc, vc, kv_dtype, self.ks, self.vs)
+            if self.nvfp4:
+                kc, vc = K.new_nvfp4_caches(w.num_blocks, w.Hkv, w.D, device=dev)
+                K.kvq_nvfp4_cache_write(k, v, pre, kc, vc, self.ks, self.vs)
+            else:
+                kc, vc = K.new_caches(kv_dtype, w.num_blocks, w.Hkv, w.D, device=dev)
+                K.kvq_cache_write(k, v, pre, kc, vc, kv_dtype, self.ks, self.vs)
             self.caches.append((kc, vc))
         del k, v
         self.out = torch.empty(w.B, w.Hq, w.D, dtype=torch.bfloat16, device=dev)
@@ -99,13 +107,21 @@ class Layers:
 
     def write(self, i):
         kc, vc = self.caches[i % self.R]
-        self.K.kvq_cache_write(self.new_k, self.new_v, self.new_slots, kc, vc, self.kv_dtype, self.ks, self.vs)
+        if self.nvfp4:
+            self.K.kvq_nvfp4_cache_write(self.new_k, self.new_v, self.new_slots, kc, vc, self.ks, self.vs)
+        else:
+            self.K.kvq_cache_write(self.new_k, self.new_v, self.new_slots, kc, vc, self.kv_dtype, self.ks,
+                                   self.vs)
 
     def attend(self, i, impl=0):
         kc, vc = self.caches[i % self.R]
         w = self.w
-        self.K.kvq_paged_decode_attn(self.q, kc, vc, self.kv_dtype, self.bt, self.sl, w.max_seq_len, w.Hkv,
-                                     self.ks, self.vs, self.sm, self.out, self.ws, impl=impl)
+        if self.nvfp4:
+            self.K.kvq_nvfp4_paged_decode_attn(self.q, kc, vc, self.bt, self.sl, w.max_seq_len, w.Hkv, self.ks,
+                                               self.vs, self.sm, self.out, self.ws)
+        else:
+            self.K.kvq_paged_decode_attn(self.q, kc, vc, self.kv_dtype, self.bt, self.sl, w.max_seq_len, w.Hkv,
+                                         self.ks, self.vs, self.sm, self.out, self.ws, impl=impl)
 
 
 def time_steps(torch, layers, steps, warmup, impl=0):
@@ -135,13 +151,16 @@ def time_steps(torch, layers, steps, warmup, impl=0):
     return step_ms, sum(attn_ms) / len(attn_ms), attn_ms[len(attn_ms) // 2]
 
 
-def measure_workload(torch, K, name, steps, warmup):
+def measure_workload(torch, K, name, steps, warmup, with_nvfp4=False):
     """FP8 and BF16 attention-call time for one workload (compact record)."""
     from quantized_decode_attention_calibrate_amd import workloads
     w = workloads.make(name, device="cuda", seed=0)
     rec = {"B": w.B, "max_seq_len": w.max_seq_len, "kv_tokens": sum(w.seq_lens), "Hq": w.Hq, "Hkv": w.Hkv,
            "D": w.D, "split_tokens": K.kvq_decode_plan_split_tokens(w.B, w.Hkv, w.max_seq_len)}
-    for kv, tag, eb in ((K.KVQ_KV_FP8_E4M3, "fp8", 1), (K.KVQ_KV_BF16, "bf16", 2)):
+    fmts = [(K.KVQ_KV_FP8_E4M3, "fp8", 1), (K.KVQ_KV_BF16, "bf16", 2)]
+    if with_nvfp4:
+        fmts.append((NVFP4, "nvfp4", NVFP4_BYTES))
+    for kv, tag, eb in fmts:
         L = Layers(K, w, kv, layers_for(w, eb), "cuda")
         step_ms, attn_ms, _ = time_steps(torch, L, steps, warmup)
         attn_b, write_b = step_bytes(w.B, w.Hq, w.Hkv, w.D, w.seq_lens, eb, w.B)
@@ -151,6 +170,8 @@ def measure_workload(torch, K, name, steps, warmup):
         del L
         torch.cuda.empty_cache()
     rec["fp8_over_bf16_attn_time"] = round(rec["fp8"]["attn_us"] / rec["bf16"]["attn_us"], 3)
+    if with_nvfp4:
+        rec["nvfp4_over_fp8_attn_time"] = round(rec["nvfp4"]["attn_us"] / rec["fp8"]["attn_us"], 3)
     rec["fp8_kv_tokens_per_s"] = round(rec["kv_tokens"] / (rec["fp8"]["attn_us"] * 1e-6), 1)
     del w
     torch.cuda.empty_cache()
@@ -275,7 +296,7 @@ def main():
         result["workloads"] = {}
         for name in ("agents126k", "mixed64", "nvfp4_131k"):
             print(f"[bench] workload {name}", file=sys.stderr, flush=True)
-            result["workloads"][name] = measure_workload(torch, K, name, 60, 10)
+            result["workloads"][name] = measure_workload(torch, K, name, 60, 10, with_nvfp4=name == "nvfp4_131k")
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         w_cpu = workloads.make(args.workload, device="cpu", seed=0)

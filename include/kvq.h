@@ -149,6 +149,7 @@ int kvq_cache_write(const void* k_dev, const void* v_dev, int64_t src_token_stri
  *   block_tables_dev   int32 [B][max_blocks_per_seq]; entries past a sequence's
  *                      last block are not read
  *   seq_lens_dev       int32 [B]
+ *   sm_scale           softmax scale, finite and > 0 (usually 1/sqrt(D))
  *   max_seq_len        host upper bound of seq_lens (sizes the grid; no
  *                      device-to-host copy happens); must be
  *                      <= max_blocks_per_seq * block_size

@@ -205,7 +205,7 @@ static int decode_common(int fmt, const void* q_dev, const void* k_cache_dev, co
     const int G = Hq / Hkv;
     if (G > 16) return KVQ_EUNSUPPORTED;
     if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * block_size) return KVQ_EINVAL;
-    if (!isfinite(sm_scale)) return KVQ_EINVAL;
+    if (!isfinite(sm_scale) || !(sm_scale > 0.0f)) return KVQ_EINVAL;
     if (fmt != kFmtBF16 && (!good_scale(k_scale) || !good_scale(v_scale))) return KVQ_EINVAL;
     if (B == 0) return KVQ_OK;
     if (!q_dev || !k_cache_dev || !v_cache_dev || !block_tables_dev || !seq_lens_dev || !out_dev ||

@@ -33,23 +33,30 @@
 
 namespace kvq {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;                 // VALU family work-group
 constexpr int kThreads = kWaves * 64;
+// MFMA family: 8 waves per work-group for NVFP4 at D = 64, else 4.  The
+// 4-bit path spends about twice the VALU work per byte of the FP8 path, and
+// a second wave per SIMD hides it (measured 44 -> 42 us on a 2 x 131k-token
+// decode); for FP8 and BF16 the extra waves only shorten each wave's chunk
+// run and were measured neutral to slightly slower.
+template <int D, int FMT>
+constexpr int mfma_waves() { return (FMT == kFmtNVFP4 && D == 64) ? 8 : 4; }
 constexpr int kMaxSplitBlocks = kMaxSplitTokens / kBlockSize;
 
 // LDS layout shared by both families (dynamic shared memory):
 //   int   blk[kMaxSplitBlocks]          physical block ids of this split
-//   float m[kWaves][16], l[kWaves][16]  per-wave softmax state per head
-//   float acc[kWaves][G][D]             per-wave unnormalised outputs
-//   (VALU only) float q[G][D], p[kWaves][16][16]
-__host__ __device__ constexpr int lds_merge_floats(int G, int D) { return kWaves * 32 + kWaves * G * D; }
+//   float m[W][16], l[W][16]            per-wave softmax state per head (W waves)
+//   float acc[W][G][D]                  per-wave unnormalised outputs
+//   (VALU only) float q[G][D], p[W][16][16]
+__host__ __device__ constexpr int lds_merge_floats(int G, int D, int W) { return W * 32 + W * G * D; }
 
 // Stage the physical block ids of logical blocks [lb0, lb0 + n) into LDS,
 // clamping logical blocks past the sequence to its last block (those tokens
 // are masked; the clamp only keeps every address inside the cache).
 __device__ __forceinline__ void stage_block_ids(int* s_blk, const int32_t* bt_row, int lb0, int n,
                                                 int last_lb) {
-    for (int i = threadIdx.x; i < n; i += kThreads) {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
         int lb = min(lb0 + i, last_lb);
         s_blk[i] = bt_row[lb];
     }
@@ -65,18 +72,19 @@ __device__ __forceinline__ void store_out(const DecodeArgs& a, int64_t o, float 
         reinterpret_cast<uint16_t*>(a.out)[o] = (uint16_t)f32_to_bf16_rne(v);
 }
 
+template <int W>
 __device__ __forceinline__ void finish_split(const DecodeArgs& a, const float* s_m, const float* s_l,
                                              const float* s_acc, int b, int g, int s, int S, int D) {
     const int G = a.G;
     const int64_t hq0 = (int64_t)b * a.Hq + (int64_t)g * G;
-    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+    for (int idx = threadIdx.x; idx < G * D; idx += W * 64) {
         const int h = idx / D, d = idx - h * D;
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w * 16 + h]);
+        for (int w = 0; w < W; ++w) M = fmaxf(M, s_m[w * 16 + h]);
         float acc = 0.f, l = 0.f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
+        for (int w = 0; w < W; ++w) {
             const float mw = s_m[w * 16 + h];
             const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
             acc += f * s_acc[(w * G + h) * D + d];
@@ -97,7 +105,7 @@ __device__ __forceinline__ void finish_split(const DecodeArgs& a, const float* s
 // A sequence with no tokens: work-group (split 0) writes zeros for its heads.
 __device__ __forceinline__ void write_empty(const DecodeArgs& a, int b, int g, int D) {
     const int64_t hq0 = (int64_t)b * a.Hq + (int64_t)g * a.G;
-    for (int idx = threadIdx.x; idx < a.G * D; idx += kThreads) store_out(a, hq0 * D + idx, 0.f);
+    for (int idx = threadIdx.x; idx < a.G * D; idx += blockDim.x) store_out(a, hq0 * D + idx, 0.f);
 }
 
 // =============================================================================
@@ -260,20 +268,26 @@ __device__ __forceinline__ void mfma_process(MfmaState<D>& st, MfmaChunk<D, FMT>
                     t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(c, i, j, hh), qb[2 * j + hh], t, 0, 0, 0);
             }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sv[4 * i + r] = t[r] * cs;
+        for (int r = 0; r < 4; ++r) sv[4 * i + r] = t[r];   // raw scores; scaled inside the exp
     }
 
     // ---- online softmax over this chunk (head n, chunk block grp) -----------
+    // The score scale cs (> 0) is applied as exp2(fma(s, cs, -m)); the running
+    // max m is kept in scaled units.  Masking runs only on the sequence's last
+    // chunk (a wave-uniform branch).
     const int valid = tok_end - (chunk_tok + 16 * grp);  // tokens of block grp in range
-    float mloc = -INFINITY;
+    const bool tail = chunk_tok + kChunkTokens > tok_end;
+    if (tail) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {  // sv[4i + r] is token offset 4i + r of block grp
-        if (e >= valid) sv[e] = -INFINITY;
-        mloc = fmaxf(mloc, sv[e]);
+        for (int e = 0; e < 16; ++e)  // sv[4i + r] is token offset 4i + r of block grp
+            if (e >= valid) sv[e] = -INFINITY;
     }
+    float mloc = sv[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mloc = fmaxf(mloc, sv[e]);
     mloc = fmaxf(mloc, shfl_xor(mloc, 16));
     mloc = fmaxf(mloc, shfl_xor(mloc, 32));
-    const float m_new = fmaxf(st.m_run, mloc);
+    const float m_new = fmaxf(st.m_run, mloc * cs);
     const float alpha = fast_exp2(st.m_run - m_new);
     st.m_run = m_new;
 
@@ -290,8 +304,8 @@ __device__ __forceinline__ void mfma_process(MfmaState<D>& st, MfmaChunk<D, FMT>
     for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
-            const float p0 = fast_exp2(sv[8 * hh + 2 * e2] - m_off);
-            const float p1 = fast_exp2(sv[8 * hh + 2 * e2 + 1] - m_off);
+            const float p0 = fast_exp2(__builtin_fmaf(sv[8 * hh + 2 * e2], cs, -m_off));
+            const float p1 = fast_exp2(__builtin_fmaf(sv[8 * hh + 2 * e2 + 1], cs, -m_off));
             psum += p0 + p1;
             if constexpr (kF16V) {
                 const f16x2 h = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(p0, p1));
@@ -315,7 +329,7 @@ __device__ __forceinline__ void mfma_process(MfmaState<D>& st, MfmaChunk<D, FMT>
     // Zero V data of tokens past the end: their weight is 0 but the bytes may be
     // anything (NaN codes).  FP8: V bytes; NVFP4: the tokens' block scales (the
     // E2M1 codes are always finite); BF16: V halfwords.
-    if (valid < 16) {
+    if (tail) {
         if constexpr (FMT == kFmtBF16) {
             u32x4 keep[2];
 #pragma unroll
@@ -372,8 +386,8 @@ __device__ __forceinline__ void mfma_process(MfmaState<D>& st, MfmaChunk<D, FMT>
     }
 }
 
-template <int D, int FMT>
-__global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
+template <int D, int FMT, int W = mfma_waves<D, FMT>()>
+__global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
     constexpr int KJ = D / 64;
     constexpr int DT = D / 16;
     // two chunks in flight per wave where the registers allow it
@@ -381,8 +395,8 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
     extern __shared__ float lds[];
     int* s_blk = reinterpret_cast<int*>(lds);
     float* s_m = lds + kMaxSplitBlocks;
-    float* s_l = s_m + kWaves * 16;
-    float* s_acc = s_l + kWaves * 16;
+    float* s_l = s_m + W * 16;
+    float* s_acc = s_l + W * 16;
 
     const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int L = a.seq_lens[b];
@@ -458,39 +472,31 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
     st.m_run = -INFINITY;
     st.l_run = 0.f;
     // this wave's chunks: wave, wave + 4, ...
-    const int my = wave < n_chunks ? (n_chunks - wave + kWaves - 1) / kWaves : 0;
+    const int my = wave < n_chunks ? (n_chunks - wave + W - 1) / W : 0;
 
     if constexpr (kPrefetch) {
-        // software pipeline: the next chunk's loads are in flight while the
-        // current one is computed; loads are issued only for chunks that exist
+        // Software pipeline: the next chunk's loads are in flight while the
+        // current one is computed.  The prefetch is unconditional so wait
+        // counts stay static: past a wave's last chunk it re-issues that
+        // chunk's addresses (L2 hits; the registers are never read).
         MfmaChunk<D, FMT> A, Bc;
         if (my > 0) {
-            mfma_load(A, a, s_blk, wave, g, n, grp);
-            int i = 0;
-            for (;;) {
-                const int ch = wave + i * kWaves;
-                if (i + 1 < my) {
-                    mfma_load(Bc, a, s_blk, ch + kWaves, g, n, grp);
-                    mfma_process(st, A, qb, cs, tok_begin + ch * kChunkTokens, tok_end, grp);
-                    ++i;
-                } else {
-                    mfma_process(st, A, qb, cs, tok_begin + ch * kChunkTokens, tok_end, grp);
-                    break;
-                }
-                const int ch2 = wave + i * kWaves;
-                if (i + 1 < my) {
-                    mfma_load(A, a, s_blk, ch2 + kWaves, g, n, grp);
-                    mfma_process(st, Bc, qb, cs, tok_begin + ch2 * kChunkTokens, tok_end, grp);
-                    ++i;
-                } else {
-                    mfma_process(st, Bc, qb, cs, tok_begin + ch2 * kChunkTokens, tok_end, grp);
-                    break;
-                }
+            int ch = wave;
+            mfma_load(A, a, s_blk, ch, g, n, grp);
+            for (int i = 0; i < my; i += 2) {
+                const int chb = i + 1 < my ? ch + W : ch;
+                mfma_load(Bc, a, s_blk, chb, g, n, grp);
+                mfma_process(st, A, qb, cs, tok_begin + ch * kChunkTokens, tok_end, grp);
+                if (i + 1 >= my) break;
+                const int cha = i + 2 < my ? chb + W : chb;
+                mfma_load(A, a, s_blk, cha, g, n, grp);
+                mfma_process(st, Bc, qb, cs, tok_begin + chb * kChunkTokens, tok_end, grp);
+                ch = cha;
             }
         }
     } else {
         for (int i = 0; i < my; ++i) {
-            const int ch = wave + i * kWaves;
+            const int ch = wave + i * W;
             MfmaChunk<D, FMT> A;
             mfma_load(A, a, s_blk, ch, g, n, grp);
             mfma_process(st, A, qb, cs, tok_begin + ch * kChunkTokens, tok_end, grp);
@@ -512,7 +518,7 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
             for (int r = 0; r < 4; ++r) s_acc[(wave * G + n) * D + 16 * dt + 4 * grp + r] = st.acc[dt][r];
     }
     __syncthreads();
-    finish_split(a, s_m, s_l, s_acc, b, g, s, S, D);
+    finish_split<W>(a, s_m, s_l, s_acc, b, g, s, S, D);
 }
 
 // =============================================================================
@@ -698,7 +704,7 @@ __global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeArgs a) {
         for (int e = 0; e < VD; ++e) s_acc[(wave * G + h) * D + lane + 64 * e] = acc[h][e];
     }
     __syncthreads();
-    finish_split(a, s_m, s_l, s_acc, b, g, s, S, D);
+    finish_split<kWaves>(a, s_m, s_l, s_acc, b, g, s, S, D);
 }
 
 // =============================================================================
@@ -781,14 +787,16 @@ __global__ void __launch_bounds__(kMergeThreads) merge_splits_kernel(DecodeArgs 
 template <int D, int FMT>
 static hipError_t launch_family(const DecodeArgs& a, int B, int impl, hipStream_t st) {
     dim3 grid(a.num_splits, a.Hkv, B);
-    size_t lds = sizeof(float) * (kMaxSplitBlocks + lds_merge_floats(a.G, D));
+    constexpr int W = mfma_waves<D, FMT>();
+    const size_t lds_mfma = sizeof(float) * (kMaxSplitBlocks + lds_merge_floats(a.G, D, W));
     if constexpr (FMT == kFmtNVFP4) {
-        hipLaunchKernelGGL((decode_mfma_kernel<D, FMT>), grid, dim3(kThreads), lds, st, a);
+        hipLaunchKernelGGL((decode_mfma_kernel<D, FMT>), grid, dim3(W * 64), lds_mfma, st, a);
     } else {
         if (impl == 2) {
-            hipLaunchKernelGGL((decode_mfma_kernel<D, FMT>), grid, dim3(kThreads), lds, st, a);
+            hipLaunchKernelGGL((decode_mfma_kernel<D, FMT>), grid, dim3(W * 64), lds_mfma, st, a);
         } else {
-            lds += sizeof(float) * (a.G * D + kWaves * 256);
+            const size_t lds = sizeof(float) * (kMaxSplitBlocks + lds_merge_floats(a.G, D, kWaves) + a.G * D +
+                                                kWaves * 256);
             hipLaunchKernelGGL((decode_valu_kernel<D, FMT == kFmtFP8>), grid, dim3(kThreads), lds, st, a);
         }
     }

@@ -58,7 +58,7 @@ def attn(K, **over):
 @pytest.mark.parametrize("over,status", [
     (dict(q=None), -1), (dict(ws=None), -1), (dict(Hq=7), -1), (dict(kv=2), -1), (dict(od=3), -1),
     (dict(D=96), -2), (dict(bs=32), -2), (dict(Hq=34, Hkv=2), -2), (dict(msl=8 * 16 + 1), -1),
-    (dict(ks=0.0), -1), (dict(vs=float("nan")), -1), (dict(sm=float("inf")), -1), (dict(wsb=64), -3),
+    (dict(ks=0.0), -1), (dict(vs=float("nan")), -1), (dict(sm=float("inf")), -1), (dict(sm=0.0), -1), (dict(sm=-0.125), -1), (dict(wsb=64), -3),
     (dict(q=FAKE + 8), -1), (dict(impl=3), -1), (dict(split=100), -1), (dict(split=16384), -1),
     (dict(B=-1), -1), (dict(nb=0), -1), (dict(msl=64 * 16385, mb=70000, split=64), -2),
 ])
