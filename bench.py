@@ -139,16 +139,16 @@ def time_steps(torch, layers, steps, warmup, impl=0):
     t1.record(st)
     torch.cuda.synchronize()
     step_ms = t0.elapsed_time(t1) / steps
-    # attention calls alone, bracketed one by one (dominant kernel's launch duration)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    # the attention call alone (split kernel + merge kernel), back to back over
+    # the rotated layer caches: its mean launch duration on the launch stream
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record(st)
     for i in range(steps):
-        layers.write(i)
-        evs[i][0].record(st)
         layers.attend(i, impl)
-        evs[i][1].record(st)
+    a1.record(st)
     torch.cuda.synchronize()
-    attn_ms = sorted(a.elapsed_time(b) for a, b in evs)
-    return step_ms, sum(attn_ms) / len(attn_ms), attn_ms[len(attn_ms) // 2]
+    attn_ms = a0.elapsed_time(a1) / steps
+    return step_ms, attn_ms
 
 
 def measure_workload(torch, K, name, steps, warmup, with_nvfp4=False):
@@ -162,7 +162,7 @@ def measure_workload(torch, K, name, steps, warmup, with_nvfp4=False):
         fmts.append((NVFP4, "nvfp4", NVFP4_BYTES))
     for kv, tag, eb in fmts:
         L = Layers(K, w, kv, layers_for(w, eb), "cuda")
-        step_ms, attn_ms, _ = time_steps(torch, L, steps, warmup)
+        step_ms, attn_ms = time_steps(torch, L, steps, warmup)
         attn_b, write_b = step_bytes(w.B, w.Hq, w.Hkv, w.D, w.seq_lens, eb, w.B)
         rec[tag] = {"attn_us": round(attn_ms * 1e3, 2), "attn_gbps": round(attn_b / (attn_ms * 1e-3) / 1e9, 1),
                     "pct_of_hbm_peak": round(100 * attn_b / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1),
@@ -214,7 +214,79 @@ def read_traffic(kernel_hash):
     return d.get("hbm_bytes_per_launch")
 
 
+PMC_REF_CODES = 32 << 20
+
+
+def pmc_reference(torch, K):
+    """One dispatch of known HBM traffic for scaling PMC byte counters:
+    kvq_e4m3_decode of 32 MiB of codes into 64 MiB of f16 (plain coalesced
+    16-byte loads and stores).  Runs once at set-up, outside every timed region."""
+    codes = torch.full((PMC_REF_CODES,), 0x38, dtype=torch.uint8, device="cuda")
+    out = torch.empty(PMC_REF_CODES, dtype=torch.float16, device="cuda")
+    K.kvq_e4m3_decode(codes, out)
+    torch.cuda.synchronize()
+    del codes, out
+
+
+def _pmc_per_kernel(path, counter):
+    """{kernel short name: [per-dispatch values]} of one rocprofv3 --pmc CSV."""
+    import csv
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter or "kvq::" not in r["Kernel_Name"]:
+                continue
+            name = r["Kernel_Name"].split("(")[0].replace("void ", "").replace("kvq::", "").replace(" ", "")
+            out.setdefault(name, []).append(float(r["Counter_Value"]))
+    return out
+
+
+def pmc_summary(fetch_csv, write_csv, workload="gptoss65k"):
+    """HBM traffic of one decode-attention call from two rocprofv3 --pmc runs
+    of this benchmark (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).  Each
+    counter is scaled by what it reads for the reference dispatch of the same
+    run (pmc_reference: a coalesced kernel of known read and write bytes)."""
+    from quantized_decode_attention_calibrate_amd import workloads
+    w = workloads.make(workload, device="cpu", seed=0)
+    fetch = _pmc_per_kernel(fetch_csv, "FETCH_SIZE")
+    write = _pmc_per_kernel(write_csv, "WRITE_SIZE")
+    med = lambda v: sorted(v)[len(v) // 2]
+    ref = next(k for k in fetch if k.startswith("e4m3_decode_kernel"))
+    fscale = PMC_REF_CODES / (med(fetch[ref]) * 1024)
+    wscale = 2 * PMC_REF_CODES / (med(write[ref]) * 1024)
+    dec = [k for k in fetch if k.startswith("decode_")]
+    mrg = [k for k in fetch if k.startswith("merge_")]
+    f_kib = {k: med(fetch[k]) for k in dec + mrg}
+    w_kib = {k: med(write[k]) for k in dec + mrg}
+    hbm = sum(f_kib.values()) * 1024 * fscale + sum(w_kib.values()) * 1024 * wscale
+    attn_b, _ = step_bytes(w.B, w.Hq, w.Hkv, w.D, w.seq_lens, 1, w.B)
+    return {
+        "about": "HBM traffic of one kvq_paged_decode_attn call (split kernel + merge kernel) on the "
+                 f"{workload} FP8 workload: medians of rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per "
+                 "dispatch), each scaled by the same counter on a plain streaming kernel of known bytes in "
+                 f"the same run (kvq_e4m3_decode: reads {PMC_REF_CODES} B of codes, writes "
+                 f"{2 * PMC_REF_CODES} B of f16).",
+        "kernel_source_hash": kernel_source_hash(),
+        "fetch_size_kib_per_dispatch": f_kib,
+        "write_size_kib_per_dispatch": w_kib,
+        "fetch_scale_factor": round(fscale, 5),
+        "write_scale_factor": round(wscale, 5),
+        "hbm_bytes_per_launch": int(round(hbm)),
+        "algorithmic_bytes_per_launch": attn_b,
+        "traffic_over_algorithmic": round(hbm / attn_b, 4),
+    }
+
+
 def main():
+    if len(sys.argv) >= 2 and sys.argv[1] == "--pmc-summary":
+        # python bench.py --pmc-summary FETCH_CSV WRITE_CSV [OUT_JSON]
+        d = pmc_summary(sys.argv[2], sys.argv[3])
+        text = json.dumps(d, indent=1)
+        if len(sys.argv) > 4:
+            with open(sys.argv[4], "w") as f:
+                f.write(text + "\n")
+        print(text)
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=600)
@@ -240,9 +312,10 @@ def main():
     print(f"[bench] building {args.workload} on {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
     w = workloads.make(args.workload, device=dev, seed=0)
     w_cpu = None
+    pmc_reference(torch, K)
     fp8 = Layers(K, w, K.KVQ_KV_FP8_E4M3, args.layers, dev)
     print("[bench] timing FP8", file=sys.stderr, flush=True)
-    step_ms, attn_ms, attn_med = time_steps(torch, fp8, args.steps, args.warmup, args.impl)
+    step_ms, attn_ms = time_steps(torch, fp8, args.steps, args.warmup, args.impl)
     attn_b, write_b = step_bytes(w.B, w.Hq, w.Hkv, w.D, w.seq_lens, 1, w.B)
     tokens = sum(w.seq_lens)
     gbps = (attn_b + write_b) / (step_ms * 1e-3) / 1e9
@@ -274,7 +347,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": "kvq_paged_decode_attn (split-K decode + merge), bytes per launch = "
-                               f"{attn_b}", "attn_ms_mean": round(attn_ms, 6), "attn_ms_median": round(attn_med, 6),
+                               f"{attn_b}", "attn_ms_mean": round(attn_ms, 6),
                      "kernel_source_hash": khash},
     }
     if not args.no_compare:
@@ -283,7 +356,7 @@ def main():
         del fp8
         torch.cuda.empty_cache()
         bf = Layers(K, w, K.KVQ_KV_BF16, args.layers, dev)
-        b_step, b_attn, _ = time_steps(torch, bf, args.steps, args.warmup, args.impl)
+        b_step, b_attn = time_steps(torch, bf, args.steps, args.warmup, args.impl)
         b_attn_b, _ = step_bytes(w.B, w.Hq, w.Hkv, w.D, w.seq_lens, 2, w.B)
         result["bf16_kv"] = {"ms_per_step": round(b_step, 6), "attn_ms_mean": round(b_attn, 6),
                              "attn_gbps": round(b_attn_b / (b_attn * 1e-3) / 1e9, 2)}

@@ -14,45 +14,87 @@ namespace kvq {
 // ---- amax ------------------------------------------------------------------
 // |bf16| ordered as an unsigned 15-bit magnitude equals the order of the
 // values (NaN patterns above Inf), so the running max is an integer max on
-// the fp32 bit pattern of the magnitude; one atomicMax per wave.
-__global__ void __launch_bounds__(256) amax_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows,
-                                                        int64_t cols, int64_t stride,
-                                                        uint32_t* __restrict__ amax_bits) {
+// the fp32 bit pattern of the magnitude.  Each thread walks 16-byte vectors
+// (row, column) with a carry instead of a per-element 64-bit division, keeps
+// kAmaxUnroll loads in flight, and the work-group reduces through LDS to one
+// atomicMax (skipped when the running value is already larger).
+constexpr int kAmaxThreads = 256;
+constexpr int kAmaxUnroll = 4;
+
+__device__ __forceinline__ uint32_t absmax8(const u32x4& w) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m = max(m, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
+    return m;
+}
+
+__global__ void __launch_bounds__(kAmaxThreads) amax_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                                 int64_t cols, int64_t stride,
+                                                                 uint32_t* __restrict__ amax_bits) {
+    __shared__ uint32_t red[kAmaxThreads / 64];
     uint32_t m = 0;
     const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if ((cols & 7) == 0 && (stride & 7) == 0) {
-        const int64_t vec_per_row = cols >> 3;
-        const int64_t nvec = rows * vec_per_row;
-        for (int64_t i = tid; i < nvec; i += nthreads) {
-            int64_t r = i / vec_per_row, c = (i - r * vec_per_row) << 3;
-            u32x4 w = *reinterpret_cast<const u32x4*>(x + r * stride + c);
+        // vector i = (r, c): element offset r * stride + 8c; thread i, i + nthreads, ...
+        const int64_t vpr = cols >> 3;
+        int64_t r = tid / vpr, c = tid - r * vpr;
+        const int64_t dr = nthreads / vpr, dc = nthreads - dr * vpr;
+        while (r < rows) {
+            u32x4 w[kAmaxUnroll];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                uint32_t lo = w[j] & 0x7FFFu, hi = (w[j] >> 16) & 0x7FFFu;
-                m = max(m, max(lo, hi));
+            for (int u = 0; u < kAmaxUnroll; ++u) {
+                if (r < rows) {
+                    w[u] = *reinterpret_cast<const u32x4*>(x + r * stride + (c << 3));
+                    c += dc;
+                    r += dr;
+                    if (c >= vpr) {
+                        c -= vpr;
+                        ++r;
+                    }
+                } else {
+                    w[u] = u32x4{0u, 0u, 0u, 0u};
+                }
             }
+#pragma unroll
+            for (int u = 0; u < kAmaxUnroll; ++u) m = max(m, absmax8(w[u]));
         }
     } else {
         const int64_t n = rows * cols;
+        int64_t r = tid / cols, c = tid - r * cols;
+        const int64_t dr = nthreads / cols, dc = nthreads - dr * cols;
         for (int64_t i = tid; i < n; i += nthreads) {
-            int64_t r = i / cols, c = i - r * cols;
             m = max(m, (uint32_t)(x[r * stride + c] & 0x7FFFu));
+            c += dc;
+            r += dr;
+            if (c >= cols) {
+                c -= cols;
+                ++r;
+            }
         }
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1)
         m = max(m, (uint32_t)__builtin_amdgcn_ds_bpermute((__lane_id() ^ o) << 2, (int)m));
-    if (__lane_id() == 0 && m != 0) atomicMax(amax_bits, m << 16);
+    if (__lane_id() == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int w = 1; w < kAmaxThreads / 64; ++w) m = max(m, red[w]);
+        const uint32_t bits = m << 16;
+        if (m != 0 && bits > __hip_atomic_load(amax_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+            atomicMax(amax_bits, bits);
+    }
 }
 
 hipError_t launch_amax_bf16(const void* x, int64_t rows, int64_t cols, int64_t stride, float* amax,
                             hipStream_t st) {
-    int64_t work = ((cols & 7) == 0 && (stride & 7) == 0) ? rows * (cols >> 3) : rows * cols;
-    int64_t blocks = (work + 255) / 256;
-    if (blocks > 4096) blocks = 4096;
+    const int64_t work = ((cols & 7) == 0 && (stride & 7) == 0) ? rows * (cols >> 3) : rows * cols;
+    // about 16 vectors per thread, at most 4 work-groups per CU
+    int64_t blocks = (work + kAmaxThreads * 16 - 1) / (kAmaxThreads * 16);
+    if (blocks > 1024) blocks = 1024;
     if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL(amax_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
+    hipLaunchKernelGGL(amax_bf16_kernel, dim3((unsigned)blocks), dim3(kAmaxThreads), 0, st,
                        (const uint16_t*)x, rows, cols, stride, (uint32_t*)amax);
     return hipGetLastError();
 }

@@ -95,6 +95,20 @@ def test_amax(K):
     assert np.isnan(a3.item())
 
 
+@pytest.mark.parametrize("where", ["last", "first", "middle", "row_edge"])
+def test_amax_large_strided(K, where):
+    # many work-groups and loop turns: a [70001][2*8][64] fused buffer, V half as strided rows
+    g = torch.Generator().manual_seed(11)
+    fused = torch.randn(70001, 16, 64, generator=g).to(torch.bfloat16)
+    pos = {"last": (70000, 15, 63), "first": (0, 8, 0), "middle": (35017, 11, 40), "row_edge": (4096, 8, 0)}[where]
+    fused[pos] = -30.5
+    vk = fused.cuda()[:, 8:, :]
+    amax = torch.zeros(1, device="cuda")
+    K.kvq_amax_bf16(vk, amax)
+    want = oracle.amax_bf16(fused[:, 8:, :].contiguous())
+    assert want == 30.5 and amax.item() == want
+
+
 @pytest.mark.parametrize("kv", [0, 1])
 @pytest.mark.parametrize("name,seed,lens,shape", [
     ("tiny", 0, None, None),
