@@ -271,8 +271,9 @@ typedef struct {
     const int32_t* seq_lens;
     int B, Hq, Hkv, D, block_size;
     float k_scale, v_scale, sm_scale;
-    const int32_t* units; /* NULL: unit i is (i / Hq, i % Hq) */
+    const int32_t* units; /* NULL: unit u is (b, i, h) = (u / (q_len*Hq), u / Hq % q_len, u % Hq) */
     int n_units;
+    int q_len;            /* queries per sequence: the q_len newest tokens */
     double* out;
     int next_unit;
     pthread_mutex_t lock;
@@ -296,12 +297,15 @@ static double v_value(const attn_job* j, int64_t slot, int g, int d) {
     return kvqo_e4m3_value(((const uint8_t*)j->v_cache)[i]) * (double)j->v_scale;
 }
 
-static void attend_one(const attn_job* j, int b, int h, double* out, double* s) {
+/* Query i of sequence b (the token at position seq_len - q_len + i) attends
+ * causally: to tokens 0 .. seq_len - q_len + i, i.e. L = seq_len - q_len + 1 + i
+ * of them; out = 0 when L <= 0. */
+static void attend_one(const attn_job* j, int b, int i, int h, double* out, double* s) {
     int G = j->Hq / j->Hkv;
     int g = h / G;
-    int L = j->seq_lens[b];
+    int L = j->seq_lens[b] - j->q_len + 1 + i;
     int D = j->D;
-    const uint16_t* q = j->q + ((int64_t)b * j->Hq + h) * D;
+    const uint16_t* q = j->q + (((int64_t)b * j->q_len + i) * j->Hq + h) * D;
     for (int d = 0; d < D; ++d) out[d] = 0.0;
     if (L <= 0) return;
     double m = -INFINITY;
@@ -335,9 +339,17 @@ static void* attn_worker(void* arg) {
         int u = j->next_unit++;
         pthread_mutex_unlock(&j->lock);
         if (u >= j->n_units) break;
-        int b = j->units ? j->units[2 * u] : u / j->Hq;
-        int h = j->units ? j->units[2 * u + 1] : u % j->Hq;
-        attend_one(j, b, h, j->out + (int64_t)u * j->D, s);
+        int b, i, h;
+        if (j->units) {
+            b = j->units[2 * u];
+            i = 0;
+            h = j->units[2 * u + 1];
+        } else {
+            b = u / (j->q_len * j->Hq);
+            i = u / j->Hq % j->q_len;
+            h = u % j->Hq;
+        }
+        attend_one(j, b, i, h, j->out + (int64_t)u * j->D, s);
     }
     free(s);
     return NULL;
@@ -365,7 +377,18 @@ void kvqo_decode_attn(const uint16_t* q, const void* k_cache, const void* v_cach
                       double* out, int nthreads) {
     attn_job j = {q, k_cache, v_cache, kv_dtype, block_tables, max_blocks, seq_lens,
                   B, Hq, Hkv, D, block_size, k_scale, v_scale, sm_scale,
-                  NULL, B * Hq, out, 0};
+                  NULL, B * Hq, 1, out, 0};
+    run_attn(&j, nthreads);
+}
+
+void kvqo_decode_attn_mq(const uint16_t* q, int q_len, const void* k_cache, const void* v_cache,
+                         int kv_dtype, const int32_t* block_tables, int max_blocks,
+                         const int32_t* seq_lens, int B, int Hq, int Hkv, int D,
+                         int block_size, float k_scale, float v_scale, float sm_scale,
+                         double* out, int nthreads) {
+    attn_job j = {q, k_cache, v_cache, kv_dtype, block_tables, max_blocks, seq_lens,
+                  B, Hq, Hkv, D, block_size, k_scale, v_scale, sm_scale,
+                  NULL, B * q_len * Hq, q_len, out, 0};
     run_attn(&j, nthreads);
 }
 
@@ -376,7 +399,7 @@ void kvqo_decode_attn_units(const uint16_t* q, const void* k_cache, const void* 
                             const int32_t* units, int n_units, double* out, int nthreads) {
     attn_job j = {q, k_cache, v_cache, kv_dtype, block_tables, max_blocks, seq_lens,
                   B, Hq, Hkv, D, block_size, k_scale, v_scale, sm_scale,
-                  units, n_units, out, 0};
+                  units, n_units, 1, out, 0};
     run_attn(&j, nthreads);
 }
 

@@ -194,3 +194,15 @@ def _lengths(name: str, cfg: dict, seed: int) -> List[int]:
 
 
 NAMES = tuple(_DEFAULTS)
+
+
+def mq_queries(w: Workload, q_len: int, seed: int = 0, device=None) -> torch.Tensor:
+    """Queries of a multi-query decode step (speculative-decoding
+    verification): bf16 [B][q_len][Hq][D] ~ N(0,1), one row per new token.
+    The new tokens are the last q_len of each sequence in w (already in the
+    cache); row q_len - 1 is w.q."""
+    device = w.q.device if device is None else torch.device(device)
+    g = _gen(seed + 3, device)
+    q = _normal((w.B, q_len, w.Hq, w.D), g, device).to(torch.bfloat16)
+    q[:, q_len - 1] = w.q.to(device)
+    return q

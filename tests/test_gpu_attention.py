@@ -32,6 +32,7 @@ CASES = [
     ("agents126k", 3, [3000, 127], dict(Hq=12, Hkv=2, D=256, calib_tokens=512)),  # G 6, D 256
     ("mixed64", 4, [129, 700], dict(Hq=16, Hkv=1, D=64)),                       # G 16
     ("mixed64", 5, [64, 1500], dict(Hq=2, Hkv=2, D=128)),                       # G 1
+    ("mixed64", 6, [700, 33, 1], dict(Hq=16, Hkv=1, D=256)),                    # G 16 at D 256: largest LDS
 ]
 
 
