@@ -151,6 +151,52 @@ def time_steps(torch, layers, steps, warmup, impl=0):
     return step_ms, attn_ms
 
 
+def measure_multiquery(torch, K, name, q_lens, steps, warmup):
+    """Multi-query decode (speculative-decoding verification) on one
+    workload's FP8 caches: the q_len newest tokens attend at once.  Reports
+    the call time next to the single-query call on the same rotated caches
+    (the cache is read once per call either way)."""
+    from quantized_decode_attention_calibrate_amd import workloads
+    w = workloads.make(name, device="cuda", seed=0)
+    L = Layers(K, w, K.KVQ_KV_FP8_E4M3, layers_for(w, 1), "cuda")
+    st = torch.cuda.current_stream()
+    attn_b1, _ = step_bytes(w.B, w.Hq, w.Hkv, w.D, w.seq_lens, 1, w.B)
+    rec = {"B": w.B, "max_seq_len": w.max_seq_len, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "kv": "fp8_e4m3"}
+
+    def timed(fn):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(st)
+        for i in range(steps):
+            fn(i)
+        a1.record(st)
+        torch.cuda.synchronize()
+        return a0.elapsed_time(a1) / steps * 1e3
+
+    t1 = timed(lambda i: L.attend(i))
+    rec["q_len_1_us"] = round(t1, 2)
+    for ql in q_lens:
+        q = workloads.mq_queries(w, ql, seed=0).cuda()
+        out = torch.empty(w.B, ql, w.Hq, w.D, dtype=torch.bfloat16, device="cuda")
+        ws = K.new_workspace_mq(w.B, ql, w.Hq, w.Hkv, w.D, w.max_seq_len)
+
+        def call(i, q=q, out=out, ws=ws):
+            kc, vc = L.caches[i % L.R]
+            K.kvq_paged_decode_attn_mq(q, kc, vc, K.KVQ_KV_FP8_E4M3, L.bt, L.sl, w.max_seq_len, w.Hkv, L.ks,
+                                       L.vs, L.sm, out, ws)
+        us = timed(call)
+        # bytes: the KV scan once plus q_len x (q in, out)
+        byts = attn_b1 + (ql - 1) * 2 * w.B * w.Hq * w.D * 2
+        rec[f"q_len_{ql}"] = {"attn_us": round(us, 2), "attn_gbps": round(byts / (us * 1e-6) / 1e9, 1),
+                              "over_q_len_1": round(us / t1, 3),
+                              "kv_tokens_verified_per_s": round(sum(w.seq_lens) * ql / (us * 1e-6), 1)}
+    del L, w
+    torch.cuda.empty_cache()
+    return rec
+
+
 def measure_workload(torch, K, name, steps, warmup, with_nvfp4=False):
     """FP8 and BF16 attention-call time for one workload (compact record)."""
     from quantized_decode_attention_calibrate_amd import workloads
@@ -370,6 +416,8 @@ def main():
         for name in ("agents126k", "mixed64", "nvfp4_131k"):
             print(f"[bench] workload {name}", file=sys.stderr, flush=True)
             result["workloads"][name] = measure_workload(torch, K, name, 60, 10, with_nvfp4=name == "nvfp4_131k")
+        print("[bench] multi-query decode", file=sys.stderr, flush=True)
+        result["multiquery"] = measure_multiquery(torch, K, "gptoss65k", (2, 4, 8), 200, 20)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         w_cpu = workloads.make(args.workload, device="cpu", seed=0)

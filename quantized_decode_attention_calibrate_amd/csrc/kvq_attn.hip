@@ -40,16 +40,28 @@ constexpr int kThreads = kWaves * 64;
 // a second wave per SIMD hides it (measured 44 -> 42 us on a 2 x 131k-token
 // decode); for FP8 and BF16 the extra waves only shorten each wave's chunk
 // run and were measured neutral to slightly slower.
-template <int D, int FMT>
-constexpr int mfma_waves() { return (FMT == kFmtNVFP4 && D == 64) ? 8 : 4; }
+template <int D, int FMT, int NT>
+constexpr int mfma_waves() { return (FMT == kFmtNVFP4 && D == 64 && NT == 1) ? 8 : 4; }
 constexpr int kMaxSplitBlocks = kMaxSplitTokens / kBlockSize;
+
+// Columns: a work-group serves the G query heads of one KV head for each of
+// the q_len queries of its sequence (q_len = 1 for single-token decode):
+// column c = i * G + hl is query i, head g * G + hl, and its output row is
+// (b * q_len + i) * Hq + g * G + hl.  The MFMA family holds the columns in NT
+// tiles of 16; GQ = G * q_len <= 16 * NT.
+__device__ __forceinline__ int64_t column_row(const DecodeArgs& a, int b, int g, int c) {
+    const int i = c / a.G;
+    return ((int64_t)b * a.q_len + i) * a.Hq + (int64_t)g * a.G + (c - i * a.G);
+}
 
 // LDS layout shared by both families (dynamic shared memory):
 //   int   blk[kMaxSplitBlocks]          physical block ids of this split
-//   float m[W][16], l[W][16]            per-wave softmax state per head (W waves)
-//   float acc[W][G][D]                  per-wave unnormalised outputs
+//   float m[W][16 NT], l[W][16 NT]      per-wave softmax state per column (W waves)
+//   float acc[W][GQ][D]                 per-wave unnormalised outputs
 //   (VALU only) float q[G][D], p[W][16][16]
-__host__ __device__ constexpr int lds_merge_floats(int G, int D, int W) { return W * 32 + W * G * D; }
+__host__ __device__ constexpr int lds_merge_floats(int GQ, int D, int W, int NT = 1) {
+    return W * 32 * NT + W * GQ * D;
+}
 
 // Stage the physical block ids of logical blocks [lb0, lb0 + n) into LDS,
 // clamping logical blocks past the sequence to its last block (those tokens
@@ -72,40 +84,45 @@ __device__ __forceinline__ void store_out(const DecodeArgs& a, int64_t o, float 
         reinterpret_cast<uint16_t*>(a.out)[o] = (uint16_t)f32_to_bf16_rne(v);
 }
 
-template <int W>
+template <int W, int NT = 1>
 __device__ __forceinline__ void finish_split(const DecodeArgs& a, const float* s_m, const float* s_l,
                                              const float* s_acc, int b, int g, int s, int S, int D) {
-    const int G = a.G;
-    const int64_t hq0 = (int64_t)b * a.Hq + (int64_t)g * G;
-    for (int idx = threadIdx.x; idx < G * D; idx += W * 64) {
-        const int h = idx / D, d = idx - h * D;
+    constexpr int CP = 16 * NT;   // columns per wave in s_m / s_l
+    const int GQ = a.G * a.q_len;
+    for (int idx = threadIdx.x; idx < GQ * D; idx += W * 64) {
+        const int c = idx / D, d = idx - c * D;
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < W; ++w) M = fmaxf(M, s_m[w * 16 + h]);
+        for (int w = 0; w < W; ++w) M = fmaxf(M, s_m[w * CP + c]);
         float acc = 0.f, l = 0.f;
 #pragma unroll
         for (int w = 0; w < W; ++w) {
-            const float mw = s_m[w * 16 + h];
+            const float mw = s_m[w * CP + c];
             const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
-            acc += f * s_acc[(w * G + h) * D + d];
-            l += f * s_l[w * 16 + h];
+            acc += f * s_acc[(w * GQ + c) * D + d];
+            l += f * s_l[w * CP + c];
         }
+        const int64_t r = column_row(a, b, g, c);
         if (S == 1) {
-            store_out(a, (hq0 + h) * D + d, acc * (a.v_scale / l));
+            // l == 0: a query that sees no token (it sits before the sequence start)
+            store_out(a, r * D + d, l > 0.f ? acc * (a.v_scale / l) : 0.f);
         } else {
-            a.ws_acc[((hq0 + h) * a.num_splits + s) * D + d] = acc;
+            a.ws_acc[(r * a.num_splits + s) * D + d] = acc;
             if (d == 0) {
-                a.ws_ml[((hq0 + h) * a.num_splits + s) * 2 + 0] = M;
-                a.ws_ml[((hq0 + h) * a.num_splits + s) * 2 + 1] = l;
+                a.ws_ml[(r * a.num_splits + s) * 2 + 0] = M;
+                a.ws_ml[(r * a.num_splits + s) * 2 + 1] = l;
             }
         }
     }
 }
 
-// A sequence with no tokens: work-group (split 0) writes zeros for its heads.
+// A sequence with no tokens: work-group (split 0) writes zeros for its columns.
 __device__ __forceinline__ void write_empty(const DecodeArgs& a, int b, int g, int D) {
-    const int64_t hq0 = (int64_t)b * a.Hq + (int64_t)g * a.G;
-    for (int idx = threadIdx.x; idx < a.G * D; idx += blockDim.x) store_out(a, hq0 * D + idx, 0.f);
+    const int GQ = a.G * a.q_len;
+    for (int idx = threadIdx.x; idx < GQ * D; idx += blockDim.x) {
+        const int c = idx / D;
+        store_out(a, column_row(a, b, g, c) * D + (idx - c * D), 0.f);
+    }
 }
 
 // =============================================================================
@@ -152,11 +169,11 @@ struct MfmaChunk<D, kFmtNVFP4> {      // 16 E2M1 codes + 1 scale per (tile, slic
     u32x4 vs[D / 16];
 };
 
-// Per-wave running softmax state of head n (lane % 16).
-template <int D>
+// Per-wave running softmax state of column 16 nt + n (lane % 16) per tile nt.
+template <int D, int NT>
 struct MfmaState {
-    f32x4 acc[D / 16];
-    float m_run, l_run;
+    f32x4 acc[NT][D / 16];
+    float m_run[NT], l_run[NT];
 };
 
 template <int D, int FMT>
@@ -248,88 +265,112 @@ __device__ __forceinline__ f16x8 v_operand_f16(const MfmaChunk<D, FMT>& c, int d
     }
 }
 
-template <int D, int FMT>
-__device__ __forceinline__ void mfma_process(MfmaState<D>& st, MfmaChunk<D, FMT>& c, const QkOperand<FMT>* qb,
-                                             float cs, int chunk_tok, int tok_end, int grp) {
+// One 64-token chunk for all NT column tiles: K and V are unpacked once and
+// shared by the tiles.  `cend[nt]` is the exclusive causal end of this lane's
+// column in tile nt (tok_end for single-token decode); `tail_from` is the
+// smallest of them over the work-group, so chunks below it need no masking.
+template <int D, int FMT, int NT>
+__device__ __forceinline__ void mfma_process(MfmaState<D, NT>& st, MfmaChunk<D, FMT>& c,
+                                             const QkOperand<FMT> (*qb)[2 * (D / 64)], const float* cs,
+                                             const int* cend, int chunk_tok, int tok_end, int tail_from,
+                                             int grp) {
     constexpr int KJ = D / 64, DT = D / 16;
     constexpr bool kF16V = FMT != kFmtBF16;   // V operand in f16 (FP8, NVFP4) or bf16
     // ---- S = K Q^T ---------------------------------------------------------
-    float sv[16];
+    float sv[NT][16];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        f32x4 t = {0.f, 0.f, 0.f, 0.f};
+        f32x4 t[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) t[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < KJ; ++j)
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
-                if constexpr (FMT == kFmtNVFP4)
-                    t = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand(c, i, j, hh), qb[2 * j + hh], t, 0, 0, 0);
-                else
-                    t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(c, i, j, hh), qb[2 * j + hh], t, 0, 0, 0);
+                const QkOperand<FMT> ka = k_operand(c, i, j, hh);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    if constexpr (FMT == kFmtNVFP4)
+                        t[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[nt][2 * j + hh], t[nt], 0, 0, 0);
+                    else
+                        t[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[nt][2 * j + hh], t[nt], 0, 0, 0);
+                }
             }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sv[4 * i + r] = t[r];   // raw scores; scaled inside the exp
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sv[nt][4 * i + r] = t[nt][r];   // raw scores; scaled inside the exp
     }
 
-    // ---- online softmax over this chunk (head n, chunk block grp) -----------
+    // ---- online softmax over this chunk (column n, chunk block grp) ---------
     // The score scale cs (> 0) is applied as exp2(fma(s, cs, -m)); the running
-    // max m is kept in scaled units.  Masking runs only on the sequence's last
-    // chunk (a wave-uniform branch).
-    const int valid = tok_end - (chunk_tok + 16 * grp);  // tokens of block grp in range
-    const bool tail = chunk_tok + kChunkTokens > tok_end;
-    if (tail) {
+    // max m is kept in scaled units.  Masking runs only on chunks that reach a
+    // column's end (a wave-uniform branch).  A column that has seen no token
+    // yet keeps m = -inf; its weights are 0 and alpha is 0.
+    const bool tail = chunk_tok + kChunkTokens > tail_from;
+    const int tok0 = chunk_tok + 16 * grp;   // token of sv[.][0]
+    f16x8 pfh[NT][2], pfl[NT][2];
+    bf16x8 pbh[NT][2], pbl[NT][2];
+    float alpha[NT];
 #pragma unroll
-        for (int e = 0; e < 16; ++e)  // sv[4i + r] is token offset 4i + r of block grp
-            if (e >= valid) sv[e] = -INFINITY;
-    }
-    float mloc = sv[0];
+    for (int nt = 0; nt < NT; ++nt) {
+        if (tail) {
+            const int valid = cend[nt] - tok0;   // tokens of block grp this column sees
 #pragma unroll
-    for (int e = 1; e < 16; ++e) mloc = fmaxf(mloc, sv[e]);
-    mloc = fmaxf(mloc, shfl_xor(mloc, 16));
-    mloc = fmaxf(mloc, shfl_xor(mloc, 32));
-    const float m_new = fmaxf(st.m_run, mloc * cs);
-    const float alpha = fast_exp2(st.m_run - m_new);
-    st.m_run = m_new;
+            for (int e = 0; e < 16; ++e)  // sv[4i + r] is token offset 4i + r of block grp
+                if (e >= valid) sv[nt][e] = -INFINITY;
+        }
+        float mloc = sv[nt][0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) mloc = fmaxf(mloc, sv[nt][e]);
+        mloc = fmaxf(mloc, shfl_xor(mloc, 16));
+        mloc = fmaxf(mloc, shfl_xor(mloc, 32));
+        const float m_new = fmaxf(st.m_run[nt], mloc * cs[nt]);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        alpha[nt] = fast_exp2(st.m_run[nt] - m_use);
+        st.m_run[nt] = m_new;
 
-    // Weights in the PV operand layout (half hh = tokens 8hh..8hh+7).  They are
-    // scaled by 2^15 (exp2 offset) so they sit in f16's normal range, and split
-    // into hi + lo 16-bit parts so the two PV MFMAs on the same exact V operand
-    // reproduce the fp32 weight to ~2^-21.  The scale is common to acc and l and
-    // cancels in the final division.
-    const float m_off = m_new - 15.0f;
-    float psum = 0.f;
-    f16x8 pfh[2], pfl[2];
-    bf16x8 pbh[2], pbl[2];
+        // Weights in the PV operand layout (half hh = tokens 8hh..8hh+7).  They
+        // are scaled by 2^15 (exp2 offset) so they sit in f16's normal range,
+        // and split into hi + lo 16-bit parts so the two PV MFMAs on the same
+        // exact V operand reproduce the fp32 weight to ~2^-21.  The scale is
+        // common to acc and l and cancels in the final division.
+        const float m_off = m_use - 15.0f;
+        float psum = 0.f;
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
+        for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-            const float p0 = fast_exp2(__builtin_fmaf(sv[8 * hh + 2 * e2], cs, -m_off));
-            const float p1 = fast_exp2(__builtin_fmaf(sv[8 * hh + 2 * e2 + 1], cs, -m_off));
-            psum += p0 + p1;
-            if constexpr (kF16V) {
-                const f16x2 h = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(p0, p1));
-                const f16x2 l =
-                    __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(p0 - (float)h[0], p1 - (float)h[1]));
-                pfh[hh][2 * e2] = h[0];
-                pfh[hh][2 * e2 + 1] = h[1];
-                pfl[hh][2 * e2] = l[0];
-                pfl[hh][2 * e2 + 1] = l[1];
-            } else {
-                const __bf16 h0 = (__bf16)p0, h1 = (__bf16)p1;
-                pbh[hh][2 * e2] = h0;
-                pbh[hh][2 * e2 + 1] = h1;
-                pbl[hh][2 * e2] = (__bf16)(p0 - (float)h0);
-                pbl[hh][2 * e2 + 1] = (__bf16)(p1 - (float)h1);
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const float p0 = fast_exp2(__builtin_fmaf(sv[nt][8 * hh + 2 * e2], cs[nt], -m_off));
+                const float p1 = fast_exp2(__builtin_fmaf(sv[nt][8 * hh + 2 * e2 + 1], cs[nt], -m_off));
+                psum += p0 + p1;
+                if constexpr (kF16V) {
+                    const f16x2 h = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(p0, p1));
+                    const f16x2 l =
+                        __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(p0 - (float)h[0], p1 - (float)h[1]));
+                    pfh[nt][hh][2 * e2] = h[0];
+                    pfh[nt][hh][2 * e2 + 1] = h[1];
+                    pfl[nt][hh][2 * e2] = l[0];
+                    pfl[nt][hh][2 * e2 + 1] = l[1];
+                } else {
+                    const __bf16 h0 = (__bf16)p0, h1 = (__bf16)p1;
+                    pbh[nt][hh][2 * e2] = h0;
+                    pbh[nt][hh][2 * e2 + 1] = h1;
+                    pbl[nt][hh][2 * e2] = (__bf16)(p0 - (float)h0);
+                    pbl[nt][hh][2 * e2 + 1] = (__bf16)(p1 - (float)h1);
+                }
             }
         }
+        st.l_run[nt] = st.l_run[nt] * alpha[nt] + psum;
     }
-    st.l_run = st.l_run * alpha + psum;
 
-    // Zero V data of tokens past the end: their weight is 0 but the bytes may be
-    // anything (NaN codes).  FP8: V bytes; NVFP4: the tokens' block scales (the
-    // E2M1 codes are always finite); BF16: V halfwords.
-    if (tail) {
+    // Zero V data of tokens past the sequence end: their weight is 0 but the
+    // bytes may be anything (NaN codes).  FP8: V bytes; NVFP4: the tokens' block
+    // scales (the E2M1 codes are always finite); BF16: V halfwords.  Tokens
+    // inside the sequence but past a column's causal end are finite; their
+    // weight is 0.
+    if (chunk_tok + kChunkTokens > tok_end) {
+        const int valid = tok_end - tok0;
         if constexpr (FMT == kFmtBF16) {
             u32x4 keep[2];
 #pragma unroll
@@ -370,33 +411,41 @@ __device__ __forceinline__ void mfma_process(MfmaState<D>& st, MfmaChunk<D, FMT>
     // ---- acc = alpha * acc + V^T P^T ----------------------------------------
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-        st.acc[dt] *= alpha;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) st.acc[nt][dt] *= alpha[nt];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             if constexpr (kF16V) {
                 const f16x8 va = v_operand_f16(c, dt, hh);
-                st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pfh[hh], st.acc[dt], 0, 0, 0);
-                st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pfl[hh], st.acc[dt], 0, 0, 0);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    st.acc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pfh[nt][hh], st.acc[nt][dt], 0, 0, 0);
+                    st.acc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pfl[nt][hh], st.acc[nt][dt], 0, 0, 0);
+                }
             } else {
                 const bf16x8 va = __builtin_bit_cast(bf16x8, c.vw[dt][hh]);
-                st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pbh[hh], st.acc[dt], 0, 0, 0);
-                st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pbl[hh], st.acc[dt], 0, 0, 0);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    st.acc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pbh[nt][hh], st.acc[nt][dt], 0, 0, 0);
+                    st.acc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pbl[nt][hh], st.acc[nt][dt], 0, 0, 0);
+                }
             }
         }
     }
 }
 
-template <int D, int FMT, int W = mfma_waves<D, FMT>()>
+template <int D, int FMT, int NT, int W = mfma_waves<D, FMT, NT>()>
 __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
     constexpr int KJ = D / 64;
     constexpr int DT = D / 16;
+    constexpr int CP = 16 * NT;   // padded columns
     // two chunks in flight per wave where the registers allow it
     constexpr bool kPrefetch = KVQ_MFMA_PREFETCH && D <= 128;
     extern __shared__ float lds[];
     int* s_blk = reinterpret_cast<int*>(lds);
     float* s_m = lds + kMaxSplitBlocks;
-    float* s_l = s_m + W * 16;
-    float* s_acc = s_l + W * 16;
+    float* s_l = s_m + W * CP;
+    float* s_acc = s_l + W * CP;
 
     const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int L = a.seq_lens[b];
@@ -409,32 +458,41 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
     const int S = (L + a.split_tokens - 1) / a.split_tokens;   // splits holding tokens
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n = lane & 15, grp = lane >> 4;
-    const int G = a.G;
+    const int G = a.G, GQ = G * a.q_len;
 
     const int lb0 = tok_begin / kBlockSize;
     const int n_chunks = (tok_end - tok_begin + kChunkTokens - 1) / kChunkTokens;
     stage_block_ids(s_blk, a.block_tables + (int64_t)b * a.max_blocks, lb0, n_chunks * 4,
                     (L + kBlockSize - 1) / kBlockSize - 1);
 
-    // Q^T operands: k-step (j, hh) covers dims 64j + 16grp + 8hh .. +7.  For
-    // NVFP4 the QK product runs in f16: head n's q is scaled by a power of two
-    // 2^qs (max |q| lands in [2^13, 2^14), far inside f16's range; the
-    // conversion is exact for every element within 2^27 of the max) and the
-    // score scale is divided by the same power of two.
-    QkOperand<FMT> qb[2 * KJ];
-    float cs = a.qk_scale_log2;
-    {
-        const int h = g * G + n;
-        const uint16_t* qrow = a.q + ((int64_t)b * a.Hq + h) * D;
+    // Causal ends: query i (token L - q_len + i) sees tokens < L - q_len + 1 + i.
+    const int q0_end = L - a.q_len + 1;
+    int cend[NT];
+    // Q^T operands per tile: k-step (j, hh) covers dims 64j + 16grp + 8hh .. +7
+    // of column 16 nt + n (zero past GQ).  For NVFP4 the QK product runs in
+    // f16: the column's q is scaled by a power of two 2^qs (max |q| lands in
+    // [2^13, 2^14), far inside f16's range; the conversion is exact for every
+    // element within 2^27 of the max) and its score scale is divided by the
+    // same power of two.
+    QkOperand<FMT> qb[NT][2 * KJ];
+    float cs[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int c = 16 * nt + n;
+        const bool live = c < GQ;
+        const int qi = live ? c / G : 0;
+        cend[nt] = live ? min(tok_end, q0_end + qi) : tok_end;
+        const uint16_t* qrow = a.q + (live ? column_row(a, b, g, c) : 0) * D;
         u32x4 qw[2 * KJ];
 #pragma unroll
         for (int j = 0; j < KJ; ++j)
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 u32x4 w = {0u, 0u, 0u, 0u};
-                if (n < G) w = *reinterpret_cast<const u32x4*>(qrow + 64 * j + 16 * grp + 8 * hh);
+                if (live) w = *reinterpret_cast<const u32x4*>(qrow + 64 * j + 16 * grp + 8 * hh);
                 qw[2 * j + hh] = w;
             }
+        cs[nt] = a.qk_scale_log2;
         if constexpr (FMT == kFmtNVFP4) {
             float qmax = 0.f;
 #pragma unroll
@@ -448,7 +506,7 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
             const int ex = qmax > 0.f ? __builtin_amdgcn_frexp_expf(qmax) : 0;
             const int qs = min(14 - ex, 100);   // denormal-only rows stay finite
             const float up = __builtin_ldexpf(1.0f, qs);
-            cs = __builtin_ldexpf(cs, -qs);
+            cs[nt] = __builtin_ldexpf(cs[nt], -qs);
 #pragma unroll
             for (int k = 0; k < 2 * KJ; ++k) {
                 f16x8 v;
@@ -457,21 +515,25 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
                     v[2 * e] = (_Float16)(bf16_lo(qw[k][e]) * up);
                     v[2 * e + 1] = (_Float16)(bf16_hi(qw[k][e]) * up);
                 }
-                qb[k] = v;
+                qb[nt][k] = v;
             }
         } else {
 #pragma unroll
-            for (int k = 0; k < 2 * KJ; ++k) qb[k] = __builtin_bit_cast(bf16x8, qw[k]);
+            for (int k = 0; k < 2 * KJ; ++k) qb[nt][k] = __builtin_bit_cast(bf16x8, qw[k]);
         }
     }
+    const int tail_from = min(tok_end, q0_end);
     __syncthreads();
 
-    MfmaState<D> st;
+    MfmaState<D, NT> st;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) st.acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    st.m_run = -INFINITY;
-    st.l_run = 0.f;
-    // this wave's chunks: wave, wave + 4, ...
+    for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) st.acc[nt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        st.m_run[nt] = -INFINITY;
+        st.l_run[nt] = 0.f;
+    }
+    // this wave's chunks: wave, wave + W, ...
     const int my = wave < n_chunks ? (n_chunks - wave + W - 1) / W : 0;
 
     if constexpr (kPrefetch) {
@@ -486,11 +548,11 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
             for (int i = 0; i < my; i += 2) {
                 const int chb = i + 1 < my ? ch + W : ch;
                 mfma_load(Bc, a, s_blk, chb, g, n, grp);
-                mfma_process(st, A, qb, cs, tok_begin + ch * kChunkTokens, tok_end, grp);
+                mfma_process(st, A, qb, cs, cend, tok_begin + ch * kChunkTokens, tok_end, tail_from, grp);
                 if (i + 1 >= my) break;
                 const int cha = i + 2 < my ? chb + W : chb;
                 mfma_load(A, a, s_blk, cha, g, n, grp);
-                mfma_process(st, Bc, qb, cs, tok_begin + chb * kChunkTokens, tok_end, grp);
+                mfma_process(st, Bc, qb, cs, cend, tok_begin + chb * kChunkTokens, tok_end, tail_from, grp);
                 ch = cha;
             }
         }
@@ -499,26 +561,30 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
             const int ch = wave + i * W;
             MfmaChunk<D, FMT> A;
             mfma_load(A, a, s_blk, ch, g, n, grp);
-            mfma_process(st, A, qb, cs, tok_begin + ch * kChunkTokens, tok_end, grp);
+            mfma_process(st, A, qb, cs, cend, tok_begin + ch * kChunkTokens, tok_end, tail_from, grp);
         }
     }
 
     // ---- wave results -> LDS ---------------------------------------------------
-    float l_run = st.l_run;
-    l_run += shfl_xor(l_run, 16);
-    l_run += shfl_xor(l_run, 32);
-    if (grp == 0) {
-        s_m[wave * 16 + n] = st.m_run;
-        s_l[wave * 16 + n] = l_run;
-    }
-    if (n < G) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+    for (int nt = 0; nt < NT; ++nt) {
+        float l_run = st.l_run[nt];
+        l_run += shfl_xor(l_run, 16);
+        l_run += shfl_xor(l_run, 32);
+        const int c = 16 * nt + n;
+        if (grp == 0) {
+            s_m[wave * CP + c] = st.m_run[nt];
+            s_l[wave * CP + c] = l_run;
+        }
+        if (c < GQ) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) s_acc[(wave * G + n) * D + 16 * dt + 4 * grp + r] = st.acc[dt][r];
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) s_acc[(wave * GQ + c) * D + 16 * dt + 4 * grp + r] = st.acc[nt][dt][r];
+        }
     }
     __syncthreads();
-    finish_split<W>(a, s_m, s_l, s_acc, b, g, s, S, D);
+    finish_split<W, NT>(a, s_m, s_l, s_acc, b, g, s, S, D);
 }
 
 // =============================================================================
@@ -704,7 +770,7 @@ __global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeArgs a) {
         for (int e = 0; e < VD; ++e) s_acc[(wave * G + h) * D + lane + 64 * e] = acc[h][e];
     }
     __syncthreads();
-    finish_split<kWaves>(a, s_m, s_l, s_acc, b, g, s, S, D);
+    finish_split<kWaves, 1>(a, s_m, s_l, s_acc, b, g, s, S, D);
 }
 
 // =============================================================================
@@ -740,8 +806,8 @@ __global__ void __launch_bounds__(kMergeThreads) merge_splits_kernel(DecodeArgs 
     extern __shared__ float s_w[];            // [num_splits] split weights
     __shared__ float red[kMergeThreads / 64];
     __shared__ f32x4 part[P][C4];
-    const int hq = blockIdx.x;                // b * Hq + h
-    const int b = hq / a.Hq;
+    const int hq = blockIdx.x;                // output row (b * q_len + i) * Hq + h
+    const int b = hq / (a.Hq * a.q_len);
     const int L = a.seq_lens[b];
     const int S = (L + a.split_tokens - 1) / a.split_tokens;
     if (S <= 1) return;                       // written by the decode kernel
@@ -760,7 +826,8 @@ __global__ void __launch_bounds__(kMergeThreads) merge_splits_kernel(DecodeArgs 
     const float M = block_reduce(m, red, true);
     float den = 0.f;
     for (int s = t; s < S; s += kMergeThreads) {
-        const float w = fast_exp2(ml[2 * s] - M);
+        // M = -inf: no split saw a token for this row (a query before the start)
+        const float w = M == -INFINITY ? 0.f : fast_exp2(ml[2 * s] - M);
         s_w[s] = w;
         den += w * ml[2 * s + 1];
     }
@@ -777,24 +844,23 @@ __global__ void __launch_bounds__(kMergeThreads) merge_splits_kernel(DecodeArgs 
     if (p == 0) {
 #pragma unroll
         for (int q = 1; q < P; ++q) num += part[q][d4];
-        const float scale = a.v_scale / den;
+        const float scale = den > 0.f ? a.v_scale / den : 0.f;
         const int64_t o = (int64_t)hq * D + 4 * d4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) store_out(a, o + e, num[e] * scale);
     }
 }
 
-template <int D, int FMT>
+template <int D, int FMT, int NT>
 static hipError_t launch_family(const DecodeArgs& a, int B, int impl, hipStream_t st) {
     dim3 grid(a.num_splits, a.Hkv, B);
-    constexpr int W = mfma_waves<D, FMT>();
-    const size_t lds_mfma = sizeof(float) * (kMaxSplitBlocks + lds_merge_floats(a.G, D, W));
-    if constexpr (FMT == kFmtNVFP4) {
-        hipLaunchKernelGGL((decode_mfma_kernel<D, FMT>), grid, dim3(W * 64), lds_mfma, st, a);
+    constexpr int W = mfma_waves<D, FMT, NT>();
+    const int GQ = a.G * a.q_len;
+    const size_t lds_mfma = sizeof(float) * (kMaxSplitBlocks + lds_merge_floats(GQ, D, W, NT));
+    if (FMT == kFmtNVFP4 || impl == 2 || NT > 1) {
+        hipLaunchKernelGGL((decode_mfma_kernel<D, FMT, NT>), grid, dim3(W * 64), lds_mfma, st, a);
     } else {
-        if (impl == 2) {
-            hipLaunchKernelGGL((decode_mfma_kernel<D, FMT>), grid, dim3(W * 64), lds_mfma, st, a);
-        } else {
+        if constexpr (FMT != kFmtNVFP4 && NT == 1) {
             const size_t lds = sizeof(float) * (kMaxSplitBlocks + lds_merge_floats(a.G, D, kWaves) + a.G * D +
                                                 kWaves * 256);
             hipLaunchKernelGGL((decode_valu_kernel<D, FMT == kFmtFP8>), grid, dim3(kThreads), lds, st, a);
@@ -802,17 +868,40 @@ static hipError_t launch_family(const DecodeArgs& a, int B, int impl, hipStream_
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.num_splits <= 1) return e;
-    hipLaunchKernelGGL((merge_splits_kernel<D>), dim3(B * a.Hq), dim3(kMergeThreads),
+    hipLaunchKernelGGL((merge_splits_kernel<D>), dim3(B * a.q_len * a.Hq), dim3(kMergeThreads),
                        sizeof(float) * a.num_splits, st, a);
     return hipGetLastError();
+}
+
+// Column tiles per work-group: G * q_len columns in tiles of 16 (1, 2 or 4;
+// at most 64 columns at D 64, 32 at D 128, 16 at D 256).
+int decode_column_tiles(int G, int q_len, int D) {
+    const int gq = G * q_len;
+    const int nt = gq <= 16 ? 1 : gq <= 32 ? 2 : gq <= 64 ? 4 : 0;
+    if (nt == 0 || nt * D > 256) return 0;
+    return nt;
+}
+
+template <int FMT, int D>
+static hipError_t launch_nt(const DecodeArgs& a, int B, int impl, hipStream_t st) {
+    switch (decode_column_tiles(a.G, a.q_len, D)) {
+        case 1: return launch_family<D, FMT, 1>(a, B, impl, st);
+        case 2:
+            if constexpr (D <= 128) return launch_family<D, FMT, 2>(a, B, impl, st);
+            return hipErrorInvalidValue;
+        case 4:
+            if constexpr (D <= 64) return launch_family<D, FMT, 4>(a, B, impl, st);
+            return hipErrorInvalidValue;
+        default: return hipErrorInvalidValue;
+    }
 }
 
 template <int FMT>
 static hipError_t launch_d(const DecodeArgs& a, int B, int D, int impl, hipStream_t st) {
     switch (D) {
-        case 64: return launch_family<64, FMT>(a, B, impl, st);
-        case 128: return launch_family<128, FMT>(a, B, impl, st);
-        case 256: return launch_family<256, FMT>(a, B, impl, st);
+        case 64: return launch_nt<FMT, 64>(a, B, impl, st);
+        case 128: return launch_nt<FMT, 128>(a, B, impl, st);
+        case 256: return launch_nt<FMT, 256>(a, B, impl, st);
         default: return hipErrorInvalidValue;
     }
 }

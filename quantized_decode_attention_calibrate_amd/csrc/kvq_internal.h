@@ -18,25 +18,27 @@ constexpr int kMaxSplitTokens = 8192;
 // Most splits one call may have (the merge keeps one weight per split in LDS).
 constexpr int kMaxSplits = 16384;
 constexpr int kChunkTokens = 64;   // tokens per wave iteration (4 blocks of 16)
+constexpr int kMaxQueryLen = 16;   // queries per sequence of a multi-query decode
 // KV cache formats of the decode kernels
 enum : int { kFmtBF16 = 0, kFmtFP8 = 1, kFmtNVFP4 = 2 };
 constexpr int kBlockSize = 16;
 
 struct DecodeArgs {
-    const uint16_t* q;           // bf16 [B][Hq][D]
+    const uint16_t* q;           // bf16 [B][q_len][Hq][D]
     const uint8_t* k_cache;      // FP8 or BF16 paged K cache (bytes)
     const uint8_t* v_cache;      // FP8 or BF16 paged V cache (bytes, dim-major blocks)
     const int32_t* block_tables; // [B][max_blocks]
     const int32_t* seq_lens;     // [B]
-    float* ws_ml;                // [B][Hq][S][2] : running max (log2 units), sum of weights
-    float* ws_acc;               // [B][Hq][S][D] : unnormalised weighted sum of V codes
-    void* out;                   // [B][Hq][D]
+    float* ws_ml;                // [B][q_len][Hq][S][2] : running max (log2 units), sum of weights
+    float* ws_acc;               // [B][q_len][Hq][S][D] : unnormalised weighted sum of V codes
+    void* out;                   // [B][q_len][Hq][D]
     int max_blocks;
     int Hq, Hkv, G;
     int split_tokens, num_splits;
     float qk_scale_log2;         // sm_scale * k_scale * log2(e)
     float v_scale;               // applied once in the merge
     int out_f32;
+    int q_len;                   // queries per sequence (1: single-token decode)
 };
 
 // Workspace: [ml: B*Hq*S*2 f32][acc: B*Hq*S*D f32], the second region starting
@@ -56,6 +58,9 @@ hipError_t launch_nvfp4_cache_write(const void* k, const void* v, int64_t src_st
                                     int Hkv, int D, void* k_cache, void* v_cache, float k_gscale, float v_gscale,
                                     hipStream_t st);
 hipError_t launch_e2m1_decode(const uint8_t* codes, uint32_t scale_code, void* out, int64_t n, hipStream_t st);
+// Column tiles of 16 (query, head) pairs the MFMA kernel uses for G * q_len
+// columns at head dim D; 0 if the shape is not supported.
+int decode_column_tiles(int G, int q_len, int D);
 // impl: 1 = VALU, 2 = MFMA.  B is the grid's z extent.
 // fmt: kFmtBF16 / kFmtFP8 / kFmtNVFP4 (NVFP4 has the MFMA family only)
 hipError_t launch_decode(const DecodeArgs& a, int B, int D, int fmt, int impl, hipStream_t st);

@@ -56,6 +56,10 @@ def _load() -> ctypes.CDLL:
         "kvq_nvfp4_paged_decode_attn_ex": (I, [P, P, P, P, I, P, I, I, I, I, I, I, I, F, F, F, P, I, P, SZ, P,
                                                I]),
         "kvq_e2m1_decode": (I, [P, ctypes.c_uint8, P, I64, P]),
+        "kvq_decode_workspace_bytes_mq": (SZ, [I, I, I, I, I, I, I, I]),
+        "kvq_paged_decode_attn_mq": (I, [P, I, P, P, I, P, I, P, I, I, I, I, I, I, I, F, F, F, P, I, P, SZ, P, I]),
+        "kvq_nvfp4_paged_decode_attn_mq": (I, [P, I, P, P, P, I, P, I, I, I, I, I, I, I, F, F, F, P, I, P, SZ,
+                                               P, I]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -234,3 +238,53 @@ def kvq_paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
         _ptr(seq_lens), max_seq_len, B, Hq, Hkv, D, BLOCK_SIZE, k_cache.shape[0], k_scale, v_scale, sm_scale,
         _ptr(out), out_dtype, _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream),
         impl, split_tokens))
+
+
+# ---- multi-query decode -------------------------------------------------------
+
+def kvq_decode_workspace_bytes_mq(B: int, q_len: int, Hq: int, Hkv: int, D: int, max_seq_len: int,
+                                  split_tokens: int = 0) -> int:
+    return _lib.kvq_decode_workspace_bytes_mq(B, q_len, Hq, Hkv, D, max_seq_len, BLOCK_SIZE, split_tokens)
+
+
+def new_workspace_mq(B: int, q_len: int, Hq: int, Hkv: int, D: int, max_seq_len: int, split_tokens: int = 0,
+                     device="cuda"):
+    """Workspace for kvq_paged_decode_attn_mq / kvq_nvfp4_paged_decode_attn_mq."""
+    n = kvq_decode_workspace_bytes_mq(B, q_len, Hq, Hkv, D, max_seq_len, split_tokens)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def _mq_args(q, block_tables, seq_lens, out):
+    B, q_len, Hq, D = q.shape
+    assert q.dtype == torch.bfloat16 and q.is_contiguous() and out.is_contiguous() and out.shape == q.shape
+    assert block_tables.dtype == torch.int32 and block_tables.is_contiguous() and block_tables.shape[0] == B
+    assert seq_lens.dtype == torch.int32 and seq_lens.shape == (B,)
+    out_dtype = {torch.bfloat16: KVQ_OUT_BF16, torch.float32: KVQ_OUT_F32}[out.dtype]
+    return B, q_len, Hq, D, out_dtype
+
+
+def kvq_paged_decode_attn_mq(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_dtype: int,
+                             block_tables: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, Hkv: int,
+                             k_scale: float, v_scale: float, sm_scale: float, out: torch.Tensor,
+                             workspace: torch.Tensor, split_tokens: int = 0, stream=None) -> None:
+    """q bf16 [B][q_len][Hq][D] (the q_len newest tokens, already in the cache);
+    out bf16 or fp32 [B][q_len][Hq][D]."""
+    B, q_len, Hq, D, out_dtype = _mq_args(q, block_tables, seq_lens, out)
+    _check("kvq_paged_decode_attn_mq", _lib.kvq_paged_decode_attn_mq(
+        _ptr(q), q_len, _ptr(k_cache), _ptr(v_cache), kv_dtype, _ptr(block_tables), block_tables.shape[1],
+        _ptr(seq_lens), max_seq_len, B, Hq, Hkv, D, BLOCK_SIZE, k_cache.shape[0], k_scale, v_scale, sm_scale,
+        _ptr(out), out_dtype, _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream),
+        split_tokens))
+
+
+def kvq_nvfp4_paged_decode_attn_mq(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                   block_tables: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, Hkv: int,
+                                   k_gscale: float, v_gscale: float, sm_scale: float, out: torch.Tensor,
+                                   workspace: torch.Tensor, split_tokens: int = 0, stream=None) -> None:
+    """NVFP4 caches; otherwise as kvq_paged_decode_attn_mq."""
+    B, q_len, Hq, D, out_dtype = _mq_args(q, block_tables, seq_lens, out)
+    _check("kvq_nvfp4_paged_decode_attn_mq", _lib.kvq_nvfp4_paged_decode_attn_mq(
+        _ptr(q), q_len, _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1],
+        _ptr(seq_lens), max_seq_len, B, Hq, Hkv, D, BLOCK_SIZE, k_cache.shape[0], k_gscale, v_gscale, sm_scale,
+        _ptr(out), out_dtype, _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream),
+        split_tokens))
