@@ -151,6 +151,40 @@ def time_steps(torch, layers, steps, warmup, impl=0):
     return step_ms, attn_ms
 
 
+def measure_prefill_write(torch, K, name, reps=5):
+    """Cache write of a whole prefill (every token of every sequence) per
+    format: bytes = bf16 K and V read + cache bytes written (+ slots)."""
+    from quantized_decode_attention_calibrate_amd import workloads
+    w = workloads.make(name, device="cuda", seed=0)
+    slots = w.slot_mapping
+    T = w.T
+    rec = {"tokens": T, "Hkv": w.Hkv, "D": w.D}
+    st = torch.cuda.current_stream()
+    for tag, eb in (("fp8", 1.0), ("bf16", 2.0), ("nvfp4", NVFP4_BYTES)):
+        if tag == "nvfp4":
+            kc, vc = K.new_nvfp4_caches(w.num_blocks, w.Hkv, w.D, device="cuda")
+            fn = lambda: K.kvq_nvfp4_cache_write(w.k, w.v, slots, kc, vc, 0.01, 0.01)
+        else:
+            kv = K.KVQ_KV_FP8_E4M3 if tag == "fp8" else K.KVQ_KV_BF16
+            kc, vc = K.new_caches(kv, w.num_blocks, w.Hkv, w.D, device="cuda")
+            fn = lambda kv=kv: K.kvq_cache_write(w.k, w.v, slots, kc, vc, kv, 0.01, 0.01)
+        fn()
+        torch.cuda.synchronize()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(st)
+        for _ in range(reps):
+            fn()
+        a1.record(st)
+        torch.cuda.synchronize()
+        us = a0.elapsed_time(a1) / reps * 1e3
+        byts = T * w.Hkv * w.D * 2 * (2 + eb) + T * 8
+        rec[tag] = {"us": round(us, 1), "gbps": round(byts / (us * 1e-6) / 1e9, 1)}
+        del kc, vc
+    del w
+    torch.cuda.empty_cache()
+    return rec
+
+
 def measure_multiquery(torch, K, name, q_lens, steps, warmup):
     """Multi-query decode (speculative-decoding verification) on one
     workload's FP8 caches: the q_len newest tokens attend at once.  Reports
@@ -416,6 +450,8 @@ def main():
         for name in ("agents126k", "mixed64", "nvfp4_131k"):
             print(f"[bench] workload {name}", file=sys.stderr, flush=True)
             result["workloads"][name] = measure_workload(torch, K, name, 60, 10, with_nvfp4=name == "nvfp4_131k")
+        print("[bench] prefill cache writes", file=sys.stderr, flush=True)
+        result["prefill_write"] = {n: measure_prefill_write(torch, K, n) for n in ("nvfp4_131k", "mixed64")}
         print("[bench] multi-query decode", file=sys.stderr, flush=True)
         result["multiquery"] = measure_multiquery(torch, K, "gptoss65k", (2, 4, 8), 200, 20)
     if not args.no_cpu_baseline:

@@ -6,6 +6,8 @@
 // and the OCP E4M3 format with maximum 448; its storage paragraph fixes FP8
 // at one byte per element.  These kernels are HBM/latency bound: one pass
 // over the input, 16-byte loads, no LDS.
+#include <type_traits>
+
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -139,72 +141,93 @@ hipError_t launch_e4m3_decode(const uint8_t* codes, void* out, int kind, int64_t
 }
 
 // ---- cache write -----------------------------------------------------------
-// One thread per (token, head, 8-element chunk of D): a 16-byte load of 8 bf16
-// for K and for V.  K goes to [blk][g][off][D] (one 8-byte store of codes);
-// V goes to [blk][g][D][bs] (8 single-byte stores, stride bs).  The quantize
-// step is an IEEE fp32 division (the scale multiplies code values), so this
-// translation unit must not be built with fast-math.
+// One work-group per (window of 16 consecutive input tokens, KV head).
+// Phase 1, lane order (token, 8-dim chunk) with the chunk fastest: coalesced
+// 16-byte loads of 8 bf16 of K and of V; K codes go straight to their
+// token-major row [blk][g][off][D]; V codes go to an LDS tile [D][16].
+// Phase 2, lane order (dim, token) with the token fastest: V elements leave
+// the tile one per lane to [blk][g][D][bs], so lanes holding consecutive
+// slots write consecutive bytes of one cache row and their stores coalesce,
+// whatever the slot mapping.  The quantize step is an IEEE fp32 division (the
+// scale multiplies code values), so this translation unit must not be built
+// with fast-math.
+constexpr int kWriteTokens = 16;     // tokens per work-group window
+constexpr int kWriteThreads = 256;
+
 template <bool FP8>
-__global__ void __launch_bounds__(256) cache_write_kernel(
+__global__ void __launch_bounds__(kWriteThreads) cache_write_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t src_stride,
     const int64_t* __restrict__ slot_mapping, int T, int Hkv, int D, uint8_t* __restrict__ k_cache,
     uint8_t* __restrict__ v_cache, int bs, float k_scale, float v_scale) {
+    using Elem = typename std::conditional<FP8, uint8_t, uint16_t>::type;
+    extern __shared__ uint32_t lds_w[];
+    Elem* vt = reinterpret_cast<Elem*>(lds_w);   // [D][16] V elements of the window
+    __shared__ int64_t s_slot[kWriteTokens];
+    const int t0 = blockIdx.x * kWriteTokens, g = blockIdx.y;
+    if (threadIdx.x < kWriteTokens) {
+        const int t = t0 + threadIdx.x;
+        s_slot[threadIdx.x] = t < T ? slot_mapping[t] : -1;
+    }
+    __syncthreads();
     const int chunks = D >> 3;
-    const int64_t per_tok = (int64_t)Hkv * chunks;
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= (int64_t)T * per_tok) return;
-    const int t = (int)(i / per_tok);
-    const int rem = (int)(i - (int64_t)t * per_tok);
-    const int g = rem / chunks;
-    const int d0 = (rem - g * chunks) << 3;
-    const int64_t slot = slot_mapping[t];
-    if (slot < 0) return;
-    const int64_t blk = slot / bs;
-    const int off = (int)(slot - blk * bs);
-    const int64_t src = (int64_t)t * src_stride + (int64_t)g * D + d0;
-    const u32x4 kw = *reinterpret_cast<const u32x4*>(k + src);
-    const u32x4 vw = *reinterpret_cast<const u32x4*>(v + src);
-    const int64_t kdst = ((blk * Hkv + g) * bs + off) * D + d0;             // [blk][g][off][d]
-    const int64_t vdst = ((blk * Hkv + g) * (int64_t)D + d0) * bs + off;    // [blk][g][d][off]
-    if constexpr (FP8) {
+    for (int i = threadIdx.x; i < kWriteTokens * chunks; i += kWriteThreads) {
+        const int tw = i / chunks, c = i - tw * chunks, d0 = c << 3;
+        const int64_t slot = s_slot[tw];
+        if (slot < 0) continue;
+        const int64_t blk = slot / bs;
+        const int off = (int)(slot - blk * bs);
+        const int64_t src = (int64_t)(t0 + tw) * src_stride + (int64_t)g * D + d0;
+        const u32x4 kw = *reinterpret_cast<const u32x4*>(k + src);
+        const u32x4 vw = *reinterpret_cast<const u32x4*>(v + src);
+        const int64_t kdst = ((blk * Hkv + g) * bs + off) * D + d0;   // [blk][g][off][d]
+        if constexpr (FP8) {
 #pragma clang fp contract(off)
-        float kf[8], vf[8];
+            float kf[8], vf[8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            kf[2 * j] = bf16_lo(kw[j]) / k_scale;
-            kf[2 * j + 1] = bf16_hi(kw[j]) / k_scale;
-            vf[2 * j] = bf16_lo(vw[j]) / v_scale;
-            vf[2 * j + 1] = bf16_hi(vw[j]) / v_scale;
+            for (int j = 0; j < 4; ++j) {
+                kf[2 * j] = bf16_lo(kw[j]) / k_scale;
+                kf[2 * j + 1] = bf16_hi(kw[j]) / k_scale;
+                vf[2 * j] = bf16_lo(vw[j]) / v_scale;
+                vf[2 * j + 1] = bf16_hi(vw[j]) / v_scale;
+            }
+            u32x2 kc;
+            kc[0] = e4m3_encode4(kf[0], kf[1], kf[2], kf[3]);
+            kc[1] = e4m3_encode4(kf[4], kf[5], kf[6], kf[7]);
+            *reinterpret_cast<u32x2*>(k_cache + kdst) = kc;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) vt[(d0 + j) * kWriteTokens + tw] = (uint8_t)e4m3_encode(vf[j]);
+        } else {
+            *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(k_cache) + kdst) = kw;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                vt[(d0 + 2 * j) * kWriteTokens + tw] = (uint16_t)(vw[j] & 0xFFFFu);
+                vt[(d0 + 2 * j + 1) * kWriteTokens + tw] = (uint16_t)(vw[j] >> 16);
+            }
         }
-        u32x2 kc;
-        kc[0] = e4m3_encode4(kf[0], kf[1], kf[2], kf[3]);
-        kc[1] = e4m3_encode4(kf[4], kf[5], kf[6], kf[7]);
-        *reinterpret_cast<u32x2*>(k_cache + kdst) = kc;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v_cache[vdst + (int64_t)j * bs] = (uint8_t)e4m3_encode(vf[j]);
-    } else {
-        uint16_t* kc = reinterpret_cast<uint16_t*>(k_cache);
-        uint16_t* vc = reinterpret_cast<uint16_t*>(v_cache);
-        *reinterpret_cast<u32x4*>(kc + kdst) = kw;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            vc[vdst + (int64_t)(2 * j) * bs] = (uint16_t)(vw[j] & 0xFFFFu);
-            vc[vdst + (int64_t)(2 * j + 1) * bs] = (uint16_t)(vw[j] >> 16);
-        }
+    }
+    __syncthreads();
+    Elem* vc = reinterpret_cast<Elem*>(v_cache);
+    for (int i = threadIdx.x; i < kWriteTokens * D; i += kWriteThreads) {
+        const int d = i / kWriteTokens, tw = i - d * kWriteTokens;
+        const int64_t slot = s_slot[tw];
+        if (slot < 0) continue;
+        const int64_t blk = slot / bs;
+        const int off = (int)(slot - blk * bs);
+        vc[((blk * Hkv + g) * (int64_t)D + d) * bs + off] = vt[d * kWriteTokens + tw];   // [blk][g][d][off]
     }
 }
 
 hipError_t launch_cache_write(const void* k, const void* v, int64_t src_stride, const int64_t* slots, int T,
                               int Hkv, int D, void* k_cache, void* v_cache, int bs, int kv_dtype,
                               float k_scale, float v_scale, hipStream_t st) {
-    const int64_t threads = (int64_t)T * Hkv * (D >> 3);
-    const unsigned blocks = (unsigned)((threads + 255) / 256);
+    const dim3 grid((unsigned)((T + kWriteTokens - 1) / kWriteTokens), (unsigned)Hkv);
+    const size_t lds = (size_t)kWriteTokens * D * (kv_dtype == 1 ? 1 : 2);
     if (kv_dtype == 1)
-        hipLaunchKernelGGL(cache_write_kernel<true>, dim3(blocks), dim3(256), 0, st, (const uint16_t*)k,
+        hipLaunchKernelGGL(cache_write_kernel<true>, grid, dim3(kWriteThreads), lds, st, (const uint16_t*)k,
                            (const uint16_t*)v, src_stride, slots, T, Hkv, D, (uint8_t*)k_cache,
                            (uint8_t*)v_cache, bs, k_scale, v_scale);
     else
-        hipLaunchKernelGGL(cache_write_kernel<false>, dim3(blocks), dim3(256), 0, st, (const uint16_t*)k,
+        hipLaunchKernelGGL(cache_write_kernel<false>, grid, dim3(kWriteThreads), lds, st, (const uint16_t*)k,
                            (const uint16_t*)v, src_stride, slots, T, Hkv, D, (uint8_t*)k_cache,
                            (uint8_t*)v_cache, bs, k_scale, v_scale);
     return hipGetLastError();
@@ -218,75 +241,98 @@ hipError_t launch_cache_write(const void* k, const void* v, int64_t src_stride, 
 //   code_i = E2M1(x_i / e)  (all zero when e == 0).
 // Region per (block, head): K codes [16][D/2], K scales [16][D/16];
 // V codes [D][8] (token 2j in the low nibble), V scales [D/16][16].
-// One thread per (token, head, group).  K bytes and all scale bytes belong to
-// one token; a V code byte holds two tokens, so V nibbles are merged into
-// their 32-bit word with atomicAnd / atomicOr on disjoint bits.
-__global__ void __launch_bounds__(256) nvfp4_cache_write_kernel(
+// Same windows as the FP8 write.  Phase 1, one lane per (token, group) with
+// the token fastest: block scales and codes; K codes and both scale bytes are
+// stored directly, V codes go to an LDS tile [D][16].  Phase 2, one lane per
+// (dim, token): a V code byte holds the nibbles of slots 2j and 2j+1, so the
+// lane of the even slot stores the whole byte when the odd slot's token is in
+// the same window (the usual case for a prefill); a nibble whose partner is
+// not is merged into its 32-bit word with atomicAnd / atomicOr on its own bits.
+__device__ __forceinline__ void nvfp4_quantize_group(const uint16_t* src, float gscale, uint32_t* codes,
+                                                     uint32_t* bcode) {
+#pragma clang fp contract(off)
+    const u32x4 w0 = *reinterpret_cast<const u32x4*>(src);
+    const u32x4 w1 = *reinterpret_cast<const u32x4*>(src + 8);
+    float xf[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        xf[2 * j] = bf16_lo(w0[j]);
+        xf[2 * j + 1] = bf16_hi(w0[j]);
+        xf[8 + 2 * j] = bf16_lo(w1[j]);
+        xf[8 + 2 * j + 1] = bf16_hi(w1[j]);
+    }
+    float bamax = 0.f;
+    bool nan = false;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const float a = __builtin_fabsf(xf[j]);
+        nan |= __builtin_isnan(a);
+        bamax = a > bamax ? a : bamax;
+    }
+    if (nan) bamax = __builtin_nanf("");
+    const float top = 6.0f * gscale;
+    *bcode = e4m3_encode(bamax / top);
+    const float e = e4m3x2_to_f32(*bcode, false)[0] * gscale;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) codes[j] = e == 0.0f ? 0u : e2m1_encode(xf[j] / e);
+}
+
+__global__ void __launch_bounds__(kWriteThreads) nvfp4_cache_write_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t src_stride,
     const int64_t* __restrict__ slot_mapping, int T, int Hkv, int D, uint8_t* __restrict__ k_cache,
     uint8_t* __restrict__ v_cache, float k_gscale, float v_gscale) {
-#pragma clang fp contract(off)
+    extern __shared__ uint32_t lds_w[];
+    uint8_t* vt = reinterpret_cast<uint8_t*>(lds_w);   // [D][16] V codes of the window, one per byte
+    __shared__ int64_t s_slot[kWriteTokens];
+    const int t0 = blockIdx.x * kWriteTokens, g = blockIdx.y;
+    if (threadIdx.x < kWriteTokens) {
+        const int t = t0 + threadIdx.x;
+        s_slot[threadIdx.x] = t < T ? slot_mapping[t] : -1;
+    }
+    __syncthreads();
     const int groups = D >> 4;
-    const int64_t per_tok = (int64_t)Hkv * groups;
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= (int64_t)T * per_tok) return;
-    const int t = (int)(i / per_tok);
-    const int rem = (int)(i - (int64_t)t * per_tok);
-    const int g = rem / groups;
-    const int grp = rem - g * groups;
-    const int64_t slot = slot_mapping[t];
-    if (slot < 0) return;
-    const int64_t blk = slot / kBlockSize;
-    const int off = (int)(slot - blk * kBlockSize);
     const int64_t region = (int64_t)kBlockSize * D / 2 + (int64_t)kBlockSize * D / 16;
     const int64_t codes_bytes = (int64_t)kBlockSize * D / 2;
-    const int64_t src = (int64_t)t * src_stride + (int64_t)g * D + grp * 16;
+    for (int i = threadIdx.x; i < kWriteTokens * groups; i += kWriteThreads) {
+        const int grp = i / kWriteTokens, tw = i - grp * kWriteTokens;
+        const int64_t slot = s_slot[tw];
+        if (slot < 0) continue;
+        const int64_t blk = slot / kBlockSize;
+        const int off = (int)(slot - blk * kBlockSize);
+        const int64_t src = (int64_t)(t0 + tw) * src_stride + (int64_t)g * D + grp * 16;
+        uint32_t codes[16], bcode;
+        nvfp4_quantize_group(k + src, k_gscale, codes, &bcode);
+        uint8_t* kr = k_cache + (blk * Hkv + g) * region;
+        u32x2 packed = {0u, 0u};
 #pragma unroll
-    for (int which = 0; which < 2; ++which) {
-        const uint16_t* x = which == 0 ? k : v;
-        const float gscale = which == 0 ? k_gscale : v_gscale;
-        const u32x4 w0 = *reinterpret_cast<const u32x4*>(x + src);
-        const u32x4 w1 = *reinterpret_cast<const u32x4*>(x + src + 8);
-        float xf[16];
+        for (int j = 0; j < 16; ++j) packed[j >> 3] |= codes[j] << (4 * (j & 7));
+        *reinterpret_cast<u32x2*>(kr + (int64_t)off * (D / 2) + grp * 8) = packed;
+        kr[codes_bytes + (int64_t)off * groups + grp] = (uint8_t)bcode;
+        nvfp4_quantize_group(v + src, v_gscale, codes, &bcode);
+        v_cache[(blk * Hkv + g) * region + codes_bytes + (int64_t)grp * kBlockSize + off] = (uint8_t)bcode;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            xf[2 * j] = bf16_lo(w0[j]);
-            xf[2 * j + 1] = bf16_hi(w0[j]);
-            xf[8 + 2 * j] = bf16_lo(w1[j]);
-            xf[8 + 2 * j + 1] = bf16_hi(w1[j]);
-        }
-        float bamax = 0.f;
-        bool nan = false;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const float a = __builtin_fabsf(xf[j]);
-            nan |= __builtin_isnan(a);
-            bamax = a > bamax ? a : bamax;
-        }
-        if (nan) bamax = __builtin_nanf("");
-        const float top = 6.0f * gscale;
-        const uint32_t bcode = e4m3_encode(bamax / top);
-        const float e = e4m3x2_to_f32(bcode, false)[0] * gscale;
-        uint32_t codes[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) codes[j] = e == 0.0f ? 0u : e2m1_encode(xf[j] / e);
-        uint8_t* region_base = (which == 0 ? k_cache : v_cache) + (blk * Hkv + g) * region;
-        if (which == 0) {
-            u32x2 packed = {0u, 0u};
-#pragma unroll
-            for (int j = 0; j < 16; ++j) packed[j >> 3] |= codes[j] << (4 * (j & 7));
-            *reinterpret_cast<u32x2*>(region_base + (int64_t)off * (D / 2) + grp * 8) = packed;
-            region_base[codes_bytes + (int64_t)off * groups + grp] = (uint8_t)bcode;
+        for (int j = 0; j < 16; ++j) vt[(grp * 16 + j) * kWriteTokens + tw] = (uint8_t)codes[j];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < kWriteTokens * D; i += kWriteThreads) {
+        const int d = i / kWriteTokens, tw = i - d * kWriteTokens;
+        const int64_t slot = s_slot[tw];
+        if (slot < 0) continue;
+        const int64_t blk = slot / kBlockSize;
+        const int off = (int)(slot - blk * kBlockSize);
+        uint8_t* vr = v_cache + (blk * Hkv + g) * region;
+        const int64_t byte = (int64_t)d * (kBlockSize / 2) + (off >> 1);
+        const uint32_t code = vt[d * kWriteTokens + tw];
+        // the token of the other nibble of this byte, if it is in the window
+        const int pw = (off & 1) ? tw - 1 : tw + 1;
+        const bool paired = pw >= 0 && pw < kWriteTokens && s_slot[pw] == (slot ^ 1);
+        if (paired) {
+            if ((off & 1) == 0) vr[byte] = (uint8_t)(code | (uint32_t)vt[d * kWriteTokens + pw] << 4);
         } else {
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int64_t byte = (int64_t)(grp * 16 + j) * (kBlockSize / 2) + (off >> 1);
-                const unsigned shift = 8u * (unsigned)(byte & 3) + 4u * (unsigned)(off & 1);
-                unsigned* word = reinterpret_cast<unsigned*>(region_base + (byte & ~(int64_t)3));
-                atomicAnd(word, ~(0xFu << shift));
-                atomicOr(word, codes[j] << shift);
-            }
-            region_base[codes_bytes + (int64_t)grp * kBlockSize + off] = (uint8_t)bcode;
+            const unsigned shift = 8u * (unsigned)(byte & 3) + 4u * (unsigned)(off & 1);
+            unsigned* word = reinterpret_cast<unsigned*>(vr + (byte & ~(int64_t)3));
+            atomicAnd(word, ~(0xFu << shift));
+            atomicOr(word, code << shift);
         }
     }
 }
@@ -294,11 +340,10 @@ __global__ void __launch_bounds__(256) nvfp4_cache_write_kernel(
 hipError_t launch_nvfp4_cache_write(const void* k, const void* v, int64_t src_stride, const int64_t* slots, int T,
                                     int Hkv, int D, void* k_cache, void* v_cache, float k_gscale, float v_gscale,
                                     hipStream_t st) {
-    const int64_t threads = (int64_t)T * Hkv * (D >> 4);
-    const unsigned blocks = (unsigned)((threads + 255) / 256);
-    hipLaunchKernelGGL(nvfp4_cache_write_kernel, dim3(blocks), dim3(256), 0, st, (const uint16_t*)k,
-                       (const uint16_t*)v, src_stride, slots, T, Hkv, D, (uint8_t*)k_cache, (uint8_t*)v_cache,
-                       k_gscale, v_gscale);
+    const dim3 grid((unsigned)((T + kWriteTokens - 1) / kWriteTokens), (unsigned)Hkv);
+    hipLaunchKernelGGL(nvfp4_cache_write_kernel, grid, dim3(kWriteThreads), (size_t)kWriteTokens * D, st,
+                       (const uint16_t*)k, (const uint16_t*)v, src_stride, slots, T, Hkv, D, (uint8_t*)k_cache,
+                       (uint8_t*)v_cache, k_gscale, v_gscale);
     return hipGetLastError();
 }
 

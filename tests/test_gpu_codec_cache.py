@@ -140,6 +140,31 @@ def test_cache_write_skips_and_strided_source(K):
     assert np.array_equal(bits_u8(kc), okc) and np.array_equal(bits_u8(vc), ovc)
 
 
+@pytest.mark.parametrize("kv", [0, 1])
+@pytest.mark.parametrize("order", ["offset5", "offset1_reversed", "shuffled"])
+def test_cache_write_any_slot_order(K, kv, order):
+    # the write works in windows of 16 input tokens; runs of slots that start
+    # mid-block, run backwards or are shuffled must give the oracle's bytes
+    w = workloads.make("mixed64", seed=10, seq_lens=[203], shape=dict(Hq=4, Hkv=2, D=64))
+    T, nb = w.T, 16
+    if order == "offset5":
+        sm = torch.arange(T, dtype=torch.int64) + 5
+    elif order == "offset1_reversed":
+        sm = torch.arange(T, dtype=torch.int64).flip(0) + 1
+    else:
+        sm = torch.randperm(nb * 16, generator=torch.Generator().manual_seed(2))[:T].to(torch.int64)
+    ks, vs = (0.02, 0.013) if kv == 1 else (1.0, 1.0)
+    kc, vc = K.new_caches(kv, nb, w.Hkv, w.D)
+    kc.view(torch.uint8).fill_(0xA5)
+    vc.view(torch.uint8).fill_(0xA5)
+    K.kvq_cache_write(w.k.cuda(), w.v.cuda(), sm.cuda(), kc, vc, kv, ks, vs)
+    kvd = oracle.KV_FP8 if kv == 1 else oracle.KV_BF16
+    fill = 0xA5 if kv == 1 else 0xA5A5
+    okc, ovc = oracle.new_caches(kvd, nb, w.Hkv, w.D, 16, fill=fill)
+    oracle.cache_write(w.k, w.v, sm, okc, ovc, kvd, ks, vs)
+    assert np.array_equal(bits_u8(kc), okc.view(np.uint8)) and np.array_equal(bits_u8(vc), ovc.view(np.uint8))
+
+
 @pytest.mark.parametrize("scale", [1.0, 2.0 ** -7, 0.0117, 3.3, 1e-12, 448.0])
 def test_cache_write_every_bf16_pattern(K, scale):
     # 65536 bf16 patterns as K (and reversed as V) of 512 tokens x 2 heads x 64 dims

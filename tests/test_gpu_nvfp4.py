@@ -90,6 +90,31 @@ def test_nvfp4_write_keeps_the_other_nibble(K):
     assert np.array_equal(kc.cpu().numpy(), okc) and np.array_equal(vc.cpu().numpy(), ovc)
 
 
+@pytest.mark.parametrize("order", ["offset5", "offset1_reversed", "shuffled", "pairs_split"])
+def test_nvfp4_write_any_slot_order(K, order):
+    # windows of 16 input tokens write whole V bytes when both slots of a byte
+    # are adjacent in the window, else nibbles; every order must give the
+    # oracle's bytes
+    w = workloads.make("mixed64", seed=11, seq_lens=[203], shape=dict(Hq=4, Hkv=2, D=64))
+    T, nb = w.T, 16
+    if order == "offset5":
+        sm = torch.arange(T, dtype=torch.int64) + 5
+    elif order == "offset1_reversed":
+        sm = torch.arange(T, dtype=torch.int64).flip(0) + 1
+    elif order == "shuffled":
+        sm = torch.randperm(nb * 16, generator=torch.Generator().manual_seed(3))[:T].to(torch.int64)
+    else:   # token 2j -> slot 2j+1 and 2j+1 -> 2j: partners adjacent but swapped
+        sm = torch.arange(T, dtype=torch.int64) ^ 1
+    gk, gv = gpu_gscales(K, w)
+    kc, vc = K.new_nvfp4_caches(nb, w.Hkv, w.D)
+    kc.fill_(0x3C)
+    vc.fill_(0x3C)
+    K.kvq_nvfp4_cache_write(w.k.cuda(), w.v.cuda(), sm.cuda(), kc, vc, gk, gv)
+    okc, ovc = oracle.new_caches(oracle.KV_NVFP4, nb, w.Hkv, w.D, 16, fill=0x3C)
+    oracle.nvfp4_cache_write(w.k, w.v, sm, okc, ovc, 16, gk, gv)
+    assert np.array_equal(kc.cpu().numpy(), okc) and np.array_equal(vc.cpu().numpy(), ovc)
+
+
 CASES = [
     ("tiny", 0, None, None),
     ("nvfp4_131k", 1, [1000, 4097], dict(Hq=16, Hkv=2)),
