@@ -62,7 +62,7 @@ def lib() -> ctypes.CDLL:
             "kvqo_nvfp4_v_value": (D, [P, I64, I, I, I, I, I, F]),
             "kvqo_decode_attn": (None, [P, P, P, I, P, I, P, I, I, I, I, I, F, F, F, P, I]),
             "kvqo_decode_attn_units": (None, [P, P, P, I, P, I, P, I, I, I, I, I, F, F, F, P, I, P, I]),
-            "kvqo_decode_attn_mq": (None, [P, I, P, P, I, P, I, P, I, I, I, I, I, F, F, F, P, I]),
+            "kvqo_decode_attn_mq": (None, [P, I, I, P, P, I, P, I, P, I, I, I, I, I, F, F, F, P, I]),
             "kvqo_fp8_cos_sim": (D, [P, I64, F]),
         }
         for name, (res, args) in sig.items():
@@ -230,9 +230,10 @@ def decode_attn(q, k_cache: np.ndarray, v_cache: np.ndarray, kv_dtype: int, bloc
 
 def decode_attn_mq(q, k_cache: np.ndarray, v_cache: np.ndarray, kv_dtype: int, block_tables, seq_lens,
                    Hkv: int, block_size: int, k_scale: float, v_scale: float, sm_scale: float,
-                   nthreads: int = 1) -> np.ndarray:
+                   nthreads: int = 1, window: int = 0) -> np.ndarray:
     """fp64 multi-query attention output [B][q_len][Hq][D] for q [B][q_len][Hq][D]
-    (query i of sequence b attends causally to tokens 0 .. seq_len - q_len + i)."""
+    (query i of sequence b, at position p = seq_len - q_len + i, attends causally
+    to tokens 0 .. p, or to its `window` newest tokens when window > 0)."""
     qb = _bits16(q)
     B, q_len, Hq, D = qb.shape
     bt = np.ascontiguousarray(np.asarray(block_tables, dtype=np.int32))
@@ -240,7 +241,7 @@ def decode_attn_mq(q, k_cache: np.ndarray, v_cache: np.ndarray, kv_dtype: int, b
     assert bt.shape[0] == B and sl.shape == (B,)
     kc, vc = np.ascontiguousarray(k_cache), np.ascontiguousarray(v_cache)
     out = np.zeros((B, q_len, Hq, D), dtype=np.float64)
-    lib().kvqo_decode_attn_mq(_ptr(qb), q_len, _ptr(kc), _ptr(vc), kv_dtype, _ptr(bt), bt.shape[1], _ptr(sl),
+    lib().kvqo_decode_attn_mq(_ptr(qb), q_len, window, _ptr(kc), _ptr(vc), kv_dtype, _ptr(bt), bt.shape[1], _ptr(sl),
                               B, Hq, Hkv, D, block_size, k_scale, v_scale, sm_scale, _ptr(out), nthreads)
     return out
 

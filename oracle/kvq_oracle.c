@@ -274,6 +274,7 @@ typedef struct {
     const int32_t* units; /* NULL: unit u is (b, i, h) = (u / (q_len*Hq), u / Hq % q_len, u % Hq) */
     int n_units;
     int q_len;            /* queries per sequence: the q_len newest tokens */
+    int window;           /* > 0: each query sees at most its `window` newest tokens */
     double* out;
     int next_unit;
     pthread_mutex_t lock;
@@ -297,9 +298,9 @@ static double v_value(const attn_job* j, int64_t slot, int g, int d) {
     return kvqo_e4m3_value(((const uint8_t*)j->v_cache)[i]) * (double)j->v_scale;
 }
 
-/* Query i of sequence b (the token at position seq_len - q_len + i) attends
- * causally: to tokens 0 .. seq_len - q_len + i, i.e. L = seq_len - q_len + 1 + i
- * of them; out = 0 when L <= 0. */
+/* Query i of sequence b (the token at position p = seq_len - q_len + i)
+ * attends causally: to tokens 0 .. p, i.e. L = p + 1 of them, or with a
+ * sliding window W > 0 to tokens max(0, p - W + 1) .. p; out = 0 when L <= 0. */
 static void attend_one(const attn_job* j, int b, int i, int h, double* out, double* s) {
     int G = j->Hq / j->Hkv;
     int g = h / G;
@@ -308,8 +309,9 @@ static void attend_one(const attn_job* j, int b, int i, int h, double* out, doub
     const uint16_t* q = j->q + (((int64_t)b * j->q_len + i) * j->Hq + h) * D;
     for (int d = 0; d < D; ++d) out[d] = 0.0;
     if (L <= 0) return;
+    int t0 = (j->window > 0 && L > j->window) ? L - j->window : 0;
     double m = -INFINITY;
-    for (int t = 0; t < L; ++t) {
+    for (int t = t0; t < L; ++t) {
         int64_t slot = (int64_t)j->block_tables[(int64_t)b * j->max_blocks + t / j->block_size] *
                            j->block_size + t % j->block_size;
         double dot = 0.0;
@@ -318,7 +320,7 @@ static void attend_one(const attn_job* j, int b, int i, int h, double* out, doub
         if (s[t] > m) m = s[t];
     }
     double denom = 0.0;
-    for (int t = 0; t < L; ++t) {
+    for (int t = t0; t < L; ++t) {
         int64_t slot = (int64_t)j->block_tables[(int64_t)b * j->max_blocks + t / j->block_size] *
                            j->block_size + t % j->block_size;
         double w = exp(s[t] - m);
@@ -377,18 +379,18 @@ void kvqo_decode_attn(const uint16_t* q, const void* k_cache, const void* v_cach
                       double* out, int nthreads) {
     attn_job j = {q, k_cache, v_cache, kv_dtype, block_tables, max_blocks, seq_lens,
                   B, Hq, Hkv, D, block_size, k_scale, v_scale, sm_scale,
-                  NULL, B * Hq, 1, out, 0};
+                  NULL, B * Hq, 1, 0, out, 0};
     run_attn(&j, nthreads);
 }
 
-void kvqo_decode_attn_mq(const uint16_t* q, int q_len, const void* k_cache, const void* v_cache,
+void kvqo_decode_attn_mq(const uint16_t* q, int q_len, int window, const void* k_cache, const void* v_cache,
                          int kv_dtype, const int32_t* block_tables, int max_blocks,
                          const int32_t* seq_lens, int B, int Hq, int Hkv, int D,
                          int block_size, float k_scale, float v_scale, float sm_scale,
                          double* out, int nthreads) {
     attn_job j = {q, k_cache, v_cache, kv_dtype, block_tables, max_blocks, seq_lens,
                   B, Hq, Hkv, D, block_size, k_scale, v_scale, sm_scale,
-                  NULL, B * q_len * Hq, q_len, out, 0};
+                  NULL, B * q_len * Hq, q_len, window, out, 0};
     run_attn(&j, nthreads);
 }
 
@@ -399,7 +401,7 @@ void kvqo_decode_attn_units(const uint16_t* q, const void* k_cache, const void* 
                             const int32_t* units, int n_units, double* out, int nthreads) {
     attn_job j = {q, k_cache, v_cache, kv_dtype, block_tables, max_blocks, seq_lens,
                   B, Hq, Hkv, D, block_size, k_scale, v_scale, sm_scale,
-                  units, n_units, 1, out, 0};
+                  units, n_units, 1, 0, out, 0};
     run_attn(&j, nthreads);
 }
 

@@ -148,10 +148,11 @@ void kvqo_decode_attn(const uint16_t* q, const void* k_cache, const void* v_cach
 /* Multi-query decode (the verification step of speculative decoding): the
  * q_len newest tokens of each sequence, all already in the cache, attend at
  * once, each causally.  q is bf16 [B][q_len][Hq][D]; query i of sequence b
- * is the token at position seq_lens[b] - q_len + i and attends to tokens
- * 0 .. seq_lens[b] - q_len + i (out = 0 if there are none).  out is fp64
- * [B][q_len][Hq][D].  q_len = 1 is kvqo_decode_attn. */
-void kvqo_decode_attn_mq(const uint16_t* q, int q_len, const void* k_cache, const void* v_cache,
+ * is the token at position p = seq_lens[b] - q_len + i and attends to tokens
+ * 0 .. p, or with a sliding window W = window > 0 to tokens
+ * max(0, p - W + 1) .. p (out = 0 if there are none).  out is fp64
+ * [B][q_len][Hq][D].  q_len = 1, window = 0 is kvqo_decode_attn. */
+void kvqo_decode_attn_mq(const uint16_t* q, int q_len, int window, const void* k_cache, const void* v_cache,
                          int kv_dtype, const int32_t* block_tables, int max_blocks,
                          const int32_t* seq_lens, int B, int Hq, int Hkv, int D,
                          int block_size, float k_scale, float v_scale, float sm_scale,
