@@ -211,6 +211,20 @@ def measure_multiquery(torch, K, name, q_lens, steps, warmup):
 
     t1 = timed(lambda i: L.attend(i))
     rec["q_len_1_us"] = round(t1, 2)
+    # sliding window (gpt-oss alternates full layers with 128-token windows):
+    # the call reads only the window's blocks
+    for W in (128, 4096):
+        q1 = w.q[:, None].contiguous()
+        out = torch.empty(w.B, 1, w.Hq, w.D, dtype=torch.bfloat16, device="cuda")
+        ws = K.new_workspace_mq(w.B, 1, w.Hq, w.Hkv, w.D, w.max_seq_len, window=W)
+
+        def call_w(i, q1=q1, out=out, ws=ws, W=W):
+            kc, vc = L.caches[i % L.R]
+            K.kvq_paged_decode_attn_mq(q1, kc, vc, K.KVQ_KV_FP8_E4M3, L.bt, L.sl, w.max_seq_len, w.Hkv, L.ks, L.vs,
+                                       L.sm, out, ws, window=W)
+        us = timed(call_w)
+        wb, _ = step_bytes(w.B, w.Hq, w.Hkv, w.D, [min(W, n) for n in w.seq_lens], 1, w.B)
+        rec[f"window_{W}"] = {"attn_us": round(us, 2), "attn_gbps": round(wb / (us * 1e-6) / 1e9, 1)}
     for ql in q_lens:
         q = workloads.mq_queries(w, ql, seed=0).cuda()
         out = torch.empty(w.B, ql, w.Hq, w.D, dtype=torch.bfloat16, device="cuda")

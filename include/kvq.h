@@ -237,7 +237,7 @@ int kvq_nvfp4_paged_decode_attn_ex(const void* q_dev, const void* k_cache_dev, c
                                    void* workspace_dev, size_t workspace_bytes, void* hip_stream,
                                    int split_tokens);
 
-/* ---- multi-query decode (speculative-decoding verification) ---------------
+/* ---- multi-query and sliding-window decode ---------------------------------
  * The verification step of speculative decoding (multi-token prediction and
  * draft models on the Radiance spec-decode campaign page, the DFlash and MTP
  * lanes of the dual-R9700 page): the q_len newest tokens of every sequence
@@ -247,26 +247,33 @@ int kvq_nvfp4_paged_decode_attn_ex(const void* q_dev, const void* k_cache_dev, c
  * seq_lens[b] - q_len + i and attends to tokens 0 .. seq_lens[b] - q_len + i:
  *   out[b][i][h][:] = the kvq_paged_decode_attn result of q[b][i][h] over the
  *                     first seq_lens[b] - q_len + 1 + i tokens (0 if none).
+ * window > 0 restricts every query to its `window` newest tokens (sliding-
+ * window attention, the layer type the dual-R9700 page's SWA section says
+ * vLLM's ROCm custom paged path cannot serve): query i at position p sees
+ * tokens max(0, p - window + 1) .. p.  Splits start at the window, so the
+ * cost follows the window, not the sequence; block-table entries of blocks
+ * wholly before the first query's window are never read (they may be stale
+ * or freed).  window = 0 is full causal attention.
  * The cache is read once for all q_len queries: the G * q_len (query, head)
  * pairs of a KV head share each K/V load as MFMA columns.
  *   q_dev      bf16 [B][q_len][Hq][D]      out_dev  [B][q_len][Hq][D]
- *   workspace  >= kvq_decode_workspace_bytes_mq(...) bytes (same rules as
- *              kvq_paged_decode_attn's)
+ *   workspace  >= kvq_decode_workspace_bytes_mq(...) bytes for the same
+ *              q_len and window (same rules as kvq_paged_decode_attn's)
  * Other arguments and errors as kvq_paged_decode_attn[_ex] (MFMA family only).
  * Supported: 1 <= q_len <= 16 and G * q_len <= 64 at D 64, <= 32 at D 128,
- * <= 16 at D 256 (KVQ_EUNSUPPORTED otherwise); q_len = 1 is the single-token
- * decode. */
-size_t kvq_decode_workspace_bytes_mq(int B, int q_len, int Hq, int Hkv, int D, int max_seq_len,
+ * <= 16 at D 256 (KVQ_EUNSUPPORTED otherwise), window >= 0; q_len = 1 with
+ * window = 0 is the single-token decode. */
+size_t kvq_decode_workspace_bytes_mq(int B, int q_len, int window, int Hq, int Hkv, int D, int max_seq_len,
                                      int block_size, int split_tokens);
-int kvq_paged_decode_attn_mq(const void* q_dev, int q_len, const void* k_cache_dev, const void* v_cache_dev,
-                             int kv_dtype, const int32_t* block_tables_dev, int max_blocks_per_seq,
+int kvq_paged_decode_attn_mq(const void* q_dev, int q_len, int window, const void* k_cache_dev,
+                             const void* v_cache_dev, int kv_dtype, const int32_t* block_tables_dev, int max_blocks_per_seq,
                              const int32_t* seq_lens_dev, int max_seq_len,
                              int B, int Hq, int Hkv, int D, int block_size, int num_blocks,
                              float k_scale, float v_scale, float sm_scale,
                              void* out_dev, int out_dtype,
                              void* workspace_dev, size_t workspace_bytes, void* hip_stream,
                              int split_tokens);
-int kvq_nvfp4_paged_decode_attn_mq(const void* q_dev, int q_len, const void* k_cache_dev,
+int kvq_nvfp4_paged_decode_attn_mq(const void* q_dev, int q_len, int window, const void* k_cache_dev,
                                    const void* v_cache_dev, const int32_t* block_tables_dev,
                                    int max_blocks_per_seq, const int32_t* seq_lens_dev, int max_seq_len,
                                    int B, int Hq, int Hkv, int D, int block_size, int num_blocks,

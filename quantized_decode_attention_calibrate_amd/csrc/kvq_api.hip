@@ -189,14 +189,23 @@ size_t kvq_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_seq_len
     return kvq_decode_workspace_bytes_ex(B, Hq, Hkv, D, max_seq_len, block_size, 0);
 }
 
-static int decode_common(int fmt, const void* q_dev, int q_len, const void* k_cache_dev, const void* v_cache_dev,
+// Token span the split plan covers: with a window W, a sequence's splits
+// start at most W + q_len - 1 tokens (plus chunk rounding) before its end.
+static int plan_span(int max_seq_len, int q_len, int window) {
+    if (window <= 0) return max_seq_len;
+    const int64_t span = (int64_t)window + q_len - 1 + (kChunkTokens - 1);
+    return span < max_seq_len ? (int)span : max_seq_len;
+}
+
+static int decode_common(int fmt, const void* q_dev, int q_len, int window, const void* k_cache_dev,
+                         const void* v_cache_dev,
                          const int32_t* block_tables_dev, int max_blocks_per_seq, const int32_t* seq_lens_dev,
                          int max_seq_len, int B, int Hq, int Hkv, int D, int block_size, int num_blocks,
                          float k_scale, float v_scale, float sm_scale, void* out_dev, int out_dtype,
                          void* workspace_dev, size_t workspace_bytes, void* hip_stream, int impl, int split_tokens) {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_seq_len < 0)
         return KVQ_EINVAL;
-    if (q_len < 1 || q_len > kMaxQueryLen) return KVQ_EINVAL;
+    if (q_len < 1 || q_len > kMaxQueryLen || window < 0) return KVQ_EINVAL;
     if (Hq % Hkv != 0) return KVQ_EINVAL;
     if (out_dtype != KVQ_OUT_BF16 && out_dtype != KVQ_OUT_F32) return KVQ_EINVAL;
     if (impl < KVQ_IMPL_AUTO || impl > KVQ_IMPL_MFMA) return KVQ_EINVAL;
@@ -205,7 +214,8 @@ static int decode_common(int fmt, const void* q_dev, int q_len, const void* k_ca
     if (!supported_d(D) || block_size != kBlockSize) return KVQ_EUNSUPPORTED;
     const int G = Hq / Hkv;
     if (G > 16) return KVQ_EUNSUPPORTED;
-    if (q_len > 1 && (impl == KVQ_IMPL_VALU || decode_column_tiles(G, q_len, D) == 0)) return KVQ_EUNSUPPORTED;
+    if ((q_len > 1 || window > 0) && impl == KVQ_IMPL_VALU) return KVQ_EUNSUPPORTED;
+    if (decode_column_tiles(G, q_len, D) == 0) return KVQ_EUNSUPPORTED;
     if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * block_size) return KVQ_EINVAL;
     if (!isfinite(sm_scale) || !(sm_scale > 0.0f)) return KVQ_EINVAL;
     if (fmt != kFmtBF16 && (!good_scale(k_scale) || !good_scale(v_scale))) return KVQ_EINVAL;
@@ -216,7 +226,7 @@ static int decode_common(int fmt, const void* q_dev, int q_len, const void* k_ca
     if (!aligned16(q_dev) || !aligned16(k_cache_dev) || !aligned16(v_cache_dev) || !aligned16(out_dev) ||
         !aligned16(workspace_dev))
         return KVQ_EINVAL;
-    const DecodePlan plan = plan_decode(B, Hkv, max_seq_len, split_tokens);
+    const DecodePlan plan = plan_decode(B, Hkv, plan_span(max_seq_len, q_len, window), split_tokens);
     if (plan.num_splits > kMaxSplits) return KVQ_EUNSUPPORTED;
     const size_t need = decode_workspace_bytes(B * q_len, Hq, D, plan.num_splits);
     if (workspace_bytes < need) return KVQ_EWORKSPACE;
@@ -242,6 +252,7 @@ static int decode_common(int fmt, const void* q_dev, int q_len, const void* k_ca
     a.v_scale = scaled ? v_scale : 1.0f;
     a.out_f32 = out_dtype == KVQ_OUT_F32;
     a.q_len = q_len;
+    a.window = window;
     return hip_status(launch_decode(a, B, D, fmt, impl, (hipStream_t)hip_stream));
 }
 
@@ -252,7 +263,7 @@ int kvq_paged_decode_attn_ex(const void* q_dev, const void* k_cache_dev, const v
                              void* workspace_dev, size_t workspace_bytes, void* hip_stream, int impl,
                              int split_tokens) {
     if (kv_dtype != KVQ_KV_BF16 && kv_dtype != KVQ_KV_FP8_E4M3) return KVQ_EINVAL;
-    return decode_common(kv_dtype == KVQ_KV_FP8_E4M3 ? kFmtFP8 : kFmtBF16, q_dev, 1, k_cache_dev, v_cache_dev,
+    return decode_common(kv_dtype == KVQ_KV_FP8_E4M3 ? kFmtFP8 : kFmtBF16, q_dev, 1, 0, k_cache_dev, v_cache_dev,
                          block_tables_dev, max_blocks_per_seq, seq_lens_dev, max_seq_len, B, Hq, Hkv, D,
                          block_size, num_blocks, k_scale, v_scale, sm_scale, out_dev, out_dtype, workspace_dev,
                          workspace_bytes, hip_stream, impl, split_tokens);
@@ -264,7 +275,7 @@ int kvq_nvfp4_paged_decode_attn_ex(const void* q_dev, const void* k_cache_dev, c
                                    int block_size, int num_blocks, float k_gscale, float v_gscale, float sm_scale,
                                    void* out_dev, int out_dtype, void* workspace_dev, size_t workspace_bytes,
                                    void* hip_stream, int split_tokens) {
-    return decode_common(kFmtNVFP4, q_dev, 1, k_cache_dev, v_cache_dev, block_tables_dev, max_blocks_per_seq,
+    return decode_common(kFmtNVFP4, q_dev, 1, 0, k_cache_dev, v_cache_dev, block_tables_dev, max_blocks_per_seq,
                          seq_lens_dev, max_seq_len, B, Hq, Hkv, D, block_size, num_blocks, k_gscale, v_gscale,
                          sm_scale, out_dev, out_dtype, workspace_dev, workspace_bytes, hip_stream, KVQ_IMPL_MFMA,
                          split_tokens);
@@ -281,37 +292,39 @@ int kvq_nvfp4_paged_decode_attn(const void* q_dev, const void* k_cache_dev, cons
                                           workspace_bytes, hip_stream, 0);
 }
 
-size_t kvq_decode_workspace_bytes_mq(int B, int q_len, int Hq, int Hkv, int D, int max_seq_len, int block_size,
-                                     int split_tokens) {
+size_t kvq_decode_workspace_bytes_mq(int B, int q_len, int window, int Hq, int Hkv, int D, int max_seq_len,
+                                     int block_size, int split_tokens) {
     (void)block_size;
-    if (q_len < 1 || q_len > kMaxQueryLen) return 0;
+    if (q_len < 1 || q_len > kMaxQueryLen || window < 0) return 0;
     if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || max_seq_len < 0) return 0;
     if (split_tokens < 0 || split_tokens % kChunkTokens != 0 || split_tokens > kMaxSplitTokens) return 0;
-    const DecodePlan p = plan_decode(B, Hkv, max_seq_len, split_tokens);
+    const DecodePlan p = plan_decode(B, Hkv, plan_span(max_seq_len, q_len, window), split_tokens);
     if (p.num_splits > kMaxSplits) return 0;
     return decode_workspace_bytes(B * q_len, Hq, D, p.num_splits);
 }
 
-int kvq_paged_decode_attn_mq(const void* q_dev, int q_len, const void* k_cache_dev, const void* v_cache_dev,
-                             int kv_dtype, const int32_t* block_tables_dev, int max_blocks_per_seq,
+int kvq_paged_decode_attn_mq(const void* q_dev, int q_len, int window, const void* k_cache_dev,
+                             const void* v_cache_dev, int kv_dtype, const int32_t* block_tables_dev, int max_blocks_per_seq,
                              const int32_t* seq_lens_dev, int max_seq_len, int B, int Hq, int Hkv, int D,
                              int block_size, int num_blocks, float k_scale, float v_scale, float sm_scale,
                              void* out_dev, int out_dtype, void* workspace_dev, size_t workspace_bytes,
                              void* hip_stream, int split_tokens) {
     if (kv_dtype != KVQ_KV_BF16 && kv_dtype != KVQ_KV_FP8_E4M3) return KVQ_EINVAL;
-    return decode_common(kv_dtype == KVQ_KV_FP8_E4M3 ? kFmtFP8 : kFmtBF16, q_dev, q_len, k_cache_dev,
+    return decode_common(kv_dtype == KVQ_KV_FP8_E4M3 ? kFmtFP8 : kFmtBF16, q_dev, q_len, window, k_cache_dev,
                          v_cache_dev, block_tables_dev, max_blocks_per_seq, seq_lens_dev, max_seq_len, B, Hq, Hkv,
                          D, block_size, num_blocks, k_scale, v_scale, sm_scale, out_dev, out_dtype, workspace_dev,
                          workspace_bytes, hip_stream, KVQ_IMPL_MFMA, split_tokens);
 }
 
-int kvq_nvfp4_paged_decode_attn_mq(const void* q_dev, int q_len, const void* k_cache_dev, const void* v_cache_dev,
+int kvq_nvfp4_paged_decode_attn_mq(const void* q_dev, int q_len, int window, const void* k_cache_dev,
+                                   const void* v_cache_dev,
                                    const int32_t* block_tables_dev, int max_blocks_per_seq,
                                    const int32_t* seq_lens_dev, int max_seq_len, int B, int Hq, int Hkv, int D,
                                    int block_size, int num_blocks, float k_gscale, float v_gscale, float sm_scale,
                                    void* out_dev, int out_dtype, void* workspace_dev, size_t workspace_bytes,
                                    void* hip_stream, int split_tokens) {
-    return decode_common(kFmtNVFP4, q_dev, q_len, k_cache_dev, v_cache_dev, block_tables_dev, max_blocks_per_seq,
+    return decode_common(kFmtNVFP4, q_dev, q_len, window, k_cache_dev, v_cache_dev, block_tables_dev,
+                         max_blocks_per_seq,
                          seq_lens_dev, max_seq_len, B, Hq, Hkv, D, block_size, num_blocks, k_gscale, v_gscale,
                          sm_scale, out_dev, out_dtype, workspace_dev, workspace_bytes, hip_stream, KVQ_IMPL_MFMA,
                          split_tokens);

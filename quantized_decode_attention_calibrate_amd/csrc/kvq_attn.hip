@@ -64,14 +64,31 @@ __host__ __device__ constexpr int lds_merge_floats(int GQ, int D, int W, int NT 
 }
 
 // Stage the physical block ids of logical blocks [lb0, lb0 + n) into LDS,
-// clamping logical blocks past the sequence to its last block (those tokens
-// are masked; the clamp only keeps every address inside the cache).
+// clamping logical blocks past the sequence to its last block and blocks
+// before a sliding window to the window's first block (those tokens are
+// masked; the clamp keeps every address inside the cache and reads no table
+// entry outside [first_lb, last_lb]).
 __device__ __forceinline__ void stage_block_ids(int* s_blk, const int32_t* bt_row, int lb0, int n,
-                                                int last_lb) {
+                                                int first_lb, int last_lb) {
     for (int i = threadIdx.x; i < n; i += blockDim.x) {
-        int lb = min(lb0 + i, last_lb);
+        int lb = min(max(lb0 + i, first_lb), last_lb);
         s_blk[i] = bt_row[lb];
     }
+}
+
+// Token range of sequence b's work-groups.  Query i is the token at position
+// p = L - q_len + i and sees tokens max(0, p - window + 1) .. p (window 0:
+// from 0).  `first` is the first token any query sees; splits start at
+// `base` = first rounded down to a chunk, so no split lies wholly before it.
+struct SeqRange {
+    int L, first, base;
+};
+__device__ __forceinline__ SeqRange seq_range(const DecodeArgs& a, int b) {
+    SeqRange r;
+    r.L = a.seq_lens[b];
+    r.first = a.window > 0 ? max(0, r.L - a.q_len - a.window + 1) : 0;
+    r.base = r.first & ~(kChunkTokens - 1);
+    return r;
 }
 
 // Merge the 4 waves' (m, l, acc) held in LDS into this split's result.  If the
@@ -266,14 +283,15 @@ __device__ __forceinline__ f16x8 v_operand_f16(const MfmaChunk<D, FMT>& c, int d
 }
 
 // One 64-token chunk for all NT column tiles: K and V are unpacked once and
-// shared by the tiles.  `cend[nt]` is the exclusive causal end of this lane's
-// column in tile nt (tok_end for single-token decode); `tail_from` is the
-// smallest of them over the work-group, so chunks below it need no masking.
+// shared by the tiles.  This lane's column in tile nt sees tokens
+// [cbeg[nt], cend[nt]) (cbeg 0 and cend = tok_end for single-token decode
+// without a window).  Chunks in [head_until, tail_from) need no masking;
+// V data of tokens outside [vbeg, tok_end) is zeroed.
 template <int D, int FMT, int NT>
 __device__ __forceinline__ void mfma_process(MfmaState<D, NT>& st, MfmaChunk<D, FMT>& c,
                                              const QkOperand<FMT> (*qb)[2 * (D / 64)], const float* cs,
-                                             const int* cend, int chunk_tok, int tok_end, int tail_from,
-                                             int grp) {
+                                             const int* cbeg, const int* cend, int chunk_tok, int tok_end,
+                                             int tail_from, int head_until, int vbeg, int grp) {
     constexpr int KJ = D / 64, DT = D / 16;
     constexpr bool kF16V = FMT != kFmtBF16;   // V operand in f16 (FP8, NVFP4) or bf16
     // ---- S = K Q^T ---------------------------------------------------------
@@ -307,7 +325,7 @@ __device__ __forceinline__ void mfma_process(MfmaState<D, NT>& st, MfmaChunk<D, 
     // max m is kept in scaled units.  Masking runs only on chunks that reach a
     // column's end (a wave-uniform branch).  A column that has seen no token
     // yet keeps m = -inf; its weights are 0 and alpha is 0.
-    const bool tail = chunk_tok + kChunkTokens > tail_from;
+    const bool tail = chunk_tok + kChunkTokens > tail_from || chunk_tok < head_until;
     const int tok0 = chunk_tok + 16 * grp;   // token of sv[.][0]
     f16x8 pfh[NT][2], pfl[NT][2];
     bf16x8 pbh[NT][2], pbl[NT][2];
@@ -315,10 +333,10 @@ __device__ __forceinline__ void mfma_process(MfmaState<D, NT>& st, MfmaChunk<D, 
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         if (tail) {
-            const int valid = cend[nt] - tok0;   // tokens of block grp this column sees
+            const int lo = cbeg[nt] - tok0, hi = cend[nt] - tok0;   // offsets of block grp this column sees
 #pragma unroll
             for (int e = 0; e < 16; ++e)  // sv[4i + r] is token offset 4i + r of block grp
-                if (e >= valid) sv[nt][e] = -INFINITY;
+                if (e >= hi || e < lo) sv[nt][e] = -INFINITY;
         }
         float mloc = sv[nt][0];
 #pragma unroll
@@ -364,13 +382,14 @@ __device__ __forceinline__ void mfma_process(MfmaState<D, NT>& st, MfmaChunk<D, 
         st.l_run[nt] = st.l_run[nt] * alpha[nt] + psum;
     }
 
-    // Zero V data of tokens past the sequence end: their weight is 0 but the
-    // bytes may be anything (NaN codes).  FP8: V bytes; NVFP4: the tokens' block
-    // scales (the E2M1 codes are always finite); BF16: V halfwords.  Tokens
-    // inside the sequence but past a column's causal end are finite; their
-    // weight is 0.
-    if (chunk_tok + kChunkTokens > tok_end) {
-        const int valid = tok_end - tok0;
+    // Zero V data of tokens past the sequence end and before the window: their
+    // weight is 0 but the bytes may be anything (unwritten slots, or another
+    // block's data through the clamped block ids).  FP8: V bytes; NVFP4: the
+    // tokens' block scales (the E2M1 codes are always finite); BF16: V
+    // halfwords.  Tokens inside [vbeg, tok_end) but outside a column's range
+    // are finite; their weight is 0.
+    if (chunk_tok + kChunkTokens > tok_end || chunk_tok < vbeg) {
+        const int valid = tok_end - tok0, vlo = vbeg - tok0;
         if constexpr (FMT == kFmtBF16) {
             u32x4 keep[2];
 #pragma unroll
@@ -380,7 +399,7 @@ __device__ __forceinline__ void mfma_process(MfmaState<D, NT>& st, MfmaChunk<D, 
                     uint32_t mask = 0;
 #pragma unroll
                     for (int e = 0; e < 2; ++e)
-                        if (8 * x + 2 * w + e < valid) mask |= 0xFFFFu << (16 * e);
+                        if (8 * x + 2 * w + e < valid && 8 * x + 2 * w + e >= vlo) mask |= 0xFFFFu << (16 * e);
                     keep[x][w] = mask;
                 }
 #pragma unroll
@@ -395,7 +414,7 @@ __device__ __forceinline__ void mfma_process(MfmaState<D, NT>& st, MfmaChunk<D, 
                 uint32_t mask = 0;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (4 * w + e < valid) mask |= 0xFFu << (8 * e);
+                    if (4 * w + e < valid && 4 * w + e >= vlo) mask |= 0xFFu << (8 * e);
                 keep[w] = mask;
             }
 #pragma unroll
@@ -448,26 +467,28 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
     float* s_acc = s_l + W * CP;
 
     const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    const int L = a.seq_lens[b];
-    const int tok_begin = s * a.split_tokens;
+    const SeqRange sr = seq_range(a, b);
+    const int L = sr.L;
+    const int tok_begin = sr.base + s * a.split_tokens;
     if (tok_begin >= L) {
         if (L <= 0 && s == 0) write_empty(a, b, g, D);
         return;
     }
     const int tok_end = min(L, tok_begin + a.split_tokens);
-    const int S = (L + a.split_tokens - 1) / a.split_tokens;   // splits holding tokens
+    const int S = (L - sr.base + a.split_tokens - 1) / a.split_tokens;   // splits holding tokens
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n = lane & 15, grp = lane >> 4;
     const int G = a.G, GQ = G * a.q_len;
 
     const int lb0 = tok_begin / kBlockSize;
     const int n_chunks = (tok_end - tok_begin + kChunkTokens - 1) / kChunkTokens;
-    stage_block_ids(s_blk, a.block_tables + (int64_t)b * a.max_blocks, lb0, n_chunks * 4,
+    stage_block_ids(s_blk, a.block_tables + (int64_t)b * a.max_blocks, lb0, n_chunks * 4, sr.first / kBlockSize,
                     (L + kBlockSize - 1) / kBlockSize - 1);
 
-    // Causal ends: query i (token L - q_len + i) sees tokens < L - q_len + 1 + i.
+    // Query i (token L - q_len + i) sees tokens [cbeg, cend): cend = that
+    // token + 1, cbeg = cend - window (or 0).
     const int q0_end = L - a.q_len + 1;
-    int cend[NT];
+    int cbeg[NT], cend[NT];
     // Q^T operands per tile: k-step (j, hh) covers dims 64j + 16grp + 8hh .. +7
     // of column 16 nt + n (zero past GQ).  For NVFP4 the QK product runs in
     // f16: the column's q is scaled by a power of two 2^qs (max |q| lands in
@@ -482,6 +503,7 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
         const bool live = c < GQ;
         const int qi = live ? c / G : 0;
         cend[nt] = live ? min(tok_end, q0_end + qi) : tok_end;
+        cbeg[nt] = live && a.window > 0 ? max(0, q0_end + qi - a.window) : 0;
         const uint16_t* qrow = a.q + (live ? column_row(a, b, g, c) : 0) * D;
         u32x4 qw[2 * KJ];
 #pragma unroll
@@ -523,6 +545,7 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
         }
     }
     const int tail_from = min(tok_end, q0_end);
+    const int head_until = a.window > 0 ? max(0, L - a.window) : 0;   // the newest query's window start
     __syncthreads();
 
     MfmaState<D, NT> st;
@@ -548,11 +571,13 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
             for (int i = 0; i < my; i += 2) {
                 const int chb = i + 1 < my ? ch + W : ch;
                 mfma_load(Bc, a, s_blk, chb, g, n, grp);
-                mfma_process(st, A, qb, cs, cend, tok_begin + ch * kChunkTokens, tok_end, tail_from, grp);
+                mfma_process(st, A, qb, cs, cbeg, cend, tok_begin + ch * kChunkTokens, tok_end, tail_from,
+                             head_until, sr.first, grp);
                 if (i + 1 >= my) break;
                 const int cha = i + 2 < my ? chb + W : chb;
                 mfma_load(A, a, s_blk, cha, g, n, grp);
-                mfma_process(st, Bc, qb, cs, cend, tok_begin + chb * kChunkTokens, tok_end, tail_from, grp);
+                mfma_process(st, Bc, qb, cs, cbeg, cend, tok_begin + chb * kChunkTokens, tok_end, tail_from,
+                             head_until, sr.first, grp);
                 ch = cha;
             }
         }
@@ -561,7 +586,8 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
             const int ch = wave + i * W;
             MfmaChunk<D, FMT> A;
             mfma_load(A, a, s_blk, ch, g, n, grp);
-            mfma_process(st, A, qb, cs, cend, tok_begin + ch * kChunkTokens, tok_end, tail_from, grp);
+            mfma_process(st, A, qb, cs, cbeg, cend, tok_begin + ch * kChunkTokens, tok_end, tail_from,
+                         head_until, sr.first, grp);
         }
     }
 
@@ -622,7 +648,7 @@ __global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeArgs a) {
 
     const int lb0 = tok_begin / kBlockSize;
     const int n_blocks = (tok_end - tok_begin + kBlockSize - 1) / kBlockSize;
-    stage_block_ids(s_blk, a.block_tables + (int64_t)b * a.max_blocks, lb0, n_blocks,
+    stage_block_ids(s_blk, a.block_tables + (int64_t)b * a.max_blocks, lb0, n_blocks, 0,
                     (L + kBlockSize - 1) / kBlockSize - 1);
     for (int i = threadIdx.x; i < G * D; i += kThreads) {
         const int h = i / D, d = i - h * D;
@@ -808,8 +834,8 @@ __global__ void __launch_bounds__(kMergeThreads) merge_splits_kernel(DecodeArgs 
     __shared__ f32x4 part[P][C4];
     const int hq = blockIdx.x;                // output row (b * q_len + i) * Hq + h
     const int b = hq / (a.Hq * a.q_len);
-    const int L = a.seq_lens[b];
-    const int S = (L + a.split_tokens - 1) / a.split_tokens;
+    const SeqRange sr = seq_range(a, b);
+    const int S = (sr.L - sr.base + a.split_tokens - 1) / a.split_tokens;
     if (S <= 1) return;                       // written by the decode kernel
     const int t = threadIdx.x;
     const int d4 = t % C4, p = t / C4;

@@ -39,6 +39,7 @@ struct DecodeArgs {
     float v_scale;               // applied once in the merge
     int out_f32;
     int q_len;                   // queries per sequence (1: single-token decode)
+    int window;                  // > 0: each query sees its `window` newest tokens
 };
 
 // Workspace: [ml: B*Hq*S*2 f32][acc: B*Hq*S*D f32], the second region starting

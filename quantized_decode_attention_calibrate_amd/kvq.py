@@ -56,9 +56,10 @@ def _load() -> ctypes.CDLL:
         "kvq_nvfp4_paged_decode_attn_ex": (I, [P, P, P, P, I, P, I, I, I, I, I, I, I, F, F, F, P, I, P, SZ, P,
                                                I]),
         "kvq_e2m1_decode": (I, [P, ctypes.c_uint8, P, I64, P]),
-        "kvq_decode_workspace_bytes_mq": (SZ, [I, I, I, I, I, I, I, I]),
-        "kvq_paged_decode_attn_mq": (I, [P, I, P, P, I, P, I, P, I, I, I, I, I, I, I, F, F, F, P, I, P, SZ, P, I]),
-        "kvq_nvfp4_paged_decode_attn_mq": (I, [P, I, P, P, P, I, P, I, I, I, I, I, I, I, F, F, F, P, I, P, SZ,
+        "kvq_decode_workspace_bytes_mq": (SZ, [I, I, I, I, I, I, I, I, I]),
+        "kvq_paged_decode_attn_mq": (I, [P, I, I, P, P, I, P, I, P, I, I, I, I, I, I, I, F, F, F, P, I, P, SZ, P,
+                                         I]),
+        "kvq_nvfp4_paged_decode_attn_mq": (I, [P, I, I, P, P, P, I, P, I, I, I, I, I, I, I, F, F, F, P, I, P, SZ,
                                                P, I]),
     }
     for name, (res, args) in sig.items():
@@ -243,14 +244,14 @@ def kvq_paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
 # ---- multi-query decode -------------------------------------------------------
 
 def kvq_decode_workspace_bytes_mq(B: int, q_len: int, Hq: int, Hkv: int, D: int, max_seq_len: int,
-                                  split_tokens: int = 0) -> int:
-    return _lib.kvq_decode_workspace_bytes_mq(B, q_len, Hq, Hkv, D, max_seq_len, BLOCK_SIZE, split_tokens)
+                                  split_tokens: int = 0, window: int = 0) -> int:
+    return _lib.kvq_decode_workspace_bytes_mq(B, q_len, window, Hq, Hkv, D, max_seq_len, BLOCK_SIZE, split_tokens)
 
 
 def new_workspace_mq(B: int, q_len: int, Hq: int, Hkv: int, D: int, max_seq_len: int, split_tokens: int = 0,
-                     device="cuda"):
+                     device="cuda", window: int = 0):
     """Workspace for kvq_paged_decode_attn_mq / kvq_nvfp4_paged_decode_attn_mq."""
-    n = kvq_decode_workspace_bytes_mq(B, q_len, Hq, Hkv, D, max_seq_len, split_tokens)
+    n = kvq_decode_workspace_bytes_mq(B, q_len, Hq, Hkv, D, max_seq_len, split_tokens, window)
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
@@ -266,12 +267,12 @@ def _mq_args(q, block_tables, seq_lens, out):
 def kvq_paged_decode_attn_mq(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_dtype: int,
                              block_tables: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, Hkv: int,
                              k_scale: float, v_scale: float, sm_scale: float, out: torch.Tensor,
-                             workspace: torch.Tensor, split_tokens: int = 0, stream=None) -> None:
+                             workspace: torch.Tensor, split_tokens: int = 0, window: int = 0, stream=None) -> None:
     """q bf16 [B][q_len][Hq][D] (the q_len newest tokens, already in the cache);
-    out bf16 or fp32 [B][q_len][Hq][D]."""
+    out bf16 or fp32 [B][q_len][Hq][D]; window > 0: sliding-window attention."""
     B, q_len, Hq, D, out_dtype = _mq_args(q, block_tables, seq_lens, out)
     _check("kvq_paged_decode_attn_mq", _lib.kvq_paged_decode_attn_mq(
-        _ptr(q), q_len, _ptr(k_cache), _ptr(v_cache), kv_dtype, _ptr(block_tables), block_tables.shape[1],
+        _ptr(q), q_len, window, _ptr(k_cache), _ptr(v_cache), kv_dtype, _ptr(block_tables), block_tables.shape[1],
         _ptr(seq_lens), max_seq_len, B, Hq, Hkv, D, BLOCK_SIZE, k_cache.shape[0], k_scale, v_scale, sm_scale,
         _ptr(out), out_dtype, _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream),
         split_tokens))
@@ -280,11 +281,12 @@ def kvq_paged_decode_attn_mq(q: torch.Tensor, k_cache: torch.Tensor, v_cache: to
 def kvq_nvfp4_paged_decode_attn_mq(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                                    block_tables: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, Hkv: int,
                                    k_gscale: float, v_gscale: float, sm_scale: float, out: torch.Tensor,
-                                   workspace: torch.Tensor, split_tokens: int = 0, stream=None) -> None:
+                                   workspace: torch.Tensor, split_tokens: int = 0, window: int = 0,
+                                   stream=None) -> None:
     """NVFP4 caches; otherwise as kvq_paged_decode_attn_mq."""
     B, q_len, Hq, D, out_dtype = _mq_args(q, block_tables, seq_lens, out)
     _check("kvq_nvfp4_paged_decode_attn_mq", _lib.kvq_nvfp4_paged_decode_attn_mq(
-        _ptr(q), q_len, _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1],
+        _ptr(q), q_len, window, _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1],
         _ptr(seq_lens), max_seq_len, B, Hq, Hkv, D, BLOCK_SIZE, k_cache.shape[0], k_gscale, v_gscale, sm_scale,
         _ptr(out), out_dtype, _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream),
         split_tokens))

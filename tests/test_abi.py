@@ -151,7 +151,7 @@ def test_nvfp4_host_calls(K):
 
 
 def test_multiquery_host_validation(K):
-    ws = lambda B, ql, Hq, Hkv, D, L, sp=0: K.kvq_decode_workspace_bytes_mq(B, ql, Hq, Hkv, D, L, sp)
+    ws = lambda B, ql, Hq, Hkv, D, L, sp=0, W=0: K.kvq_decode_workspace_bytes_mq(B, ql, Hq, Hkv, D, L, sp, W)
     pad = lambda n: (n + 255) // 256 * 256
     # rows are (sequence, query, head); the split plan is the single-query one
     for B, ql, Hq, Hkv, D, L in [(1, 4, 64, 8, 64, 65536), (3, 2, 24, 4, 256, 5000), (2, 16, 2, 2, 64, 300)]:
@@ -160,9 +160,16 @@ def test_multiquery_host_validation(K):
         assert ws(B, ql, Hq, Hkv, D, L) == pad(B * ql * Hq * S * 8) + B * ql * Hq * S * D * 4
     assert ws(1, 1, 8, 2, 64, 100) == K.kvq_decode_workspace_bytes(1, 8, 2, 64, 100)
     assert ws(1, 0, 8, 2, 64, 100) == 0 and ws(1, 17, 8, 2, 64, 100) == 0
+    assert ws(1, 1, 8, 2, 64, 100, W=-1) == 0
+    # a window bounds the split plan by W + q_len - 1 + 63 tokens
+    for B, ql, W, L in [(1, 1, 128, 65536), (4, 3, 1000, 131072), (2, 2, 4096, 300)]:
+        span = min(L, W + ql - 1 + 63)
+        split = K.kvq_decode_plan_split_tokens(B, 8, span)
+        S = max(1, math.ceil(span / split))
+        assert ws(B, ql, 64, 8, 64, L, W=W) == pad(B * ql * 64 * S * 8) + B * ql * 64 * S * 64 * 4
 
-    def call(q_len, Hq=16, Hkv=2, D=64, nvfp4=False):
-        args = (FAKE, q_len, FAKE, FAKE) + (() if nvfp4 else (1,)) + (
+    def call(q_len, Hq=16, Hkv=2, D=64, nvfp4=False, window=0):
+        args = (FAKE, q_len, window, FAKE, FAKE) + (() if nvfp4 else (1,)) + (
             FAKE, 8, FAKE, 100, 1, Hq, Hkv, D, 16, 10, 1.0, 1.0, 0.125, FAKE, 0, FAKE, 1 << 30, None, 0)
         fn = K.lib().kvq_nvfp4_paged_decode_attn_mq if nvfp4 else K.lib().kvq_paged_decode_attn_mq
         return fn(*args)
@@ -171,3 +178,4 @@ def test_multiquery_host_validation(K):
     assert call(5, Hq=16, Hkv=2, D=128) == -2  # 40 > 32 at D 128
     assert call(3, Hq=12, Hkv=2, D=256) == -2  # 18 > 16 at D 256
     assert call(0, nvfp4=True) == -1 and call(9, nvfp4=True) == -2
+    assert call(1, window=-5) == -1 and call(2, nvfp4=True, window=-1) == -1

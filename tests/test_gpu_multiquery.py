@@ -42,33 +42,34 @@ def K():
     return kvq()
 
 
-def run_mq(K, s, q, kv, split_tokens, dtype=torch.float32):
+def run_mq(K, s, q, kv, split_tokens, dtype=torch.float32, window=0, bt=None):
     w = s.w
     B, q_len = q.shape[0], q.shape[1]
     out = torch.empty(B, q_len, w.Hq, w.D, dtype=dtype, device="cuda")
-    ws = K.new_workspace_mq(B, q_len, w.Hq, w.Hkv, w.D, w.max_seq_len, split_tokens)
+    ws = K.new_workspace_mq(B, q_len, w.Hq, w.Hkv, w.D, w.max_seq_len, split_tokens, window=window)
     sl = torch.tensor(w.seq_lens, dtype=torch.int32, device="cuda")
+    bt = (w.block_tables if bt is None else bt).cuda()
     if kv == 2:
-        K.kvq_nvfp4_paged_decode_attn_mq(q.cuda(), s.kc, s.vc, w.block_tables.cuda(), sl, w.max_seq_len, w.Hkv,
-                                         s.gk, s.gv, s.sm, out, ws, split_tokens=split_tokens)
+        K.kvq_nvfp4_paged_decode_attn_mq(q.cuda(), s.kc, s.vc, bt, sl, w.max_seq_len, w.Hkv, s.gk, s.gv, s.sm,
+                                         out, ws, split_tokens=split_tokens, window=window)
     else:
-        K.kvq_paged_decode_attn_mq(q.cuda(), s.kc, s.vc, kv, s.bt, s.sl, w.max_seq_len, w.Hkv, s.ks, s.vs,
-                                   s.sm_scale, out, ws, split_tokens=split_tokens)
+        K.kvq_paged_decode_attn_mq(q.cuda(), s.kc, s.vc, kv, bt, s.sl, w.max_seq_len, w.Hkv, s.ks, s.vs,
+                                   s.sm_scale, out, ws, split_tokens=split_tokens, window=window)
     torch.cuda.synchronize()
     return out
 
 
-def oracle_mq(s, q, kv):
+def oracle_mq(s, q, kv, window=0):
     w = s.w
     if kv == 2:
         okc, ovc = oracle.new_caches(oracle.KV_NVFP4, w.num_blocks, w.Hkv, w.D, 16, fill=0xFF)
         oracle.nvfp4_cache_write(w.k, w.v, w.slot_mapping, okc, ovc, 16, s.gk, s.gv)
         return oracle.decode_attn_mq(q, okc, ovc, oracle.KV_NVFP4, w.block_tables, w.seq_lens, w.Hkv, 16,
-                                     s.gk, s.gv, s.sm, nthreads=8)
+                                     s.gk, s.gv, s.sm, nthreads=8, window=window)
     kc, vc = s.oracle_caches()
     kvd = oracle.KV_FP8 if kv == 1 else oracle.KV_BF16
     return oracle.decode_attn_mq(q, kc, vc, kvd, w.block_tables, w.seq_lens, w.Hkv, 16, s.ks, s.vs, s.sm_scale,
-                                 nthreads=8)
+                                 nthreads=8, window=window)
 
 
 def setup(K, w, kv):
