@@ -146,7 +146,7 @@ hipError_t launch_e4m3_decode(const uint8_t* codes, void* out, int kind, int64_t
 // 16-byte loads of 8 bf16 of K and of V; K codes go straight to their
 // token-major row [blk][g][off][D]; V codes go to an LDS tile [D][16].
 // Phase 2, lane order (dim, token) with the token fastest: V elements leave
-// the tile one per lane to [blk][g][D][bs], so lanes holding consecutive
+// the tile one per lane to [blk][g][D][16], so lanes holding consecutive
 // slots write consecutive bytes of one cache row and their stores coalesce,
 // whatever the slot mapping.  The quantize step is an IEEE fp32 division (the
 // scale multiplies code values), so this translation unit must not be built
@@ -158,28 +158,31 @@ template <bool FP8>
 __global__ void __launch_bounds__(kWriteThreads) cache_write_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t src_stride,
     const int64_t* __restrict__ slot_mapping, int T, int Hkv, int D, uint8_t* __restrict__ k_cache,
-    uint8_t* __restrict__ v_cache, int bs, float k_scale, float v_scale) {
+    uint8_t* __restrict__ v_cache, float k_scale, float v_scale) {
     using Elem = typename std::conditional<FP8, uint8_t, uint16_t>::type;
     extern __shared__ uint32_t lds_w[];
     Elem* vt = reinterpret_cast<Elem*>(lds_w);   // [D][16] V elements of the window
     __shared__ int64_t s_slot[kWriteTokens];
     const int t0 = blockIdx.x * kWriteTokens, g = blockIdx.y;
-    if (threadIdx.x < kWriteTokens) {
-        const int t = t0 + threadIdx.x;
-        s_slot[threadIdx.x] = t < T ? slot_mapping[t] : -1;
-    }
-    __syncthreads();
     const int chunks = D >> 3;
+    // each lane reads its token's slot itself, alongside the K/V loads (the
+    // source address does not depend on it), so phase 1 is one round trip
     for (int i = threadIdx.x; i < kWriteTokens * chunks; i += kWriteThreads) {
         const int tw = i / chunks, c = i - tw * chunks, d0 = c << 3;
-        const int64_t slot = s_slot[tw];
-        if (slot < 0) continue;
-        const int64_t blk = slot / bs;
-        const int off = (int)(slot - blk * bs);
-        const int64_t src = (int64_t)(t0 + tw) * src_stride + (int64_t)g * D + d0;
+        const int t = t0 + tw;
+        if (t >= T) {
+            if (c == 0) s_slot[tw] = -1;
+            continue;
+        }
+        const int64_t src = (int64_t)t * src_stride + (int64_t)g * D + d0;
+        const int64_t slot = slot_mapping[t];
         const u32x4 kw = *reinterpret_cast<const u32x4*>(k + src);
         const u32x4 vw = *reinterpret_cast<const u32x4*>(v + src);
-        const int64_t kdst = ((blk * Hkv + g) * bs + off) * D + d0;   // [blk][g][off][d]
+        if (c == 0) s_slot[tw] = slot;
+        if (slot < 0) continue;
+        const int64_t blk = slot / kBlockSize;   // block_size is validated to be kBlockSize
+        const int off = (int)(slot - blk * kBlockSize);
+        const int64_t kdst = ((blk * Hkv + g) * kBlockSize + off) * D + d0;   // [blk][g][off][d]
         if constexpr (FP8) {
 #pragma clang fp contract(off)
             float kf[8], vf[8];
@@ -211,25 +214,26 @@ __global__ void __launch_bounds__(kWriteThreads) cache_write_kernel(
         const int d = i / kWriteTokens, tw = i - d * kWriteTokens;
         const int64_t slot = s_slot[tw];
         if (slot < 0) continue;
-        const int64_t blk = slot / bs;
-        const int off = (int)(slot - blk * bs);
-        vc[((blk * Hkv + g) * (int64_t)D + d) * bs + off] = vt[d * kWriteTokens + tw];   // [blk][g][d][off]
+        const int64_t blk = slot / kBlockSize;   // block_size is validated to be kBlockSize
+        const int off = (int)(slot - blk * kBlockSize);
+        vc[((blk * Hkv + g) * (int64_t)D + d) * kBlockSize + off] = vt[d * kWriteTokens + tw];   // [blk][g][d][off]
     }
 }
 
 hipError_t launch_cache_write(const void* k, const void* v, int64_t src_stride, const int64_t* slots, int T,
                               int Hkv, int D, void* k_cache, void* v_cache, int bs, int kv_dtype,
                               float k_scale, float v_scale, hipStream_t st) {
+    (void)bs;   // validated to be kBlockSize
     const dim3 grid((unsigned)((T + kWriteTokens - 1) / kWriteTokens), (unsigned)Hkv);
     const size_t lds = (size_t)kWriteTokens * D * (kv_dtype == 1 ? 1 : 2);
     if (kv_dtype == 1)
         hipLaunchKernelGGL(cache_write_kernel<true>, grid, dim3(kWriteThreads), lds, st, (const uint16_t*)k,
                            (const uint16_t*)v, src_stride, slots, T, Hkv, D, (uint8_t*)k_cache,
-                           (uint8_t*)v_cache, bs, k_scale, v_scale);
+                           (uint8_t*)v_cache, k_scale, v_scale);
     else
         hipLaunchKernelGGL(cache_write_kernel<false>, grid, dim3(kWriteThreads), lds, st, (const uint16_t*)k,
                            (const uint16_t*)v, src_stride, slots, T, Hkv, D, (uint8_t*)k_cache,
-                           (uint8_t*)v_cache, bs, k_scale, v_scale);
+                           (uint8_t*)v_cache, k_scale, v_scale);
     return hipGetLastError();
 }
 
@@ -248,11 +252,9 @@ hipError_t launch_cache_write(const void* k, const void* v, int64_t src_stride, 
 // lane of the even slot stores the whole byte when the odd slot's token is in
 // the same window (the usual case for a prefill); a nibble whose partner is
 // not is merged into its 32-bit word with atomicAnd / atomicOr on its own bits.
-__device__ __forceinline__ void nvfp4_quantize_group(const uint16_t* src, float gscale, uint32_t* codes,
-                                                     uint32_t* bcode) {
+__device__ __forceinline__ void nvfp4_quantize_group(const u32x4& w0, const u32x4& w1, float gscale,
+                                                     uint32_t* codes, uint32_t* bcode) {
 #pragma clang fp contract(off)
-    const u32x4 w0 = *reinterpret_cast<const u32x4*>(src);
-    const u32x4 w1 = *reinterpret_cast<const u32x4*>(src + 8);
     float xf[16];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -285,30 +287,35 @@ __global__ void __launch_bounds__(kWriteThreads) nvfp4_cache_write_kernel(
     uint8_t* vt = reinterpret_cast<uint8_t*>(lds_w);   // [D][16] V codes of the window, one per byte
     __shared__ int64_t s_slot[kWriteTokens];
     const int t0 = blockIdx.x * kWriteTokens, g = blockIdx.y;
-    if (threadIdx.x < kWriteTokens) {
-        const int t = t0 + threadIdx.x;
-        s_slot[threadIdx.x] = t < T ? slot_mapping[t] : -1;
-    }
-    __syncthreads();
     const int groups = D >> 4;
     const int64_t region = (int64_t)kBlockSize * D / 2 + (int64_t)kBlockSize * D / 16;
     const int64_t codes_bytes = (int64_t)kBlockSize * D / 2;
     for (int i = threadIdx.x; i < kWriteTokens * groups; i += kWriteThreads) {
         const int grp = i / kWriteTokens, tw = i - grp * kWriteTokens;
-        const int64_t slot = s_slot[tw];
+        const int t = t0 + tw;
+        if (t >= T) {
+            if (grp == 0) s_slot[tw] = -1;
+            continue;
+        }
+        // the lane reads its token's slot itself, alongside the K/V loads (the
+        // source address does not depend on it): one round trip
+        const int64_t src = (int64_t)t * src_stride + (int64_t)g * D + grp * 16;
+        const int64_t slot = slot_mapping[t];
+        const u32x4 k0 = *reinterpret_cast<const u32x4*>(k + src), k1 = *reinterpret_cast<const u32x4*>(k + src + 8);
+        const u32x4 v0 = *reinterpret_cast<const u32x4*>(v + src), v1 = *reinterpret_cast<const u32x4*>(v + src + 8);
+        if (grp == 0) s_slot[tw] = slot;
         if (slot < 0) continue;
         const int64_t blk = slot / kBlockSize;
         const int off = (int)(slot - blk * kBlockSize);
-        const int64_t src = (int64_t)(t0 + tw) * src_stride + (int64_t)g * D + grp * 16;
         uint32_t codes[16], bcode;
-        nvfp4_quantize_group(k + src, k_gscale, codes, &bcode);
+        nvfp4_quantize_group(k0, k1, k_gscale, codes, &bcode);
         uint8_t* kr = k_cache + (blk * Hkv + g) * region;
         u32x2 packed = {0u, 0u};
 #pragma unroll
         for (int j = 0; j < 16; ++j) packed[j >> 3] |= codes[j] << (4 * (j & 7));
         *reinterpret_cast<u32x2*>(kr + (int64_t)off * (D / 2) + grp * 8) = packed;
         kr[codes_bytes + (int64_t)off * groups + grp] = (uint8_t)bcode;
-        nvfp4_quantize_group(v + src, v_gscale, codes, &bcode);
+        nvfp4_quantize_group(v0, v1, v_gscale, codes, &bcode);
         v_cache[(blk * Hkv + g) * region + codes_bytes + (int64_t)grp * kBlockSize + off] = (uint8_t)bcode;
 #pragma unroll
         for (int j = 0; j < 16; ++j) vt[(grp * 16 + j) * kWriteTokens + tw] = (uint8_t)codes[j];
