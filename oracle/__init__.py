@@ -62,6 +62,9 @@ def lib() -> ctypes.CDLL:
             "kvqo_nvfp4_v_value": (D, [P, I64, I, I, I, I, I, F]),
             "kvqo_decode_attn": (None, [P, P, P, I, P, I, P, I, I, I, I, I, F, F, F, P, I]),
             "kvqo_decode_attn_units": (None, [P, P, P, I, P, I, P, I, I, I, I, I, F, F, F, P, I, P, I]),
+            "kvqo_block_bytes": (ctypes.c_size_t, [I, I, I, I]),
+            "kvqo_gather_blocks": (None, [P, ctypes.c_size_t, P, I, P]),
+            "kvqo_scatter_blocks": (None, [P, ctypes.c_size_t, P, I, P]),
             "kvqo_decode_attn_mq": (None, [P, I, I, P, P, I, P, I, P, I, I, I, I, I, F, F, F, P, I]),
             "kvqo_fp8_cos_sim": (D, [P, I64, F]),
         }
@@ -249,3 +252,27 @@ def decode_attn_mq(q, k_cache: np.ndarray, v_cache: np.ndarray, kv_dtype: int, b
 def fp8_cos_sim(x, scale: float) -> float:
     b = _bits16(x).reshape(-1)
     return lib().kvqo_fp8_cos_sim(_ptr(b), b.size, scale)
+
+
+# ---- block copies for a host-memory tier ---------------------------------------
+
+def block_bytes(kv_dtype: int, Hkv: int, D: int, block_size: int = 16) -> int:
+    return lib().kvqo_block_bytes(kv_dtype, Hkv, D, block_size)
+
+
+def gather_blocks(cache: np.ndarray, ids, block_bytes_: int) -> np.ndarray:
+    """Blocks ids[i] of a cache (any dtype, blocks of block_bytes_ bytes) as [n][block_bytes_] uint8."""
+    c = np.ascontiguousarray(cache).view(np.uint8).reshape(-1)
+    i = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
+    out = np.zeros((i.size, block_bytes_), dtype=np.uint8)
+    lib().kvqo_gather_blocks(_ptr(c), block_bytes_, _ptr(i), i.size, _ptr(out))
+    return out
+
+
+def scatter_blocks(src: np.ndarray, ids, block_bytes_: int, cache: np.ndarray) -> None:
+    """Writes src[i] (uint8 [n][block_bytes_]) to block ids[i] of cache, in place."""
+    assert cache.flags["C_CONTIGUOUS"]
+    c = cache.view(np.uint8).reshape(-1)   # a view: writes land in cache
+    i = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
+    s = np.ascontiguousarray(src, dtype=np.uint8)
+    lib().kvqo_scatter_blocks(_ptr(s), block_bytes_, _ptr(i), i.size, _ptr(c))

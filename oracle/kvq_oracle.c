@@ -416,3 +416,26 @@ double kvqo_fp8_cos_sim(const uint16_t* x, int64_t n, float scale) {
     }
     return xy / sqrt(xx * yy);
 }
+
+/* ------------------------------------------------------------------------ */
+/* block copies for a host-memory tier                                        */
+/* ------------------------------------------------------------------------ */
+
+size_t kvqo_block_bytes(int kv_dtype, int Hkv, int D, int block_size) {
+    size_t per_head;
+    if (kv_dtype == 2)
+        per_head = (size_t)block_size * D / 2 + (size_t)block_size * D / 16;
+    else
+        per_head = (size_t)block_size * D * (kv_dtype == 0 ? 2 : 1);
+    return (size_t)Hkv * per_head;
+}
+
+void kvqo_gather_blocks(const uint8_t* cache, size_t block_bytes, const int32_t* ids, int n, uint8_t* dst) {
+    for (int i = 0; i < n; ++i)
+        memcpy(dst + (size_t)i * block_bytes, cache + (size_t)ids[i] * block_bytes, block_bytes);
+}
+
+void kvqo_scatter_blocks(const uint8_t* src, size_t block_bytes, const int32_t* ids, int n, uint8_t* cache) {
+    for (int i = 0; i < n; ++i)
+        memcpy(cache + (size_t)ids[i] * block_bytes, src + (size_t)i * block_bytes, block_bytes);
+}

@@ -32,6 +32,7 @@
 #ifndef KVQ_ORACLE_H
 #define KVQ_ORACLE_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -169,6 +170,18 @@ void kvqo_decode_attn_units(const uint16_t* q, const void* k_cache, const void* 
 /* Reconstruction cosine similarity of n bf16 values against their FP8
  * round trip value(E4M3(x / scale)) * scale, in fp64. */
 double kvqo_fp8_cos_sim(const uint16_t* x, int64_t n, float scale);
+
+/* ---- block copies for a host-memory KV tier ------------------------------
+ * The Radiance FP8 guide's operator notes count FP8 blocks as half the BF16
+ * bytes for host offload, and the dual-R9700 page runs a 10 GiB CPU KV tier.
+ * A physical block of a K (or V) cache is one contiguous run of
+ * kvqo_block_bytes bytes (all heads): Hkv * bs * D * 2 (BF16), * 1 (FP8),
+ * Hkv * (bs * D / 2 + bs * D / 16) (NVFP4). */
+size_t kvqo_block_bytes(int kv_dtype, int Hkv, int D, int block_size);
+/* dst[i] = block ids[i] of cache, i < n (blocks of block_bytes bytes). */
+void kvqo_gather_blocks(const uint8_t* cache, size_t block_bytes, const int32_t* ids, int n, uint8_t* dst);
+/* block ids[i] of cache = src[i]. */
+void kvqo_scatter_blocks(const uint8_t* src, size_t block_bytes, const int32_t* ids, int n, uint8_t* cache);
 
 #ifdef __cplusplus
 }
