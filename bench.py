@@ -185,6 +185,46 @@ def measure_prefill_write(torch, K, name, reps=5):
     return rec
 
 
+def measure_offload(torch, K, name, reps=5):
+    """Offload of one layer's whole cache (every block of every sequence, K then
+    V) to pinned host memory and its restore, per format: the host tier moves
+    kvq_cache_block_bytes per block, so FP8 halves and NVFP4 cuts to 0.28 x
+    the BF16 bytes."""
+    from quantized_decode_attention_calibrate_amd import workloads
+    w = workloads.make(name, device="cpu", seed=0)
+    ids = torch.cat([w.block_tables[b, :(L + 15) // 16] for b, L in enumerate(w.seq_lens)]).to(torch.int32)
+    ids = ids.cuda()
+    n = ids.numel()
+    rec = {"blocks": n}
+    st = torch.cuda.current_stream()
+    for tag, fmt in (("bf16", K.KVQ_KV_BF16), ("fp8", K.KVQ_KV_FP8_E4M3), ("nvfp4", K.KVQ_FORMAT_NVFP4)):
+        bb = K.kvq_cache_block_bytes(fmt, w.Hkv, w.D)
+        if fmt == K.KVQ_FORMAT_NVFP4:
+            kc, vc = K.new_nvfp4_caches(w.num_blocks, w.Hkv, w.D, device="cuda")
+        else:
+            kc, vc = K.new_caches(fmt, w.num_blocks, w.Hkv, w.D, device="cuda")
+        staging = torch.empty(2 * n * bb, dtype=torch.uint8, device="cuda")
+        host = torch.empty(2 * n * bb, dtype=torch.uint8, pin_memory=True)
+        times = {}
+        for what, fn in (("offload", lambda: K.kvq_offload_blocks(kc, vc, bb, ids, staging, host)),
+                         ("restore", lambda: K.kvq_restore_blocks(host, staging, bb, ids, kc, vc))):
+            fn()
+            torch.cuda.synchronize()
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(st)
+            for _ in range(reps):
+                fn()
+            a1.record(st)
+            torch.cuda.synchronize()
+            times[what] = a0.elapsed_time(a1) / reps * 1e3
+        rec[tag] = {"block_bytes": bb, "host_bytes": 2 * n * bb, "offload_us": round(times["offload"], 1),
+                    "restore_us": round(times["restore"], 1),
+                    "offload_gbps": round(2 * n * bb / (times["offload"] * 1e-6) / 1e9, 1)}
+        del kc, vc, staging, host
+    torch.cuda.empty_cache()
+    return rec
+
+
 def measure_multiquery(torch, K, name, q_lens, steps, warmup):
     """Multi-query decode (speculative-decoding verification) on one
     workload's FP8 caches: the q_len newest tokens attend at once.  Reports
@@ -466,6 +506,8 @@ def main():
             result["workloads"][name] = measure_workload(torch, K, name, 60, 10, with_nvfp4=name == "nvfp4_131k")
         print("[bench] prefill cache writes", file=sys.stderr, flush=True)
         result["prefill_write"] = {n: measure_prefill_write(torch, K, n) for n in ("nvfp4_131k", "mixed64")}
+        print("[bench] host-tier offload", file=sys.stderr, flush=True)
+        result["offload"] = measure_offload(torch, K, "gptoss65k")
         print("[bench] multi-query decode", file=sys.stderr, flush=True)
         result["multiquery"] = measure_multiquery(torch, K, "gptoss65k", (2, 4, 8), 200, 20)
     if not args.no_cpu_baseline:

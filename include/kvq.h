@@ -282,6 +282,34 @@ int kvq_nvfp4_paged_decode_attn_mq(const void* q_dev, int q_len, int window, con
                                    void* workspace_dev, size_t workspace_bytes, void* hip_stream,
                                    int split_tokens);
 
+/* ---- block copies for a host-memory KV tier --------------------------------
+ * The Radiance FP8 guide's operator notes account offloaded KV by block bytes
+ * (FP8 blocks are half the BF16 bytes) and the dual-R9700 page runs a 10 GiB
+ * CPU KV tier.  A physical block of a K or V cache written by this library is
+ * one contiguous run of kvq_cache_block_bytes bytes (all KV heads), so a tier
+ * moves whole blocks by id.
+ *   kv_format          KVQ_KV_BF16, KVQ_KV_FP8_E4M3, or 2 for NVFP4
+ *   block_ids_dev      int32 [n] physical block ids (< the cache's num_blocks:
+ *                      a device-side contract like the block tables)
+ * kvq_gather_blocks: dst[i] = block ids[i] (dst: n * block_bytes device
+ * bytes); kvq_scatter_blocks: block ids[i] = src[i].
+ * kvq_offload_blocks: K blocks then V blocks of the listed ids, gathered into
+ * staging_dev (2 * n * block_bytes device bytes, 16-B aligned, owned by the
+ * caller) and copied with one hipMemcpyAsync to host_dst (2 * n * block_bytes,
+ * pinned host memory for an asynchronous copy); kvq_restore_blocks is the
+ * reverse into the listed (possibly different) block ids.  block_bytes must
+ * be a positive multiple of 16; n = 0 does nothing.  All calls are
+ * asynchronous on hip_stream; host_dst is complete when the stream is. */
+size_t kvq_cache_block_bytes(int kv_format, int Hkv, int D, int block_size);
+int kvq_gather_blocks(const void* cache_dev, size_t block_bytes, const int32_t* block_ids_dev, int n,
+                      void* dst_dev, void* hip_stream);
+int kvq_scatter_blocks(const void* src_dev, size_t block_bytes, const int32_t* block_ids_dev, int n,
+                       void* cache_dev, void* hip_stream);
+int kvq_offload_blocks(const void* k_cache_dev, const void* v_cache_dev, size_t block_bytes,
+                       const int32_t* block_ids_dev, int n, void* staging_dev, void* host_dst, void* hip_stream);
+int kvq_restore_blocks(const void* host_src, void* staging_dev, size_t block_bytes, const int32_t* block_ids_dev,
+                       int n, void* k_cache_dev, void* v_cache_dev, void* hip_stream);
+
 /* E2M1 codec utility: byte i of codes_dev holds two codes (low nibble first);
  * out_dev[2i], out_dev[2i+1] = value(code) * value(scale_code) as f16, where
  * scale_code is an E4M3 block-scale code -- computed exactly as the NVFP4

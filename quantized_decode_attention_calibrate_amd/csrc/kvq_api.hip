@@ -330,6 +330,64 @@ int kvq_nvfp4_paged_decode_attn_mq(const void* q_dev, int q_len, int window, con
                          split_tokens);
 }
 
+size_t kvq_cache_block_bytes(int kv_format, int Hkv, int D, int block_size) {
+    if (Hkv <= 0 || !supported_d(D) || block_size != kBlockSize) return 0;
+    if (kv_format == 2) return (size_t)Hkv * (size_t)(kBlockSize * D / 2 + kBlockSize * D / 16);
+    if (kv_format == KVQ_KV_BF16) return (size_t)Hkv * kBlockSize * D * 2;
+    if (kv_format == KVQ_KV_FP8_E4M3) return (size_t)Hkv * kBlockSize * D;
+    return 0;
+}
+
+static int block_copy_args(const void* a, const void* b, size_t block_bytes, const int32_t* ids, int n) {
+    if (n < 0 || block_bytes == 0 || block_bytes % 16 != 0) return KVQ_EINVAL;
+    if (n == 0) return KVQ_OK;
+    if (!a || !b || !ids || !aligned16(a) || !aligned16(b)) return KVQ_EINVAL;
+    return 1;
+}
+
+int kvq_gather_blocks(const void* cache_dev, size_t block_bytes, const int32_t* block_ids_dev, int n, void* dst_dev,
+                      void* hip_stream) {
+    const int v = block_copy_args(cache_dev, dst_dev, block_bytes, block_ids_dev, n);
+    if (v != 1) return v;
+    return hip_status(launch_block_copy(cache_dev, dst_dev, block_ids_dev, n, block_bytes, 1, (hipStream_t)hip_stream));
+}
+
+int kvq_scatter_blocks(const void* src_dev, size_t block_bytes, const int32_t* block_ids_dev, int n, void* cache_dev,
+                       void* hip_stream) {
+    const int v = block_copy_args(src_dev, cache_dev, block_bytes, block_ids_dev, n);
+    if (v != 1) return v;
+    return hip_status(launch_block_copy(src_dev, cache_dev, block_ids_dev, n, block_bytes, 0, (hipStream_t)hip_stream));
+}
+
+int kvq_offload_blocks(const void* k_cache_dev, const void* v_cache_dev, size_t block_bytes,
+                       const int32_t* block_ids_dev, int n, void* staging_dev, void* host_dst, void* hip_stream) {
+    int v = block_copy_args(k_cache_dev, v_cache_dev, block_bytes, block_ids_dev, n);
+    if (v != 1) return v;
+    if (!staging_dev || !host_dst || !aligned16(staging_dev)) return KVQ_EINVAL;
+    const hipStream_t st = (hipStream_t)hip_stream;
+    const size_t half = (size_t)n * block_bytes;
+    v = hip_status(launch_block_copy(k_cache_dev, staging_dev, block_ids_dev, n, block_bytes, 1, st));
+    if (v != KVQ_OK) return v;
+    v = hip_status(launch_block_copy(v_cache_dev, (char*)staging_dev + half, block_ids_dev, n, block_bytes, 1, st));
+    if (v != KVQ_OK) return v;
+    return hip_status(hipMemcpyAsync(host_dst, staging_dev, 2 * half, hipMemcpyDeviceToHost, st));
+}
+
+int kvq_restore_blocks(const void* host_src, void* staging_dev, size_t block_bytes, const int32_t* block_ids_dev,
+                       int n, void* k_cache_dev, void* v_cache_dev, void* hip_stream) {
+    int v = block_copy_args(k_cache_dev, v_cache_dev, block_bytes, block_ids_dev, n);
+    if (v != 1) return v;
+    if (!staging_dev || !host_src || !aligned16(staging_dev)) return KVQ_EINVAL;
+    const hipStream_t st = (hipStream_t)hip_stream;
+    const size_t half = (size_t)n * block_bytes;
+    v = hip_status(hipMemcpyAsync(staging_dev, host_src, 2 * half, hipMemcpyHostToDevice, st));
+    if (v != KVQ_OK) return v;
+    v = hip_status(launch_block_copy(staging_dev, k_cache_dev, block_ids_dev, n, block_bytes, 0, st));
+    if (v != KVQ_OK) return v;
+    return hip_status(launch_block_copy((const char*)staging_dev + half, v_cache_dev, block_ids_dev, n, block_bytes, 0,
+                                        st));
+}
+
 int kvq_paged_decode_attn(const void* q_dev, const void* k_cache_dev, const void* v_cache_dev, int kv_dtype,
                           const int32_t* block_tables_dev, int max_blocks_per_seq, const int32_t* seq_lens_dev,
                           int max_seq_len, int B, int Hq, int Hkv, int D, int block_size, int num_blocks,

@@ -354,6 +354,30 @@ hipError_t launch_nvfp4_cache_write(const void* k, const void* v, int64_t src_st
     return hipGetLastError();
 }
 
+// ---- block copies for a host-memory tier ---------------------------------------
+// A physical block of a K or V cache is one contiguous run of block_bytes
+// (all heads).  One work-group per listed block (grid-stride over blocks),
+// 16-byte words: gather copies block ids[i] to row i of a dense buffer,
+// scatter copies row i back to block ids[i].
+__global__ void __launch_bounds__(256) block_copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                         const int32_t* __restrict__ ids, int n,
+                                                         int64_t words, int gather) {
+    for (int i = blockIdx.x; i < n; i += gridDim.x) {
+        const int64_t blk = ids[i];
+        const u32x4* s = src + (gather ? blk : (int64_t)i) * words;
+        u32x4* d = dst + (gather ? (int64_t)i : blk) * words;
+        for (int64_t w = threadIdx.x; w < words; w += blockDim.x) d[w] = s[w];
+    }
+}
+
+hipError_t launch_block_copy(const void* src, void* dst, const int32_t* ids, int n, size_t block_bytes, int gather,
+                             hipStream_t st) {
+    const unsigned grid = (unsigned)(n < 65536 ? n : 65536);
+    hipLaunchKernelGGL(block_copy_kernel, dim3(grid), dim3(256), 0, st, (const u32x4*)src, (u32x4*)dst, ids, n,
+                       (int64_t)(block_bytes / 16), gather);
+    return hipGetLastError();
+}
+
 // ---- E2M1 decode utility: out[2i], out[2i+1] = the two codes of byte i times
 // the E4M3 value of scale_code, computed as the NVFP4 decode kernel does (f16).
 __global__ void __launch_bounds__(256) e2m1_decode_kernel(const uint8_t* __restrict__ codes, uint32_t scale_code,

@@ -58,6 +58,8 @@ hipError_t launch_cache_write(const void* k, const void* v, int64_t src_stride, 
 hipError_t launch_nvfp4_cache_write(const void* k, const void* v, int64_t src_stride, const int64_t* slots, int T,
                                     int Hkv, int D, void* k_cache, void* v_cache, float k_gscale, float v_gscale,
                                     hipStream_t st);
+hipError_t launch_block_copy(const void* src, void* dst, const int32_t* ids, int n, size_t block_bytes, int gather,
+                             hipStream_t st);
 hipError_t launch_e2m1_decode(const uint8_t* codes, uint32_t scale_code, void* out, int64_t n, hipStream_t st);
 // Column tiles of 16 (query, head) pairs the MFMA kernel uses for G * q_len
 // columns at head dim D; 0 if the shape is not supported.

@@ -56,6 +56,11 @@ def _load() -> ctypes.CDLL:
         "kvq_nvfp4_paged_decode_attn_ex": (I, [P, P, P, P, I, P, I, I, I, I, I, I, I, F, F, F, P, I, P, SZ, P,
                                                I]),
         "kvq_e2m1_decode": (I, [P, ctypes.c_uint8, P, I64, P]),
+        "kvq_cache_block_bytes": (SZ, [I, I, I, I]),
+        "kvq_gather_blocks": (I, [P, SZ, P, I, P, P]),
+        "kvq_scatter_blocks": (I, [P, SZ, P, I, P, P]),
+        "kvq_offload_blocks": (I, [P, P, SZ, P, I, P, P, P]),
+        "kvq_restore_blocks": (I, [P, P, SZ, P, I, P, P, P]),
         "kvq_decode_workspace_bytes_mq": (SZ, [I, I, I, I, I, I, I, I, I]),
         "kvq_paged_decode_attn_mq": (I, [P, I, I, P, P, I, P, I, P, I, I, I, I, I, I, I, F, F, F, P, I, P, SZ, P,
                                          I]),
@@ -290,3 +295,49 @@ def kvq_nvfp4_paged_decode_attn_mq(q: torch.Tensor, k_cache: torch.Tensor, v_cac
         _ptr(seq_lens), max_seq_len, B, Hq, Hkv, D, BLOCK_SIZE, k_cache.shape[0], k_gscale, v_gscale, sm_scale,
         _ptr(out), out_dtype, _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream),
         split_tokens))
+
+
+# ---- block copies for a host-memory KV tier ----------------------------------------
+
+KVQ_FORMAT_NVFP4 = 2
+
+
+def kvq_cache_block_bytes(kv_format: int, Hkv: int, D: int) -> int:
+    return _lib.kvq_cache_block_bytes(kv_format, Hkv, D, BLOCK_SIZE)
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
+def kvq_gather_blocks(cache: torch.Tensor, block_bytes: int, ids: torch.Tensor, dst: torch.Tensor, stream=None):
+    assert ids.dtype == torch.int32 and ids.is_contiguous() and _nbytes(dst) >= ids.numel() * block_bytes
+    _check("kvq_gather_blocks", _lib.kvq_gather_blocks(_ptr(cache), block_bytes, _ptr(ids), ids.numel(), _ptr(dst),
+                                                       _stream(stream)))
+
+
+def kvq_scatter_blocks(src: torch.Tensor, block_bytes: int, ids: torch.Tensor, cache: torch.Tensor, stream=None):
+    assert ids.dtype == torch.int32 and ids.is_contiguous() and _nbytes(src) >= ids.numel() * block_bytes
+    _check("kvq_scatter_blocks", _lib.kvq_scatter_blocks(_ptr(src), block_bytes, _ptr(ids), ids.numel(),
+                                                         _ptr(cache), _stream(stream)))
+
+
+def kvq_offload_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_bytes: int, ids: torch.Tensor,
+                       staging: torch.Tensor, host_dst: torch.Tensor, stream=None):
+    """K blocks then V blocks of `ids` into host_dst (pinned, >= 2 * n * block_bytes bytes)."""
+    n = ids.numel()
+    assert ids.dtype == torch.int32 and ids.is_contiguous()
+    assert _nbytes(staging) >= 2 * n * block_bytes and _nbytes(host_dst) >= 2 * n * block_bytes
+    assert host_dst.device.type == "cpu" and host_dst.is_contiguous()
+    _check("kvq_offload_blocks", _lib.kvq_offload_blocks(_ptr(k_cache), _ptr(v_cache), block_bytes, _ptr(ids), n,
+                                                         _ptr(staging), _ptr(host_dst), _stream(stream)))
+
+
+def kvq_restore_blocks(host_src: torch.Tensor, staging: torch.Tensor, block_bytes: int, ids: torch.Tensor,
+                       k_cache: torch.Tensor, v_cache: torch.Tensor, stream=None):
+    n = ids.numel()
+    assert ids.dtype == torch.int32 and ids.is_contiguous()
+    assert _nbytes(staging) >= 2 * n * block_bytes and _nbytes(host_src) >= 2 * n * block_bytes
+    assert host_src.device.type == "cpu" and host_src.is_contiguous()
+    _check("kvq_restore_blocks", _lib.kvq_restore_blocks(_ptr(host_src), _ptr(staging), block_bytes, _ptr(ids), n,
+                                                         _ptr(k_cache), _ptr(v_cache), _stream(stream)))

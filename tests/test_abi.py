@@ -179,3 +179,18 @@ def test_multiquery_host_validation(K):
     assert call(3, Hq=12, Hkv=2, D=256) == -2  # 18 > 16 at D 256
     assert call(0, nvfp4=True) == -1 and call(9, nvfp4=True) == -2
     assert call(1, window=-5) == -1 and call(2, nvfp4=True, window=-1) == -1
+
+
+def test_block_copy_host_validation(K):
+    for fmt, kvd in ((K.KVQ_KV_BF16, oracle.KV_BF16), (K.KVQ_KV_FP8_E4M3, oracle.KV_FP8), (2, oracle.KV_NVFP4)):
+        for Hkv, D in ((8, 64), (4, 256), (1, 128)):
+            assert K.kvq_cache_block_bytes(fmt, Hkv, D) == oracle.block_bytes(kvd, Hkv, D)
+    assert K.kvq_cache_block_bytes(3, 8, 64) == 0 and K.kvq_cache_block_bytes(1, 8, 96) == 0
+    L = K.lib()
+    assert L.kvq_gather_blocks(FAKE, 8192, FAKE, -1, FAKE, None) == -1
+    assert L.kvq_gather_blocks(FAKE, 100, FAKE, 3, FAKE, None) == -1      # not a multiple of 16
+    assert L.kvq_gather_blocks(FAKE, 8192, None, 3, FAKE, None) == -1
+    assert L.kvq_scatter_blocks(FAKE + 8, 8192, FAKE, 3, FAKE, None) == -1  # misaligned
+    assert L.kvq_gather_blocks(FAKE, 8192, FAKE, 0, FAKE, None) == 0        # nothing to do, no HIP call
+    assert L.kvq_offload_blocks(FAKE, FAKE, 8192, FAKE, 2, None, FAKE, None) == -1
+    assert L.kvq_restore_blocks(FAKE, FAKE + 4, 8192, FAKE, 2, FAKE, FAKE, None) == -1
