@@ -53,7 +53,8 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 1
+/* 2: multi-query and sliding-window decode, host-memory block tier */
+#define KVQ_ABI_VERSION 2
 
 enum kvq_status {
     KVQ_OK = 0,

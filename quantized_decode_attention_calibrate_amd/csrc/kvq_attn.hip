@@ -161,9 +161,6 @@ __device__ __forceinline__ void write_empty(const DecodeArgs& a, int b, int g, i
 //                     so the lane's 16 contiguous bytes are that dim's 16 tokens
 //     B col n      <- weights of head n for the same 8 tokens
 //     C            -> acc[dt]: lane holds out[dim 16dt + 4grp + r][head n]
-#ifndef KVQ_MFMA_PREFETCH
-#define KVQ_MFMA_PREFETCH 1
-#endif
 
 // Raw bytes of one 64-token chunk as this lane needs them, per cache format.
 template <int D, int FMT>
@@ -458,8 +455,9 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
     constexpr int KJ = D / 64;
     constexpr int DT = D / 16;
     constexpr int CP = 16 * NT;   // padded columns
-    // two chunks in flight per wave where the registers allow it
-    constexpr bool kPrefetch = KVQ_MFMA_PREFETCH && D <= 128;
+    // two chunks in flight per wave where the registers allow it (measured
+    // faster than one for every D <= 128 shape, single and multi-query)
+    constexpr bool kPrefetch = D <= 128;
     extern __shared__ float lds[];
     int* s_blk = reinterpret_cast<int*>(lds);
     float* s_m = lds + kMaxSplitBlocks;

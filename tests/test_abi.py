@@ -38,7 +38,8 @@ def test_every_declared_symbol_is_exported(K):
     assert len(names) >= 12
     for n in names:
         assert hasattr(K.lib(), n), n
-    assert K.kvq_abi_version() == 1
+    want = int(re.search(r"#define KVQ_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert K.kvq_abi_version() == want == 2
     assert K.kvq_strerror(-3) == "workspace too small"
 
 
