@@ -65,6 +65,7 @@ def lib() -> ctypes.CDLL:
             "kvqo_block_bytes": (ctypes.c_size_t, [I, I, I, I]),
             "kvqo_gather_blocks": (None, [P, ctypes.c_size_t, P, I, P]),
             "kvqo_scatter_blocks": (None, [P, ctypes.c_size_t, P, I, P]),
+            "kvqo_decode_attn_fp8qp": (None, [P, I, I, P, P, P, I, P, I, I, I, I, I, F, F, F, F, P, I]),
             "kvqo_decode_attn_mq": (None, [P, I, I, P, P, I, P, I, P, I, I, I, I, I, F, F, F, P, I]),
             "kvqo_fp8_cos_sim": (D, [P, I64, F]),
         }
@@ -246,6 +247,22 @@ def decode_attn_mq(q, k_cache: np.ndarray, v_cache: np.ndarray, kv_dtype: int, b
     out = np.zeros((B, q_len, Hq, D), dtype=np.float64)
     lib().kvqo_decode_attn_mq(_ptr(qb), q_len, window, _ptr(kc), _ptr(vc), kv_dtype, _ptr(bt), bt.shape[1], _ptr(sl),
                               B, Hq, Hkv, D, block_size, k_scale, v_scale, sm_scale, _ptr(out), nthreads)
+    return out
+
+
+def decode_attn_fp8qp(q, k_cache: np.ndarray, v_cache: np.ndarray, block_tables, seq_lens, Hkv: int,
+                      block_size: int, q_scale: float, k_scale: float, v_scale: float, sm_scale: float,
+                      nthreads: int = 1, window: int = 0) -> np.ndarray:
+    """FP8 Q and P attention [B][q_len][Hq][D] over an FP8 cache (see kvq_oracle.h)."""
+    qb = _bits16(q)
+    B, q_len, Hq, D = qb.shape
+    bt = np.ascontiguousarray(np.asarray(block_tables, dtype=np.int32))
+    sl = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    kc, vc = np.ascontiguousarray(k_cache), np.ascontiguousarray(v_cache)
+    out = np.zeros((B, q_len, Hq, D), dtype=np.float64)
+    lib().kvqo_decode_attn_fp8qp(_ptr(qb), q_len, window, _ptr(kc), _ptr(vc), _ptr(bt), bt.shape[1], _ptr(sl),
+                                 B, Hq, Hkv, D, block_size, q_scale, k_scale, v_scale, sm_scale, _ptr(out),
+                                 nthreads)
     return out
 
 

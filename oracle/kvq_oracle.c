@@ -275,6 +275,8 @@ typedef struct {
     int n_units;
     int q_len;            /* queries per sequence: the q_len newest tokens */
     int window;           /* > 0: each query sees at most its `window` newest tokens */
+    int fp8qp;            /* FP8 Q and P variant (FP8 cache only) */
+    float q_scale;        /* fp8qp: Q quantization scale */
     double* out;
     int next_unit;
     pthread_mutex_t lock;
@@ -330,6 +332,46 @@ static void attend_one(const attn_job* j, int b, int i, int h, double* out, doub
     for (int d = 0; d < D; ++d) out[d] /= denom;
 }
 
+/* FP8 Q and P: q codes E4M3(fp32(q) / q_scale); x_t = c * sum_d value(qc_d) *
+ * value(kc_td) with c = fp32(sm_scale * q_scale * k_scale * log2 e); integer
+ * reference R = ceil(max_t x_t); P code pc_t = E4M3(fp32(448 * 2^(x_t - R)));
+ * out = v_scale * sum_t value(pc_t) value(vc_t) / sum_t value(pc_t). */
+static void attend_one_fp8qp(const attn_job* j, int b, int i, int h, double* out, double* s) {
+    int G = j->Hq / j->Hkv;
+    int g = h / G;
+    int L = j->seq_lens[b] - j->q_len + 1 + i;
+    int D = j->D;
+    const uint16_t* q = j->q + (((int64_t)b * j->q_len + i) * j->Hq + h) * D;
+    for (int d = 0; d < D; ++d) out[d] = 0.0;
+    if (L <= 0) return;
+    int t0 = (j->window > 0 && L > j->window) ? L - j->window : 0;
+    const double c = (double)(float)((double)j->sm_scale * (double)j->q_scale * (double)j->k_scale *
+                                     1.4426950408889634);
+    double qv[256];
+    for (int d = 0; d < D; ++d) qv[d] = kvqo_e4m3_value(kvqo_e4m3_quantize(q[d], j->q_scale));
+    const uint8_t* kc = (const uint8_t*)j->k_cache;
+    const uint8_t* vc = (const uint8_t*)j->v_cache;
+    double xmax = -INFINITY;
+    for (int t = t0; t < L; ++t) {
+        int64_t slot = (int64_t)j->block_tables[(int64_t)b * j->max_blocks + t / j->block_size] *
+                           j->block_size + t % j->block_size;
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d) dot += qv[d] * kvqo_e4m3_value(kc[k_index(slot, g, d, j->Hkv, D, j->block_size)]);
+        s[t] = c * dot;
+        if (s[t] > xmax) xmax = s[t];
+    }
+    const double R = ceil(xmax);
+    double denom = 0.0;
+    for (int t = t0; t < L; ++t) {
+        int64_t slot = (int64_t)j->block_tables[(int64_t)b * j->max_blocks + t / j->block_size] *
+                           j->block_size + t % j->block_size;
+        double pw = kvqo_e4m3_value(kvqo_e4m3_encode((float)(448.0 * exp2(s[t] - R))));
+        denom += pw;
+        for (int d = 0; d < D; ++d) out[d] += pw * kvqo_e4m3_value(vc[v_index(slot, g, d, j->Hkv, D, j->block_size)]);
+    }
+    for (int d = 0; d < D; ++d) out[d] = out[d] * (double)j->v_scale / denom;
+}
+
 static void* attn_worker(void* arg) {
     attn_job* j = (attn_job*)arg;
     int max_L = 0;
@@ -351,7 +393,10 @@ static void* attn_worker(void* arg) {
             i = u / j->Hq % j->q_len;
             h = u % j->Hq;
         }
-        attend_one(j, b, i, h, j->out + (int64_t)u * j->D, s);
+        if (j->fp8qp)
+            attend_one_fp8qp(j, b, i, h, j->out + (int64_t)u * j->D, s);
+        else
+            attend_one(j, b, i, h, j->out + (int64_t)u * j->D, s);
     }
     free(s);
     return NULL;
@@ -379,7 +424,7 @@ void kvqo_decode_attn(const uint16_t* q, const void* k_cache, const void* v_cach
                       double* out, int nthreads) {
     attn_job j = {q, k_cache, v_cache, kv_dtype, block_tables, max_blocks, seq_lens,
                   B, Hq, Hkv, D, block_size, k_scale, v_scale, sm_scale,
-                  NULL, B * Hq, 1, 0, out, 0};
+                  NULL, B * Hq, 1, 0, 0, 0.0f, out, 0};
     run_attn(&j, nthreads);
 }
 
@@ -390,7 +435,7 @@ void kvqo_decode_attn_mq(const uint16_t* q, int q_len, int window, const void* k
                          double* out, int nthreads) {
     attn_job j = {q, k_cache, v_cache, kv_dtype, block_tables, max_blocks, seq_lens,
                   B, Hq, Hkv, D, block_size, k_scale, v_scale, sm_scale,
-                  NULL, B * q_len * Hq, q_len, window, out, 0};
+                  NULL, B * q_len * Hq, q_len, window, 0, 0.0f, out, 0};
     run_attn(&j, nthreads);
 }
 
@@ -401,7 +446,18 @@ void kvqo_decode_attn_units(const uint16_t* q, const void* k_cache, const void* 
                             const int32_t* units, int n_units, double* out, int nthreads) {
     attn_job j = {q, k_cache, v_cache, kv_dtype, block_tables, max_blocks, seq_lens,
                   B, Hq, Hkv, D, block_size, k_scale, v_scale, sm_scale,
-                  units, n_units, 1, 0, out, 0};
+                  units, n_units, 1, 0, 0, 0.0f, out, 0};
+    run_attn(&j, nthreads);
+}
+
+void kvqo_decode_attn_fp8qp(const uint16_t* q, int q_len, int window, const uint8_t* k_cache,
+                            const uint8_t* v_cache, const int32_t* block_tables, int max_blocks,
+                            const int32_t* seq_lens, int B, int Hq, int Hkv, int D, int block_size,
+                            float q_scale, float k_scale, float v_scale, float sm_scale, double* out,
+                            int nthreads) {
+    attn_job j = {q, k_cache, v_cache, 1, block_tables, max_blocks, seq_lens,
+                  B, Hq, Hkv, D, block_size, k_scale, v_scale, sm_scale,
+                  NULL, B * q_len * Hq, q_len, window, 1, q_scale, out, 0};
     run_attn(&j, nthreads);
 }
 

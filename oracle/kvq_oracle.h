@@ -159,6 +159,24 @@ void kvqo_decode_attn_mq(const uint16_t* q, int q_len, int window, const void* k
                          int block_size, float k_scale, float v_scale, float sm_scale,
                          double* out, int nthreads);
 
+/* FP8 Q and P variant over an FP8 cache (a reading of the Radiance FP8
+ * guide's Q maxima and prob_scale): same queries, causality and window as
+ * kvqo_decode_attn_mq, with
+ *   qc_d  = E4M3(fp32(q_d) / q_scale)                     (kvqo_e4m3_quantize)
+ *   x_t   = c * sum_d value(qc_d) * value(kc_td),  c = fp32(sm_scale * q_scale
+ *           * k_scale * log2 e) rounded once from fp64
+ *   R     = ceil(max_t x_t)          (an integer: a power-of-two reference)
+ *   pc_t  = E4M3(fp32(448 * 2^(x_t - R)))                  (P in (0, 448])
+ *   out   = v_scale * sum_t value(pc_t) value(vc_t) / sum_t value(pc_t)
+ * in fp64.  The power-of-two reference makes the P codes independent of how
+ * a kernel orders or splits the tokens (rescaling by 2^k commutes with E4M3
+ * rounding in the normal range). */
+void kvqo_decode_attn_fp8qp(const uint16_t* q, int q_len, int window, const uint8_t* k_cache,
+                            const uint8_t* v_cache, const int32_t* block_tables, int max_blocks,
+                            const int32_t* seq_lens, int B, int Hq, int Hkv, int D, int block_size,
+                            float q_scale, float k_scale, float v_scale, float sm_scale, double* out,
+                            int nthreads);
+
 /* Same as kvqo_decode_attn, for a chosen subset of (b, h) units:
  * units[2*i] = b, units[2*i+1] = h; out is [n_units][D]. */
 void kvqo_decode_attn_units(const uint16_t* q, const void* k_cache, const void* v_cache,
