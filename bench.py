@@ -280,6 +280,24 @@ def measure_multiquery(torch, K, name, q_lens, steps, warmup):
         rec[f"q_len_{ql}"] = {"attn_us": round(us, 2), "attn_gbps": round(byts / (us * 1e-6) / 1e9, 1),
                               "over_q_len_1": round(us / t1, 3),
                               "kv_tokens_verified_per_s": round(sum(w.seq_lens) * ql / (us * 1e-6), 1)}
+    # FP8 Q and P variant: both products on FP8 MFMA, q_scale calibrated on the queries
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    for ql in (1, 4):
+        q = workloads.mq_queries(w, ql, seed=0).cuda()
+        amax.zero_()
+        K.kvq_amax_bf16(q, amax)
+        qs = K.kvq_calibrate([float(amax.item())])[0]
+        out = torch.empty(w.B, ql, w.Hq, w.D, dtype=torch.bfloat16, device="cuda")
+        ws = K.new_workspace_mq(w.B, ql, w.Hq, w.Hkv, w.D, w.max_seq_len)
+
+        def call_qp(i, q=q, out=out, ws=ws, qs=qs):
+            kc, vc = L.caches[i % L.R]
+            K.kvq_paged_decode_attn_fp8qp(q, kc, vc, L.bt, L.sl, w.max_seq_len, w.Hkv, qs, L.ks, L.vs, L.sm, out, ws)
+        us = timed(call_qp)
+        byts = attn_b1 + (ql - 1) * 2 * w.B * w.Hq * w.D * 2
+        base = t1 if ql == 1 else rec.get(f"q_len_{ql}", {}).get("attn_us")
+        rec[f"fp8qp_q_len_{ql}"] = {"attn_us": round(us, 2), "attn_gbps": round(byts / (us * 1e-6) / 1e9, 1),
+                                    "over_fp8_path": round(us / base, 3) if base else None}
     del L, w
     torch.cuda.empty_cache()
     return rec

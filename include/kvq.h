@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-/* 2: multi-query and sliding-window decode, host-memory block tier */
+/* 2: multi-query and sliding-window decode, FP8 Q/P variant, host-memory block tier */
 #define KVQ_ABI_VERSION 2
 
 enum kvq_status {
@@ -282,6 +282,40 @@ int kvq_nvfp4_paged_decode_attn_mq(const void* q_dev, int q_len, int window, con
                                    void* out_dev, int out_dtype,
                                    void* workspace_dev, size_t workspace_bytes, void* hip_stream,
                                    int split_tokens);
+
+/* ---- FP8 Q and P variant -------------------------------------------------------
+ * The Radiance FP8 guide observes Q maxima alongside K and V and names a
+ * prob_scale on other attention paths.  This variant runs both products on
+ * FP8 MFMA (v_mfma_f32_16x16x32_fp8_fp8) straight from the cache bytes, over an
+ * FP8 cache, with the queries, causality and window of
+ * kvq_paged_decode_attn_mq:
+ *   qc_d = E4M3(fp32(q_d) / q_scale)    (q_scale from kvq_calibrate on Q maxima)
+ *   x_t  = c * sum_d value(qc_d) * value(kc_td),
+ *          c = fp32(sm_scale * q_scale * k_scale * log2 e) rounded once from fp64
+ *   R    = ceil(max_t x_t), an integer: a power-of-two softmax reference
+ *   pc_t = E4M3(448 * 2^(x_t - R))      (prob_scale 1/448: P in (0, 448])
+ *   out  = v_scale * sum_t value(pc_t) value(vc_t) / sum_t value(pc_t)
+ * The kernel keeps an integer running reference, so every rescale is an
+ * exact power of two and a weight's code does not depend on the split or
+ * chunk order, except for E4M3 subnormal weights, which round more finely
+ * against an earlier, lower reference.  The FP8 MFMA dot step is not exact:
+ * it sums each group of 8 products aligned to the group's largest exponent
+ * sum 2^E and drops what lies below 2^(E-13), so scores, PV sums and the
+ * weight sum carry a small bounded error and a weight near an E4M3 midpoint
+ * may take either code.  The result lies within a band around the definition
+ * derived from that model (median width ~2.5e-3 for unit-scale V).  3-bit Q
+ * and P move every weight by a few per cent: on N(0,1) data the output is
+ * ~8e-2 (relative L2) away from kvq_paged_decode_attn_mq's.  Same workspace
+ * as kvq_decode_workspace_bytes_mq; errors as kvq_paged_decode_attn_mq plus
+ * KVQ_EINVAL for a bad q_scale. */
+int kvq_paged_decode_attn_fp8qp(const void* q_dev, int q_len, int window, const void* k_cache_dev,
+                                const void* v_cache_dev, const int32_t* block_tables_dev, int max_blocks_per_seq,
+                                const int32_t* seq_lens_dev, int max_seq_len,
+                                int B, int Hq, int Hkv, int D, int block_size, int num_blocks,
+                                float q_scale, float k_scale, float v_scale, float sm_scale,
+                                void* out_dev, int out_dtype,
+                                void* workspace_dev, size_t workspace_bytes, void* hip_stream,
+                                int split_tokens);
 
 /* ---- block copies for a host-memory KV tier --------------------------------
  * The Radiance FP8 guide's operator notes account offloaded KV by block bytes

@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
             "kvqo_gather_blocks": (None, [P, ctypes.c_size_t, P, I, P]),
             "kvqo_scatter_blocks": (None, [P, ctypes.c_size_t, P, I, P]),
             "kvqo_decode_attn_fp8qp": (None, [P, I, I, P, P, P, I, P, I, I, I, I, I, F, F, F, F, P, I]),
+            "kvqo_decode_attn_fp8qp_band": (None, [P, I, I, P, P, P, I, P, I, I, I, I, I, F, F, F, F,
+                                                   ctypes.c_double, P, P, P, P, P, P]),
             "kvqo_decode_attn_mq": (None, [P, I, I, P, P, I, P, I, P, I, I, I, I, I, F, F, F, P, I]),
             "kvqo_fp8_cos_sim": (D, [P, I64, F]),
         }
@@ -264,6 +266,35 @@ def decode_attn_fp8qp(q, k_cache: np.ndarray, v_cache: np.ndarray, block_tables,
                                  B, Hq, Hkv, D, block_size, q_scale, k_scale, v_scale, sm_scale, _ptr(out),
                                  nthreads)
     return out
+
+
+def decode_attn_fp8qp_band(q, k_cache: np.ndarray, v_cache: np.ndarray, block_tables, seq_lens, Hkv: int,
+                           block_size: int, q_scale: float, k_scale: float, v_scale: float, sm_scale: float,
+                           dot_ulp: float, window: int = 0, weights: bool = False):
+    """(lo, hi, tol, n_ambiguous): what a one-pass kernel on FP8 matrix cores
+    may return for decode_attn_fp8qp -- every output in [lo - tol, hi + tol].
+    dot_ulp: the FP8 dot step's cut below the largest exponent sum of a group
+    of 8 products (kvq_oracle.h states the model).  weights=True appends the
+    per-token weight intervals (w_lo, w_hi), [B][q_len][Hq][max seq_len]."""
+    qb = _bits16(q)
+    B, q_len, Hq, D = qb.shape
+    bt = np.ascontiguousarray(np.asarray(block_tables, dtype=np.int32))
+    sl = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    kc, vc = np.ascontiguousarray(k_cache), np.ascontiguousarray(v_cache)
+    lo = np.zeros((B, q_len, Hq, D), dtype=np.float64)
+    hi = np.zeros_like(lo)
+    tol = np.zeros_like(lo)
+    n = np.zeros(1, dtype=np.int32)
+    max_l = max(1, int(sl.max())) if sl.size else 1
+    wl = np.zeros((B, q_len, Hq, max_l)) if weights else None
+    wh = np.zeros_like(wl) if weights else None
+    lib().kvqo_decode_attn_fp8qp_band(_ptr(qb), q_len, window, _ptr(kc), _ptr(vc), _ptr(bt), bt.shape[1], _ptr(sl),
+                                      B, Hq, Hkv, D, block_size, q_scale, k_scale, v_scale, sm_scale, dot_ulp,
+                                      _ptr(lo), _ptr(hi), _ptr(tol), _ptr(n), _ptr(wl) if weights else None,
+                                      _ptr(wh) if weights else None)
+    if weights:
+        return lo, hi, tol, int(n[0]), wl, wh
+    return lo, hi, tol, int(n[0])
 
 
 def fp8_cos_sim(x, scale: float) -> float:

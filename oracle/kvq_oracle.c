@@ -450,6 +450,178 @@ void kvqo_decode_attn_units(const uint16_t* q, const void* k_cache, const void* 
     run_attn(&j, nthreads);
 }
 
+/* Binade of an E4M3 value as an exponent-aligning adder sees it: 2^floor(log2 |v|),
+ * and 2^-6 (the exponent of the smallest normal) for subnormal codes and zero. */
+static double e4m3_binade(double v) {
+    v = fabs(v);
+    if (v < 0.015625) return 0.015625;
+    int e;
+    frexp(v, &e);
+    return ldexp(1.0, e - 1);
+}
+
+#define FP8_DOT_GROUP 8   /* products an FP8 matrix-core dot step sums before rounding */
+
+void kvqo_decode_attn_fp8qp_band(const uint16_t* q, int q_len, int window, const uint8_t* k_cache,
+                                 const uint8_t* v_cache, const int32_t* block_tables, int max_blocks,
+                                 const int32_t* seq_lens, int B, int Hq, int Hkv, int D, int block_size,
+                                 float q_scale, float k_scale, float v_scale, float sm_scale, double dot_ulp,
+                                 double* lo, double* hi, double* tol, int* n_ambiguous, double* w_lo,
+                                 double* w_hi) {
+    const int G = Hq / Hkv;
+    const double c = (double)(float)((double)sm_scale * (double)q_scale * (double)k_scale * 1.4426950408889634);
+    const double e21 = ldexp(1.0, -21), e24 = ldexp(1.0, -24);
+    int max_L = 0;
+    for (int b = 0; b < B; ++b)
+        if (seq_lens[b] > max_L) max_L = seq_lens[b];
+    const size_t n_alloc = (size_t)(max_L > 0 ? max_L : 1);
+    double* pl = (double*)malloc(sizeof(double) * n_alloc);
+    double* ph = (double*)malloc(sizeof(double) * n_alloc);
+    double* x = (double*)malloc(sizeof(double) * n_alloc);
+    double* dx = (double*)malloc(sizeof(double) * n_alloc);
+    double* vv = (double*)malloc(sizeof(double) * n_alloc);
+    *n_ambiguous = 0;
+    for (int b = 0; b < B; ++b)
+        for (int i = 0; i < q_len; ++i)
+            for (int h = 0; h < Hq; ++h) {
+                const int64_t row = ((int64_t)b * q_len + i) * Hq + h;
+                double* olo = lo + row * D;
+                double* ohi = hi + row * D;
+                double* otol = tol + row * D;
+                for (int d = 0; d < D; ++d) olo[d] = ohi[d] = otol[d] = 0.0;
+                const int Lseq = seq_lens[b];
+                const int L = Lseq - q_len + 1 + i;
+                if (L <= 0) continue;
+                const int t0 = (window > 0 && L > window) ? L - window : 0;
+                const uint16_t* qr = q + row * D;
+                const int g = h / G;
+                double qv[256], qb[256];
+                for (int d = 0; d < D; ++d) {
+                    qv[d] = kvqo_e4m3_value(kvqo_e4m3_quantize(qr[d], q_scale));
+                    qb[d] = e4m3_binade(qv[d]);
+                }
+                /* scores and their error bounds: within each group of 8 dims the products are
+                   aligned to the largest exponent sum 2^E and cut below 2^E dot_ulp, then the group
+                   sums add in fp32; the kernel's fma with the scale and its ceil round once more */
+                double r_hi = -INFINITY;
+                for (int t = t0; t < L; ++t) {
+                    const int64_t slot = (int64_t)block_tables[(int64_t)b * max_blocks + t / block_size] * block_size +
+                                         t % block_size;
+                    double dot = 0.0, sabs = 0.0, gsum = 0.0;
+                    for (int d0 = 0; d0 < D; d0 += FP8_DOT_GROUP) {
+                        double gmax = 0.0;
+                        for (int d = d0; d < d0 + FP8_DOT_GROUP; ++d) {
+                            const double kv = kvqo_e4m3_value(k_cache[k_index(slot, g, d, Hkv, D, block_size)]);
+                            dot += qv[d] * kv;
+                            sabs += fabs(qv[d] * kv);
+                            gmax = fmax(gmax, qb[d] * e4m3_binade(kv));
+                        }
+                        gsum += gmax;
+                    }
+                    x[t] = c * dot;
+                    dx[t] = c * (FP8_DOT_GROUP * dot_ulp * gsum + ldexp(sabs, -19)) + ldexp(fabs(x[t]) + 1.0, -23);
+                    r_hi = fmax(r_hi, ceil(x[t] + dx[t]));
+                }
+                /* each weight: E4M3(448 2^(x' - r)) for a score x' within dx of x and any reference
+                   r the kernel can hold, from ceil(x') up to the final one (at most r_hi), in the
+                   frame of r_hi; rounding is monotone, so the interval ends are the roundings of
+                   the interval ends (with fp32 and exp2 slack) */
+                double l_min = 0.0, l_max = 0.0;
+                for (int t = t0; t < L; ++t) {
+                    const double r0 = ceil(x[t] - dx[t]);
+                    double pmin = INFINITY, pmax = 0.0;
+                    if (r0 < r_hi - 400.0) pmin = 0.0;
+                    for (double r = fmax(r0, r_hi - 400.0); r <= r_hi; r += 1.0) {
+                        const double ylo = 448.0 * exp2(x[t] - dx[t] - r) * (1.0 - e21);
+                        const double yhi = fmin(448.0, 448.0 * exp2(x[t] + dx[t] - r) * (1.0 + e21));
+                        const uint8_t clo = kvqo_e4m3_encode((float)ylo), chi = kvqo_e4m3_encode((float)yhi);
+                        pmin = fmin(pmin, ldexp(kvqo_e4m3_value(clo), (int)(r - r_hi)));
+                        pmax = fmax(pmax, ldexp(kvqo_e4m3_value(chi), (int)(r - r_hi)));
+                        if (r == r_hi && clo != chi) ++*n_ambiguous;
+                        if (yhi < ldexp(1.0, -11)) {   /* rounds to zero from here on */
+                            pmin = 0.0;
+                            break;
+                        }
+                    }
+                    pl[t] = pmin;
+                    ph[t] = pmax;
+                    if (w_lo) {
+                        w_lo[row * max_L + t] = pmin;
+                        w_hi[row * max_L + t] = pmax;
+                    }
+                    l_min += pmin;
+                    l_max += pmax;
+                }
+                /* accumulation bound: the PV and weight-sum products are cut the same way within
+                   each group of 8 tokens (aligned at multiples of 8; tokens a column does not see
+                   carry a zero weight, whose binade is 2^-6), then added in fp32 */
+                const double eps = (double)((L - t0 + 31) / 32 + 8) * e24;
+                double lgsum = 0.0;
+                for (int t8 = t0 & ~(FP8_DOT_GROUP - 1); t8 < L; t8 += FP8_DOT_GROUP) {
+                    double gmax = 0.015625;
+                    for (int t = (t8 > t0 ? t8 : t0); t < t8 + FP8_DOT_GROUP && t < L; ++t)
+                        gmax = fmax(gmax, e4m3_binade(ph[t]));
+                    lgsum += gmax;
+                }
+                const double dl = FP8_DOT_GROUP * dot_ulp * lgsum + eps * l_max;
+                /* the V codes a group of 8 tokens may hold: up to the end of the group or the sequence */
+                const int t_end = (L + FP8_DOT_GROUP - 1) / FP8_DOT_GROUP * FP8_DOT_GROUP < Lseq
+                                      ? (L + FP8_DOT_GROUP - 1) / FP8_DOT_GROUP * FP8_DOT_GROUP
+                                      : Lseq;
+                for (int d = 0; d < D; ++d) {
+                    for (int t = t0 & ~(FP8_DOT_GROUP - 1); t < t_end; ++t) {
+                        const int64_t slot = (int64_t)block_tables[(int64_t)b * max_blocks + t / block_size] *
+                                                 block_size + t % block_size;
+                        vv[t] = kvqo_e4m3_value(v_cache[v_index(slot, g, d, Hkv, D, block_size)]);
+                    }
+                    /* extremes of sum p v / sum p over p_t in [pl_t, ph_t]: Dinkelbach iterations (the
+                       maximum takes ph_t where v_t > f and pl_t elsewhere, the minimum the reverse) */
+                    for (int dir = 0; dir < 2; ++dir) {
+                        double f = 0.0, num = 0.0, den = 0.0;
+                        for (int t = t0; t < L; ++t) {
+                            num += ph[t] * vv[t];
+                            den += ph[t];
+                        }
+                        f = num / den;
+                        for (int it = 0; it < 64; ++it) {
+                            num = den = 0.0;
+                            for (int t = t0; t < L; ++t) {
+                                double p = (dir == 0) == (vv[t] > f) ? ph[t] : pl[t];
+                                num += p * vv[t];
+                                den += p;
+                            }
+                            double fn = num / den;
+                            if (fn == f) break;
+                            f = fn;
+                        }
+                        if (dir == 0)
+                            ohi[d] = f * (double)v_scale;
+                        else
+                            olo[d] = f * (double)v_scale;
+                    }
+                    double a_abs = 0.0, ga = 0.0;
+                    for (int t8 = t0 & ~(FP8_DOT_GROUP - 1); t8 < L; t8 += FP8_DOT_GROUP) {
+                        double gmax = 0.015625 * 0.015625;
+                        for (int t = t8; t < t8 + FP8_DOT_GROUP && t < t_end; ++t) {
+                            const int seen = t >= t0 && t < L;
+                            gmax = fmax(gmax, (seen ? e4m3_binade(ph[t]) : 0.015625) * e4m3_binade(vv[t]));
+                            if (seen) a_abs += ph[t] * fabs(vv[t]);
+                        }
+                        ga += gmax;
+                    }
+                    const double da = FP8_DOT_GROUP * dot_ulp * ga + eps * a_abs;
+                    const double omax = fmax(fabs(olo[d]), fabs(ohi[d])) / (double)v_scale;
+                    otol[d] = l_min > dl ? (double)v_scale * ((da + omax * dl) / (l_min - dl) + ldexp(omax, -21))
+                                         : INFINITY;
+                }
+            }
+    free(pl);
+    free(ph);
+    free(x);
+    free(dx);
+    free(vv);
+}
+
 void kvqo_decode_attn_fp8qp(const uint16_t* q, int q_len, int window, const uint8_t* k_cache,
                             const uint8_t* v_cache, const int32_t* block_tables, int max_blocks,
                             const int32_t* seq_lens, int B, int Hq, int Hkv, int D, int block_size,

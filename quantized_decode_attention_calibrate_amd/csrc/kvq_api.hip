@@ -202,7 +202,8 @@ static int decode_common(int fmt, const void* q_dev, int q_len, int window, cons
                          const int32_t* block_tables_dev, int max_blocks_per_seq, const int32_t* seq_lens_dev,
                          int max_seq_len, int B, int Hq, int Hkv, int D, int block_size, int num_blocks,
                          float k_scale, float v_scale, float sm_scale, void* out_dev, int out_dtype,
-                         void* workspace_dev, size_t workspace_bytes, void* hip_stream, int impl, int split_tokens) {
+                         void* workspace_dev, size_t workspace_bytes, void* hip_stream, int impl, int split_tokens,
+                         float q_scale = 1.0f) {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_seq_len < 0)
         return KVQ_EINVAL;
     if (q_len < 1 || q_len > kMaxQueryLen || window < 0) return KVQ_EINVAL;
@@ -219,6 +220,7 @@ static int decode_common(int fmt, const void* q_dev, int q_len, int window, cons
     if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * block_size) return KVQ_EINVAL;
     if (!isfinite(sm_scale) || !(sm_scale > 0.0f)) return KVQ_EINVAL;
     if (fmt != kFmtBF16 && (!good_scale(k_scale) || !good_scale(v_scale))) return KVQ_EINVAL;
+    if (fmt == kFmtFP8QP && !good_scale(q_scale)) return KVQ_EINVAL;
     if (B == 0) return KVQ_OK;
     if (!q_dev || !k_cache_dev || !v_cache_dev || !block_tables_dev || !seq_lens_dev || !out_dev ||
         !workspace_dev)
@@ -248,7 +250,10 @@ static int decode_common(int fmt, const void* q_dev, int q_len, int window, cons
     a.G = G;
     a.split_tokens = plan.split_tokens;
     a.num_splits = plan.num_splits;
-    a.qk_scale_log2 = (float)((double)sm_scale * (scaled ? (double)k_scale : 1.0) * 1.4426950408889634);
+    a.qk_scale_log2 = fmt == kFmtFP8QP
+                          ? (float)((double)sm_scale * (double)q_scale * (double)k_scale * 1.4426950408889634)
+                          : (float)((double)sm_scale * (scaled ? (double)k_scale : 1.0) * 1.4426950408889634);
+    a.q_scale = q_scale;
     a.v_scale = scaled ? v_scale : 1.0f;
     a.out_f32 = out_dtype == KVQ_OUT_F32;
     a.q_len = q_len;
@@ -386,6 +391,18 @@ int kvq_restore_blocks(const void* host_src, void* staging_dev, size_t block_byt
     if (v != KVQ_OK) return v;
     return hip_status(launch_block_copy((const char*)staging_dev + half, v_cache_dev, block_ids_dev, n, block_bytes, 0,
                                         st));
+}
+
+int kvq_paged_decode_attn_fp8qp(const void* q_dev, int q_len, int window, const void* k_cache_dev,
+                                const void* v_cache_dev, const int32_t* block_tables_dev, int max_blocks_per_seq,
+                                const int32_t* seq_lens_dev, int max_seq_len, int B, int Hq, int Hkv, int D,
+                                int block_size, int num_blocks, float q_scale, float k_scale, float v_scale,
+                                float sm_scale, void* out_dev, int out_dtype, void* workspace_dev,
+                                size_t workspace_bytes, void* hip_stream, int split_tokens) {
+    return decode_common(kFmtFP8QP, q_dev, q_len, window, k_cache_dev, v_cache_dev, block_tables_dev,
+                         max_blocks_per_seq, seq_lens_dev, max_seq_len, B, Hq, Hkv, D, block_size, num_blocks,
+                         k_scale, v_scale, sm_scale, out_dev, out_dtype, workspace_dev, workspace_bytes, hip_stream,
+                         KVQ_IMPL_MFMA, split_tokens, q_scale);
 }
 
 int kvq_paged_decode_attn(const void* q_dev, const void* k_cache_dev, const void* v_cache_dev, int kv_dtype,

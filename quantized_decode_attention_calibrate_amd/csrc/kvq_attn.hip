@@ -176,6 +176,8 @@ struct MfmaChunk<D, kFmtBF16> {       // the same elements at two bytes each
     u32x4 vw[D / 16][2];
 };
 template <int D>
+struct MfmaChunk<D, kFmtFP8QP> : MfmaChunk<D, kFmtFP8> {};   // the same raw FP8 bytes
+template <int D>
 struct MfmaChunk<D, kFmtNVFP4> {      // 16 E2M1 codes + 1 scale per (tile, slice); V dim row + 16 token scales
     u32x2 kc[4][D / 64];
     uint32_t ks[4][D / 64];
@@ -222,7 +224,7 @@ __device__ __forceinline__ void mfma_load(MfmaChunk<D, FMT>& c, const DecodeArgs
             const int64_t row = (((int64_t)pk * a.Hkv + g) * kBlockSize + off) * D;
 #pragma unroll
             for (int j = 0; j < KJ; ++j) {
-                if constexpr (FMT == kFmtFP8) {
+                if constexpr (FMT == kFmtFP8 || FMT == kFmtFP8QP) {
                     c.kw[i][j] = *reinterpret_cast<const u32x4*>(a.k_cache + row + 64 * j + 16 * grp);
                 } else {
                     const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.k_cache) + row + 64 * j + 16 * grp;
@@ -234,7 +236,7 @@ __device__ __forceinline__ void mfma_load(MfmaChunk<D, FMT>& c, const DecodeArgs
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
             const int64_t vrow = (((int64_t)pv * a.Hkv + g) * D + 16 * dt + n) * kBlockSize;
-            if constexpr (FMT == kFmtFP8) {
+            if constexpr (FMT == kFmtFP8 || FMT == kFmtFP8QP) {
                 c.vw[dt] = *reinterpret_cast<const u32x4*>(a.v_cache + vrow);
             } else {
                 const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.v_cache) + vrow;
@@ -249,11 +251,14 @@ __device__ __forceinline__ void mfma_load(MfmaChunk<D, FMT>& c, const DecodeArgs
 // of the tile's token row; bf16 for FP8 / BF16 caches, f16 for NVFP4 (codes
 // times the group's E4M3 block scale, exact in f16).
 template <int FMT>
-using QkOperand = typename std::conditional<FMT == kFmtNVFP4, f16x8, bf16x8>::type;
+using QkOperand = typename std::conditional<
+    FMT == kFmtNVFP4, f16x8, typename std::conditional<FMT == kFmtFP8QP, long, bf16x8>::type>::type;
 
 template <int D, int FMT>
 __device__ __forceinline__ QkOperand<FMT> k_operand(const MfmaChunk<D, FMT>& c, int i, int j, int hh) {
-    if constexpr (FMT == kFmtFP8) {
+    if constexpr (FMT == kFmtFP8QP) {
+        return __builtin_bit_cast(long, u32x2{c.kw[i][j][2 * hh], c.kw[i][j][2 * hh + 1]});   // raw codes
+    } else if constexpr (FMT == kFmtFP8) {
         return e4m3x8_to_bf16(c.kw[i][j][2 * hh], c.kw[i][j][2 * hh + 1]);
     } else if constexpr (FMT == kFmtBF16) {
         return __builtin_bit_cast(bf16x8, c.kw[i][j][hh]);
@@ -450,6 +455,123 @@ __device__ __forceinline__ void mfma_process(MfmaState<D, NT>& st, MfmaChunk<D, 
     }
 }
 
+// FP8 Q and P: one 64-token chunk on v_mfma_f32_16x16x32_fp8_fp8 with the raw
+// K and V bytes as operands.  The softmax reference R is an integer (in log2
+// units), so each rescale is an exact power of two and the P codes
+// E4M3(448 * 2^(x - R)) do not depend on the chunk order (up to E4M3
+// subnormals, which round more finely against a lower reference).  l is the
+// column sum of the P codes, taken with one MFMA against an all-ones A
+// operand, so every lane holds its column's whole sum.  The FP8 dot step
+// drops product bits below 2^-13 of each 8-product group's largest exponent
+// sum, so scores and sums are close to, not equal to, their exact values.
+template <int D, int NT>
+__device__ __forceinline__ void mfma_process_qp8(MfmaState<D, NT>& st, MfmaChunk<D, kFmtFP8QP>& c,
+                                                 const long (*qb)[2 * (D / 64)], float cs, const int* cbeg,
+                                                 const int* cend, int chunk_tok, int tok_end, int tail_from,
+                                                 int head_until, int vbeg, int grp) {
+    constexpr int KJ = D / 64, DT = D / 16;
+    float sv[NT][16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f32x4 t[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) t[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < KJ; ++j)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const long ka = k_operand(c, i, j, hh);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    t[nt] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(ka, qb[nt][2 * j + hh], t[nt], 0, 0, 0);
+            }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sv[nt][4 * i + r] = t[nt][r];
+    }
+    const bool tail = chunk_tok + kChunkTokens > tail_from || chunk_tok < head_until;
+    const int tok0 = chunk_tok + 16 * grp;
+    constexpr long kOnes = 0x3838383838383838L;   // eight E4M3 1.0
+    long pq[NT][2];
+    float alpha[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        if (tail) {
+            const int lo = cbeg[nt] - tok0, hi = cend[nt] - tok0;
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                if (e >= hi || e < lo) sv[nt][e] = -INFINITY;
+        }
+        float mloc = sv[nt][0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) mloc = fmaxf(mloc, sv[nt][e]);
+        mloc = fmaxf(mloc, shfl_xor(mloc, 16));
+        mloc = fmaxf(mloc, shfl_xor(mloc, 32));
+        const float r_new = fmaxf(st.m_run[nt], __builtin_ceilf(mloc * cs));   // integer-valued
+        const float r_use = r_new == -INFINITY ? 0.f : r_new;
+        alpha[nt] = st.m_run[nt] == -INFINITY ? 0.f : __builtin_ldexpf(1.0f, (int)(st.m_run[nt] - r_use));
+        st.m_run[nt] = r_new;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            u32x2 w;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                float y[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    y[e] = 448.0f * fast_exp2(__builtin_fmaf(sv[nt][8 * hh + 4 * q + e], cs, -r_use));
+                // y <= 448 up to one fp32 rounding of the reference (448.00003 rounds
+                // to 448): round to nearest even, no saturation or NaN to handle
+                uint32_t lo16 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false) & 0xFFFFu;
+                w[q] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], (int)lo16, true);
+            }
+            pq[nt][hh] = __builtin_bit_cast(long, w);
+        }
+        f32x4 ls = {0.f, 0.f, 0.f, 0.f};
+        ls = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(kOnes, pq[nt][0], ls, 0, 0, 0);
+        ls = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(kOnes, pq[nt][1], ls, 0, 0, 0);
+        st.l_run[nt] = st.l_run[nt] * alpha[nt] + ls[0];
+    }
+    if (chunk_tok + kChunkTokens > tok_end || chunk_tok < vbeg) {
+        const int valid = tok_end - tok0, vlo = vbeg - tok0;
+        u32x4 keep;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            uint32_t mask = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (4 * w + e < valid && 4 * w + e >= vlo) mask |= 0xFFu << (8 * e);
+            keep[w] = mask;
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) c.vw[dt] &= keep;
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) st.acc[nt][dt] *= alpha[nt];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const long va = __builtin_bit_cast(long, u32x2{c.vw[dt][2 * hh], c.vw[dt][2 * hh + 1]});
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                st.acc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(va, pq[nt][hh], st.acc[nt][dt], 0, 0, 0);
+        }
+    }
+}
+
+template <int D, int FMT, int NT>
+__device__ __forceinline__ void process_chunk(MfmaState<D, NT>& st, MfmaChunk<D, FMT>& c,
+                                              const QkOperand<FMT> (*qb)[2 * (D / 64)], const float* cs,
+                                              const int* cbeg, const int* cend, int chunk_tok, int tok_end,
+                                              int tail_from, int head_until, int vbeg, int grp) {
+    if constexpr (FMT == kFmtFP8QP)
+        mfma_process_qp8(st, c, qb, cs[0], cbeg, cend, chunk_tok, tok_end, tail_from, head_until, vbeg, grp);
+    else
+        mfma_process(st, c, qb, cs, cbeg, cend, chunk_tok, tok_end, tail_from, head_until, vbeg, grp);
+}
+
 template <int D, int FMT, int NT, int W = mfma_waves<D, FMT, NT>()>
 __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
     constexpr int KJ = D / 64;
@@ -513,7 +635,20 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
                 qw[2 * j + hh] = w;
             }
         cs[nt] = a.qk_scale_log2;
-        if constexpr (FMT == kFmtNVFP4) {
+        if constexpr (FMT == kFmtFP8QP) {
+            // q codes E4M3(fp32(q) / q_scale), the cache write's quantizer
+#pragma clang fp contract(off)
+#pragma unroll
+            for (int k = 0; k < 2 * KJ; ++k) {
+                u32x2 wc;
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2)
+                    wc[h2] = e4m3_encode4(bf16_lo(qw[k][2 * h2]) / a.q_scale, bf16_hi(qw[k][2 * h2]) / a.q_scale,
+                                          bf16_lo(qw[k][2 * h2 + 1]) / a.q_scale,
+                                          bf16_hi(qw[k][2 * h2 + 1]) / a.q_scale);
+                qb[nt][k] = live ? __builtin_bit_cast(long, wc) : 0L;
+            }
+        } else if constexpr (FMT == kFmtNVFP4) {
             float qmax = 0.f;
 #pragma unroll
             for (int k = 0; k < 2 * KJ; ++k)
@@ -569,13 +704,13 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
             for (int i = 0; i < my; i += 2) {
                 const int chb = i + 1 < my ? ch + W : ch;
                 mfma_load(Bc, a, s_blk, chb, g, n, grp);
-                mfma_process(st, A, qb, cs, cbeg, cend, tok_begin + ch * kChunkTokens, tok_end, tail_from,
-                             head_until, sr.first, grp);
+                process_chunk(st, A, qb, cs, cbeg, cend, tok_begin + ch * kChunkTokens, tok_end, tail_from,
+                              head_until, sr.first, grp);
                 if (i + 1 >= my) break;
                 const int cha = i + 2 < my ? chb + W : chb;
                 mfma_load(A, a, s_blk, cha, g, n, grp);
-                mfma_process(st, Bc, qb, cs, cbeg, cend, tok_begin + chb * kChunkTokens, tok_end, tail_from,
-                             head_until, sr.first, grp);
+                process_chunk(st, Bc, qb, cs, cbeg, cend, tok_begin + chb * kChunkTokens, tok_end, tail_from,
+                              head_until, sr.first, grp);
                 ch = cha;
             }
         }
@@ -584,8 +719,8 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
             const int ch = wave + i * W;
             MfmaChunk<D, FMT> A;
             mfma_load(A, a, s_blk, ch, g, n, grp);
-            mfma_process(st, A, qb, cs, cbeg, cend, tok_begin + ch * kChunkTokens, tok_end, tail_from,
-                         head_until, sr.first, grp);
+            process_chunk(st, A, qb, cs, cbeg, cend, tok_begin + ch * kChunkTokens, tok_end, tail_from,
+                          head_until, sr.first, grp);
         }
     }
 
@@ -593,8 +728,10 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         float l_run = st.l_run[nt];
-        l_run += shfl_xor(l_run, 16);
-        l_run += shfl_xor(l_run, 32);
+        if constexpr (FMT != kFmtFP8QP) {   // (the FP8 Q/P path already holds whole column sums)
+            l_run += shfl_xor(l_run, 16);
+            l_run += shfl_xor(l_run, 32);
+        }
         const int c = 16 * nt + n;
         if (grp == 0) {
             s_m[wave * CP + c] = st.m_run[nt];
@@ -881,10 +1018,10 @@ static hipError_t launch_family(const DecodeArgs& a, int B, int impl, hipStream_
     constexpr int W = mfma_waves<D, FMT, NT>();
     const int GQ = a.G * a.q_len;
     const size_t lds_mfma = sizeof(float) * (kMaxSplitBlocks + lds_merge_floats(GQ, D, W, NT));
-    if (FMT == kFmtNVFP4 || impl == 2 || NT > 1) {
+    if (FMT == kFmtNVFP4 || FMT == kFmtFP8QP || impl == 2 || NT > 1) {
         hipLaunchKernelGGL((decode_mfma_kernel<D, FMT, NT>), grid, dim3(W * 64), lds_mfma, st, a);
     } else {
-        if constexpr (FMT != kFmtNVFP4 && NT == 1) {
+        if constexpr ((FMT == kFmtFP8 || FMT == kFmtBF16) && NT == 1) {
             const size_t lds = sizeof(float) * (kMaxSplitBlocks + lds_merge_floats(a.G, D, kWaves) + a.G * D +
                                                 kWaves * 256);
             hipLaunchKernelGGL((decode_valu_kernel<D, FMT == kFmtFP8>), grid, dim3(kThreads), lds, st, a);
@@ -935,6 +1072,7 @@ hipError_t launch_decode(const DecodeArgs& a, int B, int D, int fmt, int impl, h
         case kFmtBF16: return launch_d<kFmtBF16>(a, B, D, impl, st);
         case kFmtFP8: return launch_d<kFmtFP8>(a, B, D, impl, st);
         case kFmtNVFP4: return launch_d<kFmtNVFP4>(a, B, D, impl, st);
+        case kFmtFP8QP: return launch_d<kFmtFP8QP>(a, B, D, impl, st);
         default: return hipErrorInvalidValue;
     }
 }

@@ -20,7 +20,8 @@ constexpr int kMaxSplits = 16384;
 constexpr int kChunkTokens = 64;   // tokens per wave iteration (4 blocks of 16)
 constexpr int kMaxQueryLen = 16;   // queries per sequence of a multi-query decode
 // KV cache formats of the decode kernels
-enum : int { kFmtBF16 = 0, kFmtFP8 = 1, kFmtNVFP4 = 2 };
+// (kFmtFP8QP: FP8 cache with FP8 Q and P on FP8 MFMA)
+enum : int { kFmtBF16 = 0, kFmtFP8 = 1, kFmtNVFP4 = 2, kFmtFP8QP = 3 };
 constexpr int kBlockSize = 16;
 
 struct DecodeArgs {
@@ -35,7 +36,8 @@ struct DecodeArgs {
     int max_blocks;
     int Hq, Hkv, G;
     int split_tokens, num_splits;
-    float qk_scale_log2;         // sm_scale * k_scale * log2(e)
+    float qk_scale_log2;         // sm_scale * k_scale * log2(e) (* q_scale for kFmtFP8QP)
+    float q_scale;               // kFmtFP8QP: Q quantization scale
     float v_scale;               // applied once in the merge
     int out_f32;
     int q_len;                   // queries per sequence (1: single-token decode)

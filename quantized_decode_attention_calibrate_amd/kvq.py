@@ -56,6 +56,8 @@ def _load() -> ctypes.CDLL:
         "kvq_nvfp4_paged_decode_attn_ex": (I, [P, P, P, P, I, P, I, I, I, I, I, I, I, F, F, F, P, I, P, SZ, P,
                                                I]),
         "kvq_e2m1_decode": (I, [P, ctypes.c_uint8, P, I64, P]),
+        "kvq_paged_decode_attn_fp8qp": (I, [P, I, I, P, P, P, I, P, I, I, I, I, I, I, I, F, F, F, F, P, I, P, SZ,
+                                            P, I]),
         "kvq_cache_block_bytes": (SZ, [I, I, I, I]),
         "kvq_gather_blocks": (I, [P, SZ, P, I, P, P]),
         "kvq_scatter_blocks": (I, [P, SZ, P, I, P, P]),
@@ -341,3 +343,18 @@ def kvq_restore_blocks(host_src: torch.Tensor, staging: torch.Tensor, block_byte
     assert host_src.device.type == "cpu" and host_src.is_contiguous()
     _check("kvq_restore_blocks", _lib.kvq_restore_blocks(_ptr(host_src), _ptr(staging), block_bytes, _ptr(ids), n,
                                                          _ptr(k_cache), _ptr(v_cache), _stream(stream)))
+
+
+# ---- FP8 Q and P variant ---------------------------------------------------------------
+
+def kvq_paged_decode_attn_fp8qp(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                block_tables: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, Hkv: int,
+                                q_scale: float, k_scale: float, v_scale: float, sm_scale: float, out: torch.Tensor,
+                                workspace: torch.Tensor, split_tokens: int = 0, window: int = 0, stream=None) -> None:
+    """FP8 cache, FP8 Q (q_scale) and FP8 P on FP8 MFMA; q [B][q_len][Hq][D] as kvq_paged_decode_attn_mq."""
+    B, q_len, Hq, D, out_dtype = _mq_args(q, block_tables, seq_lens, out)
+    _check("kvq_paged_decode_attn_fp8qp", _lib.kvq_paged_decode_attn_fp8qp(
+        _ptr(q), q_len, window, _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1],
+        _ptr(seq_lens), max_seq_len, B, Hq, Hkv, D, BLOCK_SIZE, k_cache.shape[0], q_scale, k_scale, v_scale,
+        sm_scale, _ptr(out), out_dtype, _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream), split_tokens))

@@ -195,3 +195,13 @@ def test_block_copy_host_validation(K):
     assert L.kvq_gather_blocks(FAKE, 8192, FAKE, 0, FAKE, None) == 0        # nothing to do, no HIP call
     assert L.kvq_offload_blocks(FAKE, FAKE, 8192, FAKE, 2, None, FAKE, None) == -1
     assert L.kvq_restore_blocks(FAKE, FAKE + 4, 8192, FAKE, 2, FAKE, FAKE, None) == -1
+
+
+def test_fp8qp_host_validation(K):
+    L = K.lib()
+
+    def call(qs, q_len=1, D=64):
+        return L.kvq_paged_decode_attn_fp8qp(FAKE, q_len, 0, FAKE, FAKE, FAKE, 8, FAKE, 100, 1, 16, 2, D, 16, 10,
+                                             qs, 1.0, 1.0, 0.125, FAKE, 0, FAKE, 1 << 30, None, 0)
+    assert call(0.0) == -1 and call(float("nan")) == -1 and call(-1.0) == -1
+    assert call(1.0, q_len=0) == -1 and call(1.0, q_len=9) == -2
