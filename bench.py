@@ -84,11 +84,16 @@ class Layers:
             self.ks, self.vs = cal(amax.cpu().tolist())
         else:
             self.ks, self.vs = 1.0, 1.0
-        rows = w.last_token_rows()
-        rows = rows[rows >= 0].to(dev)
+        all_rows = w.last_token_rows().to(dev)
+        rows = all_rows[all_rows >= 0]
         self.new_k = k[rows].contiguous()
         self.new_v = v[rows].contiguous()
         self.new_slots = w.slot_mapping.to(dev)[rows].contiguous()
+        # per sequence (slot -1 for an empty one) for the fused append call
+        safe = all_rows.clamp(min=0)
+        self.app_k, self.app_v = k[safe].contiguous(), v[safe].contiguous()
+        self.app_slots = torch.where(all_rows >= 0, w.slot_mapping.to(dev)[safe],
+                                     torch.full_like(all_rows, -1)).contiguous()
         self.caches = []
         pre = w.prefill_slots().to(dev)
         for _ in range(R):
@@ -113,6 +118,14 @@ class Layers:
             self.K.kvq_cache_write(self.new_k, self.new_v, self.new_slots, kc, vc, self.kv_dtype, self.ks,
                                    self.vs)
 
+    def append(self, i):
+        """The step as one call: the new token's cache write fused into the decode."""
+        kc, vc = self.caches[i % self.R]
+        w = self.w
+        self.K.kvq_paged_decode_attn_append(self.app_k, self.app_v, self.app_slots, self.q, kc, vc, self.kv_dtype,
+                                            self.bt, self.sl, w.max_seq_len, w.Hkv, self.ks, self.vs, self.sm,
+                                            self.out, self.ws)
+
     def attend(self, i, impl=0):
         kc, vc = self.caches[i % self.R]
         w = self.w
@@ -124,18 +137,25 @@ class Layers:
                                          self.ks, self.vs, self.sm, self.out, self.ws, impl=impl)
 
 
-def time_steps(torch, layers, steps, warmup, impl=0):
-    """Returns (ms per step, mean ms of the attention call alone), HIP events on the launch stream."""
+def time_steps(torch, layers, steps, warmup, impl=0, fused=False):
+    """Returns (ms per step, mean ms of the attention call alone), HIP events
+    on the launch stream.  A step is the new token's cache write and the
+    decode attention: one kvq_paged_decode_attn_append call (fused), or
+    kvq_cache_write then kvq_paged_decode_attn."""
+    def step(i):
+        if fused:
+            layers.append(i)
+        else:
+            layers.write(i)
+            layers.attend(i, impl)
     for i in range(warmup):
-        layers.write(i)
-        layers.attend(i, impl)
+        step(i)
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record(st)
     for i in range(steps):
-        layers.write(i)
-        layers.attend(i, impl)
+        step(i)
     t1.record(st)
     torch.cuda.synchronize()
     step_ms = t0.elapsed_time(t1) / steps
@@ -467,7 +487,9 @@ def main():
     pmc_reference(torch, K)
     fp8 = Layers(K, w, K.KVQ_KV_FP8_E4M3, args.layers, dev)
     print("[bench] timing FP8", file=sys.stderr, flush=True)
-    step_ms, attn_ms = time_steps(torch, fp8, args.steps, args.warmup, args.impl)
+    fused = args.impl != 1      # the fused append runs on the MFMA family
+    step_ms, attn_ms = time_steps(torch, fp8, args.steps, args.warmup, args.impl, fused=fused)
+    two_step_ms, _ = time_steps(torch, fp8, args.steps, args.warmup, args.impl, fused=False)
     attn_b, write_b = step_bytes(w.B, w.Hq, w.Hkv, w.D, w.seq_lens, 1, w.B)
     tokens = sum(w.seq_lens)
     gbps = (attn_b + write_b) / (step_ms * 1e-3) / 1e9
@@ -489,13 +511,15 @@ def main():
         "data": "synthetic (seeded N(0,1), 0.5% of K/V x10)",
         "config": {"workload": f"{args.workload}: B={w.B} x L={w.max_seq_len}, Hq={w.Hq}/Hkv={w.Hkv}, D={w.D}, "
                                f"block 16, FP8 E4M3 paged KV, {args.layers} layer caches rotated; step = "
-                               "cache write of the new token + decode attention",
+                               "cache write of the new token + decode attention"
+                               + (" (one kvq_paged_decode_attn_append call)" if fused else ""),
                    "B": w.B, "seq_len": w.max_seq_len, "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.D,
                    "kv_dtype": "fp8_e4m3", "layers_rotated": args.layers,
                    "split_tokens": K.kvq_decode_plan_split_tokens(w.B, w.Hkv, w.max_seq_len)},
         "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "kv_tokens_per_s": round(tokens / (step_ms * 1e-3), 1),
         "step_bytes": attn_b + write_b,
+        "two_launch_ms_per_step": round(two_step_ms, 6),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": "kvq_paged_decode_attn (split-K decode + merge), bytes per launch = "
@@ -508,7 +532,7 @@ def main():
         del fp8
         torch.cuda.empty_cache()
         bf = Layers(K, w, K.KVQ_KV_BF16, args.layers, dev)
-        b_step, b_attn = time_steps(torch, bf, args.steps, args.warmup, args.impl)
+        b_step, b_attn = time_steps(torch, bf, args.steps, args.warmup, args.impl, fused=fused)
         b_attn_b, _ = step_bytes(w.B, w.Hq, w.Hkv, w.D, w.seq_lens, 2, w.B)
         result["bf16_kv"] = {"ms_per_step": round(b_step, 6), "attn_ms_mean": round(b_attn, 6),
                              "attn_gbps": round(b_attn_b / (b_attn * 1e-3) / 1e9, 2)}

@@ -53,7 +53,8 @@
 extern "C" {
 #endif
 
-/* 2: multi-query and sliding-window decode, FP8 Q/P variant, host-memory block tier */
+/* 2: multi-query and sliding-window decode, FP8 Q/P variant, fused append,
+ *    host-memory block tier */
 #define KVQ_ABI_VERSION 2
 
 enum kvq_status {
@@ -186,6 +187,33 @@ int kvq_paged_decode_attn_ex(const void* q_dev, const void* k_cache_dev, const v
                              void* out_dev, int out_dtype,
                              void* workspace_dev, size_t workspace_bytes, void* hip_stream,
                              int impl, int split_tokens);
+
+/* kvq_paged_decode_attn_append: one decode step's cache write and attention
+ * in one launch, the same result as kvq_cache_write of each sequence's newest
+ * token (T = B) followed by kvq_paged_decode_attn (single query, FP8 or BF16,
+ * MFMA family).  It saves the separate write launch, which at one token per
+ * sequence is all fixed cost.
+ *   k_new_dev, v_new_dev  bf16 [B][Hkv][D]; row b starts at b * new_token_stride
+ *                         elements (as kvq_cache_write's source)
+ *   slot_mapping_dev      int64 [B]: slot of sequence b's newest token, which
+ *                         must be the slot of position seq_lens[b] - 1 in
+ *                         block_tables (it is the token the attention reads);
+ *                         < 0 writes nothing for b
+ *   the rest              as kvq_paged_decode_attn_ex (impl is MFMA)
+ * Each token is quantized and stored by the work-group that reads it (the one
+ * holding the sequence's last split for that KV head), before it reads it;
+ * no other work-group reads that block in the call.  A slot that is not the
+ * newest position's leaves the attention of that call undefined (a race with
+ * whichever work-group reads it); the bytes written are the same either way.
+ * Errors as kvq_cache_write and kvq_paged_decode_attn_ex. */
+int kvq_paged_decode_attn_append(const void* k_new_dev, const void* v_new_dev, int64_t new_token_stride,
+                                 const int64_t* slot_mapping_dev, const void* q_dev, void* k_cache_dev,
+                                 void* v_cache_dev, int kv_dtype, const int32_t* block_tables_dev,
+                                 int max_blocks_per_seq, const int32_t* seq_lens_dev, int max_seq_len,
+                                 int B, int Hq, int Hkv, int D, int block_size, int num_blocks,
+                                 float k_scale, float v_scale, float sm_scale, void* out_dev, int out_dtype,
+                                 void* workspace_dev, size_t workspace_bytes, void* hip_stream,
+                                 int split_tokens);
 
 /* Split length (tokens) the automatic plan picks for this shape. */
 int kvq_decode_plan_split_tokens(int B, int Hkv, int max_seq_len, int block_size);

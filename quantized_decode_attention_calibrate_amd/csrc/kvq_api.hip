@@ -197,13 +197,21 @@ static int plan_span(int max_seq_len, int q_len, int window) {
     return span < max_seq_len ? (int)span : max_seq_len;
 }
 
+// The newest token of each sequence for kvq_paged_decode_attn_append.
+struct AppendArgs {
+    const void* k_new;
+    const void* v_new;
+    int64_t stride;
+    const int64_t* slots;
+};
+
 static int decode_common(int fmt, const void* q_dev, int q_len, int window, const void* k_cache_dev,
                          const void* v_cache_dev,
                          const int32_t* block_tables_dev, int max_blocks_per_seq, const int32_t* seq_lens_dev,
                          int max_seq_len, int B, int Hq, int Hkv, int D, int block_size, int num_blocks,
                          float k_scale, float v_scale, float sm_scale, void* out_dev, int out_dtype,
                          void* workspace_dev, size_t workspace_bytes, void* hip_stream, int impl, int split_tokens,
-                         float q_scale = 1.0f) {
+                         float q_scale = 1.0f, const AppendArgs* app = nullptr) {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_seq_len < 0)
         return KVQ_EINVAL;
     if (q_len < 1 || q_len > kMaxQueryLen || window < 0) return KVQ_EINVAL;
@@ -235,7 +243,7 @@ static int decode_common(int fmt, const void* q_dev, int q_len, int window, cons
     if (impl == KVQ_IMPL_AUTO || fmt == kFmtNVFP4) impl = KVQ_IMPL_MFMA;
 
     const bool scaled = fmt != kFmtBF16;
-    DecodeArgs a;
+    DecodeArgs a = {};
     a.q = (const uint16_t*)q_dev;
     a.k_cache = (const uint8_t*)k_cache_dev;
     a.v_cache = (const uint8_t*)v_cache_dev;
@@ -258,6 +266,14 @@ static int decode_common(int fmt, const void* q_dev, int q_len, int window, cons
     a.out_f32 = out_dtype == KVQ_OUT_F32;
     a.q_len = q_len;
     a.window = window;
+    if (app) {
+        a.k_new = (const uint16_t*)app->k_new;
+        a.v_new = (const uint16_t*)app->v_new;
+        a.new_stride = app->stride;
+        a.new_slots = app->slots;
+        a.k_scale_w = k_scale;
+        a.v_scale_w = v_scale;
+    }
     return hip_status(launch_decode(a, B, D, fmt, impl, (hipStream_t)hip_stream));
 }
 
@@ -391,6 +407,26 @@ int kvq_restore_blocks(const void* host_src, void* staging_dev, size_t block_byt
     if (v != KVQ_OK) return v;
     return hip_status(launch_block_copy((const char*)staging_dev + half, v_cache_dev, block_ids_dev, n, block_bytes, 0,
                                         st));
+}
+
+int kvq_paged_decode_attn_append(const void* k_new_dev, const void* v_new_dev, int64_t new_token_stride,
+                                 const int64_t* slot_mapping_dev, const void* q_dev, void* k_cache_dev,
+                                 void* v_cache_dev, int kv_dtype, const int32_t* block_tables_dev,
+                                 int max_blocks_per_seq, const int32_t* seq_lens_dev, int max_seq_len, int B, int Hq,
+                                 int Hkv, int D, int block_size, int num_blocks, float k_scale, float v_scale,
+                                 float sm_scale, void* out_dev, int out_dtype, void* workspace_dev,
+                                 size_t workspace_bytes, void* hip_stream, int split_tokens) {
+    if (kv_dtype != KVQ_KV_BF16 && kv_dtype != KVQ_KV_FP8_E4M3) return KVQ_EINVAL;
+    if (B > 0) {
+        if (!k_new_dev || !v_new_dev || !slot_mapping_dev) return KVQ_EINVAL;
+        if (new_token_stride < (int64_t)Hkv * D || (new_token_stride & 7) != 0) return KVQ_EINVAL;
+        if (!aligned16(k_new_dev) || !aligned16(v_new_dev)) return KVQ_EINVAL;
+    }
+    const AppendArgs app = {k_new_dev, v_new_dev, new_token_stride, slot_mapping_dev};
+    return decode_common(kv_dtype == KVQ_KV_FP8_E4M3 ? kFmtFP8 : kFmtBF16, q_dev, 1, 0, k_cache_dev, v_cache_dev,
+                         block_tables_dev, max_blocks_per_seq, seq_lens_dev, max_seq_len, B, Hq, Hkv, D,
+                         block_size, num_blocks, k_scale, v_scale, sm_scale, out_dev, out_dtype, workspace_dev,
+                         workspace_bytes, hip_stream, KVQ_IMPL_MFMA, split_tokens, 1.0f, &app);
 }
 
 int kvq_paged_decode_attn_fp8qp(const void* q_dev, int q_len, int window, const void* k_cache_dev,

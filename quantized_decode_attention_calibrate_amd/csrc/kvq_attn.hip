@@ -572,7 +572,19 @@ __device__ __forceinline__ void process_chunk(MfmaState<D, NT>& st, MfmaChunk<D,
         mfma_process(st, c, qb, cs, cbeg, cend, chunk_tok, tok_end, tail_from, head_until, vbeg, grp);
 }
 
-template <int D, int FMT, int NT, int W = mfma_waves<D, FMT, NT>()>
+// Orders this wave's cache stores before its later loads of the same bytes:
+// at work-group scope it waits for the stores to complete.
+__device__ __forceinline__ void append_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup"); }
+
+// APPEND: the fused cache write of each sequence's newest token
+// (kvq_paged_decode_attn_append).  The token's block is read by one
+// work-group only, the one holding the sequence's last split for this KV
+// head, and within it by the wave whose round-robin share ends with the
+// chunk holding that token.  That wave quantizes the token and stores it
+// right after the block ids are staged, and before it loads that chunk it
+// waits for its own stores (a work-group-scope fence), so the chunk's loads
+// see the new bytes.
+template <int D, int FMT, int NT, int W = mfma_waves<D, FMT, NT>(), bool APPEND = false>
 __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
     constexpr int KJ = D / 64;
     constexpr int DT = D / 16;
@@ -602,6 +614,21 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
 
     const int lb0 = tok_begin / kBlockSize;
     const int n_chunks = (tok_end - tok_begin + kChunkTokens - 1) / kChunkTokens;
+    // fused append: the newest token's bf16 values, loaded early (consumed after the barrier)
+    const bool writer = APPEND && tok_end == L && wave == (n_chunks - 1) % W;
+    uint16_t k_new[D / 64], v_new[D / 64];
+    int64_t new_slot = -1;
+    if constexpr (APPEND) {
+        if (writer) {
+            new_slot = a.new_slots[b];
+            const int64_t row = (int64_t)b * a.new_stride + (int64_t)g * D;
+#pragma unroll
+            for (int r = 0; r < D / 64; ++r) {
+                k_new[r] = a.k_new[row + lane + 64 * r];
+                v_new[r] = a.v_new[row + lane + 64 * r];
+            }
+        }
+    }
     stage_block_ids(s_blk, a.block_tables + (int64_t)b * a.max_blocks, lb0, n_chunks * 4, sr.first / kBlockSize,
                     (L + kBlockSize - 1) / kBlockSize - 1);
 
@@ -680,6 +707,28 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
     const int tail_from = min(tok_end, q0_end);
     const int head_until = a.window > 0 ? max(0, L - a.window) : 0;   // the newest query's window start
     __syncthreads();
+    if constexpr (APPEND) {
+        if (writer && new_slot >= 0) {   // the cache write's quantizer, element by element
+            const int64_t blk = new_slot / kBlockSize;
+            const int off = (int)(new_slot - blk * kBlockSize);
+            uint8_t* kc = const_cast<uint8_t*>(a.k_cache);
+            uint8_t* vc = const_cast<uint8_t*>(a.v_cache);
+#pragma unroll
+            for (int r = 0; r < D / 64; ++r) {
+                const int d = lane + 64 * r;
+                const int64_t ki = ((blk * a.Hkv + g) * kBlockSize + off) * D + d;   // [blk][g][off][d]
+                const int64_t vi = ((blk * a.Hkv + g) * D + d) * kBlockSize + off;   // [blk][g][d][off]
+                if constexpr (FMT == kFmtFP8) {
+#pragma clang fp contract(off)
+                    kc[ki] = (uint8_t)e4m3_encode(bits_f32((uint32_t)k_new[r] << 16) / a.k_scale_w);
+                    vc[vi] = (uint8_t)e4m3_encode(bits_f32((uint32_t)v_new[r] << 16) / a.v_scale_w);
+                } else {
+                    reinterpret_cast<uint16_t*>(kc)[ki] = k_new[r];
+                    reinterpret_cast<uint16_t*>(vc)[vi] = v_new[r];
+                }
+            }
+        }
+    }
 
     MfmaState<D, NT> st;
 #pragma unroll
@@ -700,14 +749,17 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
         MfmaChunk<D, FMT> A, Bc;
         if (my > 0) {
             int ch = wave;
+            if (APPEND && writer && my == 1) append_fence();
             mfma_load(A, a, s_blk, ch, g, n, grp);
             for (int i = 0; i < my; i += 2) {
                 const int chb = i + 1 < my ? ch + W : ch;
+                if (APPEND && writer && i + 2 == my) append_fence();
                 mfma_load(Bc, a, s_blk, chb, g, n, grp);
                 process_chunk(st, A, qb, cs, cbeg, cend, tok_begin + ch * kChunkTokens, tok_end, tail_from,
                               head_until, sr.first, grp);
                 if (i + 1 >= my) break;
                 const int cha = i + 2 < my ? chb + W : chb;
+                if (APPEND && writer && i + 3 == my) append_fence();
                 mfma_load(A, a, s_blk, cha, g, n, grp);
                 process_chunk(st, Bc, qb, cs, cbeg, cend, tok_begin + chb * kChunkTokens, tok_end, tail_from,
                               head_until, sr.first, grp);
@@ -718,6 +770,7 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
         for (int i = 0; i < my; ++i) {
             const int ch = wave + i * W;
             MfmaChunk<D, FMT> A;
+            if (APPEND && writer && i + 1 == my) append_fence();
             mfma_load(A, a, s_blk, ch, g, n, grp);
             process_chunk(st, A, qb, cs, cbeg, cend, tok_begin + ch * kChunkTokens, tok_end, tail_from,
                           head_until, sr.first, grp);
@@ -1018,7 +1071,12 @@ static hipError_t launch_family(const DecodeArgs& a, int B, int impl, hipStream_
     constexpr int W = mfma_waves<D, FMT, NT>();
     const int GQ = a.G * a.q_len;
     const size_t lds_mfma = sizeof(float) * (kMaxSplitBlocks + lds_merge_floats(GQ, D, W, NT));
-    if (FMT == kFmtNVFP4 || FMT == kFmtFP8QP || impl == 2 || NT > 1) {
+    if (a.k_new) {   // fused append: single-query FP8 / BF16 on the MFMA family only
+        if constexpr ((FMT == kFmtFP8 || FMT == kFmtBF16) && NT == 1)
+            hipLaunchKernelGGL((decode_mfma_kernel<D, FMT, NT, W, true>), grid, dim3(W * 64), lds_mfma, st, a);
+        else
+            return hipErrorInvalidValue;
+    } else if (FMT == kFmtNVFP4 || FMT == kFmtFP8QP || impl == 2 || NT > 1) {
         hipLaunchKernelGGL((decode_mfma_kernel<D, FMT, NT>), grid, dim3(W * 64), lds_mfma, st, a);
     } else {
         if constexpr ((FMT == kFmtFP8 || FMT == kFmtBF16) && NT == 1) {

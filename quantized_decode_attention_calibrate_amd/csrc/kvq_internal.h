@@ -42,6 +42,15 @@ struct DecodeArgs {
     int out_f32;
     int q_len;                   // queries per sequence (1: single-token decode)
     int window;                  // > 0: each query sees its `window` newest tokens
+    // Fused append (k_new != nullptr): sequence b's newest token (position
+    // seq_lens[b] - 1) is quantized from bf16 rows k_new / v_new + b * new_stride
+    // + g * D and stored at new_slots[b] (< 0: not written) by the work-group
+    // that reads it, before it reads it.
+    const uint16_t* k_new;
+    const uint16_t* v_new;
+    int64_t new_stride;
+    const int64_t* new_slots;
+    float k_scale_w, v_scale_w;  // cache quantization scales of the write (FP8)
 };
 
 // Workspace: [ml: B*Hq*S*2 f32][acc: B*Hq*S*D f32], the second region starting

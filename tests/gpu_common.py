@@ -47,9 +47,11 @@ def gpu_calibrate(K, x: torch.Tensor) -> float:
 class Setup:
     """A workload on the GPU with its caches written by kvq_cache_write: the
     prefill (all tokens but each sequence's newest) in one call, then the
-    decode-step write of the newest token per sequence."""
+    decode-step write of the newest token per sequence (unless
+    write_newest=False, for the fused append path)."""
 
-    def __init__(self, w: workloads.Workload, kv_dtype: int, sentinel: int = 0xFF, scales=None):
+    def __init__(self, w: workloads.Workload, kv_dtype: int, sentinel: int = 0xFF, scales=None,
+                 write_newest: bool = True):
         K = kvq()
         self.K, self.w, self.kv_dtype = K, w, kv_dtype
         dev = "cuda"
@@ -76,7 +78,7 @@ class Setup:
             K.kvq_cache_write(self.k, self.v, pre, self.kc, self.vc, kv_dtype, self.ks, self.vs)
             rows = w.last_token_rows()
             rows = rows[rows >= 0].to(dev)
-            if rows.numel():
+            if rows.numel() and write_newest:
                 K.kvq_cache_write(self.k[rows], self.v[rows], slots[rows].contiguous(), self.kc, self.vc,
                                   kv_dtype, self.ks, self.vs)
         self.sm_scale = float(np.float32(1.0 / math.sqrt(w.D)))

@@ -205,3 +205,20 @@ def test_fp8qp_host_validation(K):
                                              qs, 1.0, 1.0, 0.125, FAKE, 0, FAKE, 1 << 30, None, 0)
     assert call(0.0) == -1 and call(float("nan")) == -1 and call(-1.0) == -1
     assert call(1.0, q_len=0) == -1 and call(1.0, q_len=9) == -2
+
+
+def test_append_host_validation(K):
+    """kvq_paged_decode_attn_append rejects bad arguments on the host, before
+    any HIP call (FAKE pointers are never dereferenced)."""
+    L = K.lib()
+
+    def call(kvd=1, stride=128, ks=1.0, k_new=FAKE, slots=FAKE, D=64, B=1):
+        return L.kvq_paged_decode_attn_append(k_new, FAKE, stride, slots, FAKE, FAKE, FAKE, kvd, FAKE, 8, FAKE, 100,
+                                              B, 16, 2, D, 16, 10, ks, 1.0, 0.125, FAKE, 0, FAKE, 1 << 30, None, 0)
+    assert call(kvd=2) == -1 and call(kvd=-1) == -1                    # FP8 or BF16 only
+    assert call(stride=120) == -1 and call(stride=132) == -1           # shorter than Hkv * D, not 8-aligned
+    assert call(k_new=None) == -1 and call(slots=None) == -1
+    assert call(k_new=FAKE + 8) == -1                                  # 16-byte aligned rows
+    assert call(ks=0.0) == -1 and call(ks=float("inf")) == -1
+    assert call(D=96, stride=192) == -2
+    assert call(B=0, k_new=None, slots=None) == 0                      # nothing to do
