@@ -1022,28 +1022,35 @@ __global__ void __launch_bounds__(kMergeThreads) merge_splits_kernel(DecodeArgs 
     __shared__ f32x4 part[P][C4];
     const int hq = blockIdx.x;                // output row (b * q_len + i) * Hq + h
     const int b = hq / (a.Hq * a.q_len);
-    const SeqRange sr = seq_range(a, b);
-    const int S = (sr.L - sr.base + a.split_tokens - 1) / a.split_tokens;
-    if (S <= 1) return;                       // written by the decode kernel
     const int t = threadIdx.x;
     const int d4 = t % C4, p = t / C4;
-    const float* ml = a.ws_ml + (int64_t)hq * a.num_splits * 2;
-    const f32x4* col = reinterpret_cast<const f32x4*>(a.ws_acc + (int64_t)hq * a.num_splits * D) + d4;
+    const int NS = a.num_splits;
+    const float* ml = a.ws_ml + (int64_t)hq * NS * 2;
+    const f32x4* col = reinterpret_cast<const f32x4*>(a.ws_acc + (int64_t)hq * NS * D) + d4;
+    // The first partial rows and (m, l) pairs are loaded before the sequence
+    // length is known (they lie inside the row's num_splits slots), so they
+    // are in flight together with seq_lens[b]; slots of splits past the
+    // sequence's last hold stale data and are masked once S is known.
     f32x4 pre[PRE];
 #pragma unroll
     for (int k = 0; k < PRE; ++k) {
         const int s = p + k * P;
-        pre[k] = s < S ? col[(int64_t)s * C4] : f32x4{0.f, 0.f, 0.f, 0.f};
+        pre[k] = s < NS ? col[(int64_t)s * C4] : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    float m = -INFINITY;
-    for (int s = t; s < S; s += kMergeThreads) m = fmaxf(m, ml[2 * s]);
+    const float m0 = t < NS ? ml[2 * t] : -INFINITY, l0 = t < NS ? ml[2 * t + 1] : 0.f;
+    const SeqRange sr = seq_range(a, b);
+    const int S = (sr.L - sr.base + a.split_tokens - 1) / a.split_tokens;
+    if (S <= 1) return;                       // written by the decode kernel
+    float m = t < S ? m0 : -INFINITY;
+    for (int s = t + kMergeThreads; s < S; s += kMergeThreads) m = fmaxf(m, ml[2 * s]);
     const float M = block_reduce(m, red, true);
     float den = 0.f;
     for (int s = t; s < S; s += kMergeThreads) {
         // M = -inf: no split saw a token for this row (a query before the start)
-        const float w = M == -INFINITY ? 0.f : fast_exp2(ml[2 * s] - M);
+        const float ms = s == t ? m0 : ml[2 * s], ls = s == t ? l0 : ml[2 * s + 1];
+        const float w = M == -INFINITY ? 0.f : fast_exp2(ms - M);
         s_w[s] = w;
-        den += w * ml[2 * s + 1];
+        den += w * ls;
     }
     den = block_reduce(den, red, false);       // its barriers also publish s_w
     f32x4 num = {0.f, 0.f, 0.f, 0.f};
