@@ -1,5 +1,7 @@
 """Full-size parity: every workload at its real shape, in the launch
-configuration the benchmark times (automatic split plan, MFMA family), checked
+configuration the benchmark times (automatic split plan, MFMA family; for
+gptoss65k also the one-call step kvq_paged_decode_attn_append that the
+benchmark times, where the decode kernel writes the newest tokens), checked
 on sampled (sequence, KV head) units that the oracle can afford:
 
 - the sampled head's paged K and V bytes (gathered through the block table)
@@ -39,7 +41,7 @@ def K():
     return kvq()
 
 
-def run_gpu(K, w, kv_dtype):
+def run_gpu(K, w, kv_dtype, fused=False):
     dev = "cuda"
     q, k, v = w.q, w.k, w.v
     if kv_dtype == K.KVQ_KV_FP8_E4M3:
@@ -51,28 +53,40 @@ def run_gpu(K, w, kv_dtype):
         ks, vs = 1.0, 1.0
     kc, vc = K.new_caches(kv_dtype, w.num_blocks, w.Hkv, w.D, device=dev)
     K.kvq_cache_write(k, v, w.prefill_slots(), kc, vc, kv_dtype, ks, vs)
-    rows = w.last_token_rows()
-    rows = rows[rows >= 0].to(dev)
-    K.kvq_cache_write(k[rows], v[rows], w.slot_mapping[rows].contiguous(), kc, vc, kv_dtype, ks, vs)
+    all_rows = w.last_token_rows().to(dev)
+    rows = all_rows[all_rows >= 0]
+    if not fused:
+        K.kvq_cache_write(k[rows], v[rows], w.slot_mapping[rows].contiguous(), kc, vc, kv_dtype, ks, vs)
     sl = torch.tensor(w.seq_lens, dtype=torch.int32, device=dev)
     ws = K.new_workspace(w.B, w.Hq, w.Hkv, w.D, w.max_seq_len)
     sm = float(np.float32(1.0 / math.sqrt(w.D)))
     outs = {}
     for dt in (torch.float32, torch.bfloat16):
         out = torch.empty(w.B, w.Hq, w.D, dtype=dt, device=dev)
-        K.kvq_paged_decode_attn(q, kc, vc, kv_dtype, w.block_tables, sl, w.max_seq_len, w.Hkv, ks, vs, sm, out, ws)
+        if fused:   # the decode step as one call: the newest tokens are written by the decode kernel
+            safe = all_rows.clamp(min=0)
+            slots = torch.where(all_rows >= 0, w.slot_mapping[safe], torch.full_like(all_rows, -1)).contiguous()
+            K.kvq_paged_decode_attn_append(k[safe].contiguous(), v[safe].contiguous(), slots, q, kc, vc, kv_dtype,
+                                           w.block_tables, sl, w.max_seq_len, w.Hkv, ks, vs, sm, out, ws)
+        else:
+            K.kvq_paged_decode_attn(q, kc, vc, kv_dtype, w.block_tables, sl, w.max_seq_len, w.Hkv, ks, vs, sm, out,
+                                    ws)
         outs[dt] = out
     torch.cuda.synchronize()
     return kc, vc, ks, vs, sm, outs
 
 
-@pytest.mark.parametrize("kv", [1, 0])
-@pytest.mark.parametrize("name", list(SAMPLES))
-def test_fullsize_sampled_units(K, name, kv):
+FULL_CASES = [(name, kv, False) for name in SAMPLES for kv in (1, 0)] + [
+    # the benchmark's step: one kvq_paged_decode_attn_append call
+    ("gptoss65k", 1, True), ("gptoss65k", 0, True), ("mixed64", 1, True)]
+
+
+@pytest.mark.parametrize("name,kv,fused", FULL_CASES)
+def test_fullsize_sampled_units(K, name, kv, fused):
     w = workloads.make(name, device="cuda", seed=0)
     say(f"full size {name}: B={w.B} L_max={w.max_seq_len} sum L={sum(w.seq_lens)} Hq={w.Hq} Hkv={w.Hkv} "
-        f"D={w.D} kv={kv} split={K.kvq_decode_plan_split_tokens(w.B, w.Hkv, w.max_seq_len)}")
-    kc, vc, ks, vs, sm, outs = run_gpu(K, w, kv)
+        f"D={w.D} kv={kv} fused={fused} split={K.kvq_decode_plan_split_tokens(w.B, w.Hkv, w.max_seq_len)}")
+    kc, vc, ks, vs, sm, outs = run_gpu(K, w, kv, fused)
     units = SAMPLES[name]
     if units is None:
         order = np.argsort(w.seq_lens)
@@ -107,7 +121,7 @@ def test_fullsize_sampled_units(K, name, kv):
         ref = oracle.decode_attn(qh, okc, ovc, kvd, np.arange(nblk, dtype=np.int32)[None, :], [L], 1, 16,
                                  ks, vs, sm, nthreads=min(G, 8))
         got = outs[torch.float32][b, g * G:(g + 1) * G].cpu().numpy()[None]
-        assert_attention_close(got, ref, f"{name} kv={kv} b={b} g={g}")
+        assert_attention_close(got, ref, f"{name} kv={kv} fused={fused} b={b} g={g}")
         o16 = outs[torch.bfloat16][b, g * G:(g + 1) * G].cpu()
         assert torch.equal(o16.view(torch.int16),
                            outs[torch.float32][b, g * G:(g + 1) * G].cpu().to(torch.bfloat16).view(torch.int16))
