@@ -152,13 +152,19 @@ def time_steps(torch, layers, steps, warmup, impl=0, fused=False):
         step(i)
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record(st)
+    # events at the ends of 5 equal blocks of the timed steps: the mean over all
+    # of them is the result, the blocks give its spread
+    nb = 5 if steps >= 5 else 1
+    marks = [round(steps * j / nb) for j in range(nb + 1)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in marks]
+    ev[0].record(st)
     for i in range(steps):
         step(i)
-    t1.record(st)
+        if i + 1 in marks[1:]:
+            ev[marks.index(i + 1)].record(st)
     torch.cuda.synchronize()
-    step_ms = t0.elapsed_time(t1) / steps
+    step_ms = ev[0].elapsed_time(ev[-1]) / steps
+    layers.spread = sorted(ev[j].elapsed_time(ev[j + 1]) / (marks[j + 1] - marks[j]) for j in range(nb))
     # the attention call alone (split kernel + merge kernel), back to back over
     # the rotated layer caches: its mean launch duration on the launch stream
     a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -339,6 +345,9 @@ def measure_workload(torch, K, name, steps, warmup, with_nvfp4=False):
         rec[tag] = {"attn_us": round(attn_ms * 1e3, 2), "attn_gbps": round(attn_b / (attn_ms * 1e-3) / 1e9, 1),
                     "pct_of_hbm_peak": round(100 * attn_b / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1),
                     "step_us": round(step_ms * 1e3, 2), "layers_rotated": L.R}
+        if kv != NVFP4:   # the step as one kvq_paged_decode_attn_append call
+            fstep, _ = time_steps(torch, L, steps, warmup, fused=True)
+            rec[tag]["step_one_call_us"] = round(fstep * 1e3, 2)
         del L
         torch.cuda.empty_cache()
     rec["fp8_over_bf16_attn_time"] = round(rec["fp8"]["attn_us"] / rec["bf16"]["attn_us"], 3)
@@ -350,7 +359,14 @@ def measure_workload(torch, K, name, steps, warmup, with_nvfp4=False):
     return rec
 
 
-def cpu_baseline(w, ks, vs, n_kv_heads):
+def env_info(torch):
+    """The run's software and device: HIP version torch was built with, the GPU and its compute units."""
+    p = torch.cuda.get_device_properties(0)
+    return {"torch": torch.__version__, "torch_hip": torch.version.hip, "device": p.name,
+            "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count}
+
+
+def cpu_baseline(w, ks, vs, n_kv_heads, threads=None):
     """The oracle (fp64 C, brute-force codecs) timed on this host's cores over a
     bounded sample: n_kv_heads KV heads (all their G query heads) of the
     workload's decode attention; scaled to the full step by Hkv / n_kv_heads.
@@ -365,7 +381,7 @@ def cpu_baseline(w, ks, vs, n_kv_heads):
     oracle.cache_write(sub_k, sub_v, w.slot_mapping, kc, vc, oracle.KV_FP8, ks, vs)
     q = w.q[:, :n_kv_heads * G, :].contiguous()
     cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
-    cores = max(1, min(cores, 16))
+    cores = max(1, min(cores, 16)) if threads is None else threads
     t = time.perf_counter()
     oracle.decode_attn(q, kc, vc, oracle.KV_FP8, w.block_tables, w.seq_lens, n_kv_heads, 16, ks, vs,
                        float(np.float32(1.0 / math.sqrt(w.D))), nthreads=cores)
@@ -497,6 +513,7 @@ def main():
     print("[bench] timing FP8", file=sys.stderr, flush=True)
     fused = args.impl != 1      # the fused append runs on the MFMA family
     step_ms, attn_ms = time_steps(torch, fp8, args.steps, args.warmup, args.impl, fused=fused)
+    fused_spread = fp8.spread
     two_step_ms, _ = time_steps(torch, fp8, args.steps, args.warmup, args.impl, fused=False)
     attn_b, write_b = step_bytes(w.B, w.Hq, w.Hkv, w.D, w.seq_lens, 1, w.B)
     tokens = sum(w.seq_lens)
@@ -531,6 +548,10 @@ def main():
         "kv_tokens_per_s": round(tokens / (step_ms * 1e-3), 1),
         "step_bytes": attn_b + write_b,
         "two_launch_ms_per_step": round(two_step_ms, 6),
+        "ms_per_step_blocks": {"blocks": len(fused_spread), "min": round(fused_spread[0], 6),
+                               "median": round(fused_spread[len(fused_spread) // 2], 6),
+                               "max": round(fused_spread[-1], 6)},
+        "env": env_info(torch),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": ("kvq_paged_decode_attn_append (split-K decode with the fused cache write + merge)"
@@ -579,6 +600,12 @@ def main():
                       f"x {tokens} tokens of one layer: {dt:.2f} s wall on {cores} threads (the step's "
                       "attention; the cache write is excluded)",
             "kv_tokens_per_s": round(tokens / step_s, 1)}
+        # one thread over one KV head (its units are independent, so it scales by Hkv)
+        s1, _, dt1 = cpu_baseline(w_cpu, ks, vs, n_kv_heads=1, threads=1)
+        result["cpu_baseline"]["single_thread"] = {
+            "value": round(attn_b / s1 / 1e9, 5), "unit": "GB/s",
+            "sample": f"1 of {w_cpu.Hkv} KV heads ({w_cpu.Hq // w_cpu.Hkv} query heads) x {tokens} tokens on one "
+                      f"thread: {dt1:.2f} s wall, scaled by {w_cpu.Hkv}"}
     print(json.dumps(result), flush=True)
 
 
