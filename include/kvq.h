@@ -198,7 +198,9 @@ int kvq_paged_decode_attn_ex(const void* q_dev, const void* k_cache_dev, const v
  *   slot_mapping_dev      int64 [B]: slot of sequence b's newest token, which
  *                         must be the slot of position seq_lens[b] - 1 in
  *                         block_tables (it is the token the attention reads);
- *                         < 0 writes nothing for b
+ *                         < 0 writes nothing for b, and neither does a
+ *                         sequence with seq_lens[b] == 0 (it has no newest
+ *                         token; pass -1)
  *   the rest              as kvq_paged_decode_attn_ex (impl is MFMA)
  * Each token is quantized and stored by the work-group that reads it (the one
  * holding the sequence's last split for that KV head), before it reads it;
