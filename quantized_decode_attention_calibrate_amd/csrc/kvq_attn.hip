@@ -1,5 +1,8 @@
-// kvq_attn.hip -- single-token split-K paged decode attention with the
-// dequantization fused into the attention kernel, and the cross-split merge.
+// kvq_attn.hip -- split-K paged decode attention with the dequantization
+// fused into the attention kernel, and the cross-split merge.  One kernel
+// template covers the FP8, BF16 and NVFP4 caches, multi-query decode (the
+// q_len newest tokens, each causal), sliding windows, the FP8 Q and P variant
+// and the fused cache write of each sequence's newest token.
 //
 // The Run 26 video description (Skildcore, "KV Cache Precision") states the
 // problem these kernels answer: each generated token reads the whole KV
