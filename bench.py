@@ -360,10 +360,33 @@ def measure_workload(torch, K, name, steps, warmup, with_nvfp4=False):
 
 
 def env_info(torch):
-    """The run's software and device: HIP version torch was built with, the GPU and its compute units."""
+    """The run's software and device: HIP version torch was built with, the
+    compiler, the GPU and its compute units, and a diagnostic streaming rate
+    (a 1 GiB device-to-device copy, read + write bytes over its time)."""
+    import subprocess
     p = torch.cuda.get_device_properties(0)
-    return {"torch": torch.__version__, "torch_hip": torch.version.hip, "device": p.name,
-            "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count}
+    try:
+        hipcc = subprocess.run(["/opt/rocm/bin/hipcc", "--version"], capture_output=True, text=True,
+                               timeout=30).stdout.strip().splitlines()[0]
+    except Exception:   # the compiler is optional at run time
+        hipcc = None
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    st = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(st)
+    for _ in range(10):
+        dst.copy_(src)
+    b.record(st)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * (1 << 30) * 10 / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"torch": torch.__version__, "torch_hip": torch.version.hip, "hipcc": hipcc, "device": p.name,
+            "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+            "copy_1gib_gbps": round(copy_gbps, 1)}
 
 
 def cpu_baseline(w, ks, vs, n_kv_heads, threads=None):
