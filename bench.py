@@ -122,9 +122,14 @@ class Layers:
         """The step as one call: the new token's cache write fused into the decode."""
         kc, vc = self.caches[i % self.R]
         w = self.w
-        self.K.kvq_paged_decode_attn_append(self.app_k, self.app_v, self.app_slots, self.q, kc, vc, self.kv_dtype,
-                                            self.bt, self.sl, w.max_seq_len, w.Hkv, self.ks, self.vs, self.sm,
-                                            self.out, self.ws)
+        if self.nvfp4:
+            self.K.kvq_nvfp4_paged_decode_attn_append(self.app_k, self.app_v, self.app_slots, self.q, kc, vc,
+                                                      self.bt, self.sl, w.max_seq_len, w.Hkv, self.ks, self.vs,
+                                                      self.sm, self.out, self.ws)
+        else:
+            self.K.kvq_paged_decode_attn_append(self.app_k, self.app_v, self.app_slots, self.q, kc, vc,
+                                                self.kv_dtype, self.bt, self.sl, w.max_seq_len, w.Hkv, self.ks,
+                                                self.vs, self.sm, self.out, self.ws)
 
     def attend(self, i, impl=0):
         kc, vc = self.caches[i % self.R]
@@ -345,9 +350,8 @@ def measure_workload(torch, K, name, steps, warmup, with_nvfp4=False):
         rec[tag] = {"attn_us": round(attn_ms * 1e3, 2), "attn_gbps": round(attn_b / (attn_ms * 1e-3) / 1e9, 1),
                     "pct_of_hbm_peak": round(100 * attn_b / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1),
                     "step_us": round(step_ms * 1e3, 2), "layers_rotated": L.R}
-        if kv != NVFP4:   # the step as one kvq_paged_decode_attn_append call
-            fstep, _ = time_steps(torch, L, steps, warmup, fused=True)
-            rec[tag]["step_one_call_us"] = round(fstep * 1e3, 2)
+        fstep, _ = time_steps(torch, L, steps, warmup, fused=True)   # the step as one call
+        rec[tag]["step_one_call_us"] = round(fstep * 1e3, 2)
         del L
         torch.cuda.empty_cache()
     rec["fp8_over_bf16_attn_time"] = round(rec["fp8"]["attn_us"] / rec["bf16"]["attn_us"], 3)

@@ -268,6 +268,21 @@ int kvq_nvfp4_paged_decode_attn_ex(const void* q_dev, const void* k_cache_dev, c
                                    void* workspace_dev, size_t workspace_bytes, void* hip_stream,
                                    int split_tokens);
 
+/* The NVFP4 decode step in one launch: kvq_nvfp4_cache_write of each
+ * sequence's newest token followed by kvq_nvfp4_paged_decode_attn, with the
+ * arguments and preconditions of kvq_paged_decode_attn_append (k_gscale /
+ * v_gscale in place of the FP8 scales).  The token's V code bytes also hold
+ * the nibble of the other slot of its pair, which is kept. */
+int kvq_nvfp4_paged_decode_attn_append(const void* k_new_dev, const void* v_new_dev, int64_t new_token_stride,
+                                       const int64_t* slot_mapping_dev, const void* q_dev, void* k_cache_dev,
+                                       void* v_cache_dev, const int32_t* block_tables_dev,
+                                       int max_blocks_per_seq, const int32_t* seq_lens_dev, int max_seq_len,
+                                       int B, int Hq, int Hkv, int D, int block_size, int num_blocks,
+                                       float k_gscale, float v_gscale, float sm_scale,
+                                       void* out_dev, int out_dtype,
+                                       void* workspace_dev, size_t workspace_bytes, void* hip_stream,
+                                       int split_tokens);
+
 /* ---- multi-query and sliding-window decode ---------------------------------
  * The verification step of speculative decoding (multi-token prediction and
  * draft models on the Radiance spec-decode campaign page, the DFlash and MTP

@@ -429,6 +429,25 @@ int kvq_paged_decode_attn_append(const void* k_new_dev, const void* v_new_dev, i
                          workspace_bytes, hip_stream, KVQ_IMPL_MFMA, split_tokens, 1.0f, &app);
 }
 
+int kvq_nvfp4_paged_decode_attn_append(const void* k_new_dev, const void* v_new_dev, int64_t new_token_stride,
+                                       const int64_t* slot_mapping_dev, const void* q_dev, void* k_cache_dev,
+                                       void* v_cache_dev, const int32_t* block_tables_dev, int max_blocks_per_seq,
+                                       const int32_t* seq_lens_dev, int max_seq_len, int B, int Hq, int Hkv, int D,
+                                       int block_size, int num_blocks, float k_gscale, float v_gscale,
+                                       float sm_scale, void* out_dev, int out_dtype, void* workspace_dev,
+                                       size_t workspace_bytes, void* hip_stream, int split_tokens) {
+    if (B > 0) {
+        if (!k_new_dev || !v_new_dev || !slot_mapping_dev) return KVQ_EINVAL;
+        if (new_token_stride < (int64_t)Hkv * D || (new_token_stride & 7) != 0) return KVQ_EINVAL;
+        if (!aligned16(k_new_dev) || !aligned16(v_new_dev)) return KVQ_EINVAL;
+    }
+    const AppendArgs app = {k_new_dev, v_new_dev, new_token_stride, slot_mapping_dev};
+    return decode_common(kFmtNVFP4, q_dev, 1, 0, k_cache_dev, v_cache_dev, block_tables_dev, max_blocks_per_seq,
+                         seq_lens_dev, max_seq_len, B, Hq, Hkv, D, block_size, num_blocks, k_gscale, v_gscale,
+                         sm_scale, out_dev, out_dtype, workspace_dev, workspace_bytes, hip_stream, KVQ_IMPL_MFMA,
+                         split_tokens, 1.0f, &app);
+}
+
 int kvq_paged_decode_attn_fp8qp(const void* q_dev, int q_len, int window, const void* k_cache_dev,
                                 const void* v_cache_dev, const int32_t* block_tables_dev, int max_blocks_per_seq,
                                 const int32_t* seq_lens_dev, int max_seq_len, int B, int Hq, int Hkv, int D,

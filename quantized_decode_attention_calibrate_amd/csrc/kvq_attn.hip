@@ -619,16 +619,26 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
     const int n_chunks = (tok_end - tok_begin + kChunkTokens - 1) / kChunkTokens;
     // fused append: the newest token's bf16 values, loaded early (consumed after the barrier)
     const bool writer = APPEND && tok_end == L && wave == (n_chunks - 1) % W;
-    uint16_t k_new[D / 64], v_new[D / 64];
+    constexpr int NG = D / 16;                 // NVFP4 blocks per (token, head) row
+    uint16_t k_new[D / 64], v_new[D / 64];     // FP8 / BF16: dims lane + 64 r
+    u32x4 n_w0 = {}, n_w1 = {};                // NVFP4: lane < NG: K block lane; lane < 2 NG: V block lane - NG
     int64_t new_slot = -1;
     if constexpr (APPEND) {
         if (writer) {
             new_slot = a.new_slots[b];
             const int64_t row = (int64_t)b * a.new_stride + (int64_t)g * D;
+            if constexpr (FMT == kFmtNVFP4) {
+                if (lane < 2 * NG) {
+                    const uint16_t* src = (lane < NG ? a.k_new : a.v_new) + row + 16 * (lane % NG);
+                    n_w0 = *reinterpret_cast<const u32x4*>(src);
+                    n_w1 = *reinterpret_cast<const u32x4*>(src + 8);
+                }
+            } else {
 #pragma unroll
-            for (int r = 0; r < D / 64; ++r) {
-                k_new[r] = a.k_new[row + lane + 64 * r];
-                v_new[r] = a.v_new[row + lane + 64 * r];
+                for (int r = 0; r < D / 64; ++r) {
+                    k_new[r] = a.k_new[row + lane + 64 * r];
+                    v_new[r] = a.v_new[row + lane + 64 * r];
+                }
             }
         }
     }
@@ -716,18 +726,47 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
             const int off = (int)(new_slot - blk * kBlockSize);
             uint8_t* kc = const_cast<uint8_t*>(a.k_cache);
             uint8_t* vc = const_cast<uint8_t*>(a.v_cache);
+            if constexpr (FMT == kFmtNVFP4) {
+                // one lane per block: K codes are a whole token row; a V code byte holds
+                // this token's nibble and the other slot's of the pair, which this
+                // work-group alone touches in the call, so it is read, merged and stored
+                constexpr int64_t region = 9 * D, code_bytes = 8 * D;
+                if (lane < 2 * NG) {
+                    const int gb = lane % NG;
+                    uint32_t codes[16], bcode;
+                    nvfp4_quantize_group(n_w0, n_w1, lane < NG ? a.k_scale_w : a.v_scale_w, codes, &bcode);
+                    if (lane < NG) {
+                        uint8_t* kr = kc + (blk * a.Hkv + g) * region;
+                        u32x2 packed = {0u, 0u};
 #pragma unroll
-            for (int r = 0; r < D / 64; ++r) {
-                const int d = lane + 64 * r;
-                const int64_t ki = ((blk * a.Hkv + g) * kBlockSize + off) * D + d;   // [blk][g][off][d]
-                const int64_t vi = ((blk * a.Hkv + g) * D + d) * kBlockSize + off;   // [blk][g][d][off]
-                if constexpr (FMT == kFmtFP8) {
+                        for (int j = 0; j < 16; ++j) packed[j >> 3] |= codes[j] << (4 * (j & 7));
+                        *reinterpret_cast<u32x2*>(kr + (int64_t)off * (D / 2) + gb * 8) = packed;
+                        kr[code_bytes + (int64_t)off * NG + gb] = (uint8_t)bcode;
+                    } else {
+                        uint8_t* vr = vc + (blk * a.Hkv + g) * region;
+                        vr[code_bytes + (int64_t)gb * kBlockSize + off] = (uint8_t)bcode;
+                        const uint32_t sh = 4u * (uint32_t)(off & 1);
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) {
+                            uint8_t* pb = vr + (int64_t)(16 * gb + j) * (kBlockSize / 2) + (off >> 1);
+                            *pb = (uint8_t)(((uint32_t)*pb & ~(0xFu << sh)) | (codes[j] << sh));
+                        }
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < D / 64; ++r) {
+                    const int d = lane + 64 * r;
+                    const int64_t ki = ((blk * a.Hkv + g) * kBlockSize + off) * D + d;   // [blk][g][off][d]
+                    const int64_t vi = ((blk * a.Hkv + g) * D + d) * kBlockSize + off;   // [blk][g][d][off]
+                    if constexpr (FMT == kFmtFP8) {
 #pragma clang fp contract(off)
-                    kc[ki] = (uint8_t)e4m3_encode(bits_f32((uint32_t)k_new[r] << 16) / a.k_scale_w);
-                    vc[vi] = (uint8_t)e4m3_encode(bits_f32((uint32_t)v_new[r] << 16) / a.v_scale_w);
-                } else {
-                    reinterpret_cast<uint16_t*>(kc)[ki] = k_new[r];
-                    reinterpret_cast<uint16_t*>(vc)[vi] = v_new[r];
+                        kc[ki] = (uint8_t)e4m3_encode(bits_f32((uint32_t)k_new[r] << 16) / a.k_scale_w);
+                        vc[vi] = (uint8_t)e4m3_encode(bits_f32((uint32_t)v_new[r] << 16) / a.v_scale_w);
+                    } else {
+                        reinterpret_cast<uint16_t*>(kc)[ki] = k_new[r];
+                        reinterpret_cast<uint16_t*>(vc)[vi] = v_new[r];
+                    }
                 }
             }
         }
@@ -1081,8 +1120,8 @@ static hipError_t launch_family(const DecodeArgs& a, int B, int impl, hipStream_
     constexpr int W = mfma_waves<D, FMT, NT>();
     const int GQ = a.G * a.q_len;
     const size_t lds_mfma = sizeof(float) * (kMaxSplitBlocks + lds_merge_floats(GQ, D, W, NT));
-    if (a.k_new) {   // fused append: single-query FP8 / BF16 on the MFMA family only
-        if constexpr ((FMT == kFmtFP8 || FMT == kFmtBF16) && NT == 1)
+    if (a.k_new) {   // fused append: single-query FP8 / BF16 / NVFP4 on the MFMA family only
+        if constexpr ((FMT == kFmtFP8 || FMT == kFmtBF16 || FMT == kFmtNVFP4) && NT == 1)
             hipLaunchKernelGGL((decode_mfma_kernel<D, FMT, NT, W, true>), grid, dim3(W * 64), lds_mfma, st, a);
         else
             return hipErrorInvalidValue;

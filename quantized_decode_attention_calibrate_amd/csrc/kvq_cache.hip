@@ -252,33 +252,6 @@ hipError_t launch_cache_write(const void* k, const void* v, int64_t src_stride, 
 // lane of the even slot stores the whole byte when the odd slot's token is in
 // the same window (the usual case for a prefill); a nibble whose partner is
 // not is merged into its 32-bit word with atomicAnd / atomicOr on its own bits.
-__device__ __forceinline__ void nvfp4_quantize_group(const u32x4& w0, const u32x4& w1, float gscale,
-                                                     uint32_t* codes, uint32_t* bcode) {
-#pragma clang fp contract(off)
-    float xf[16];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        xf[2 * j] = bf16_lo(w0[j]);
-        xf[2 * j + 1] = bf16_hi(w0[j]);
-        xf[8 + 2 * j] = bf16_lo(w1[j]);
-        xf[8 + 2 * j + 1] = bf16_hi(w1[j]);
-    }
-    float bamax = 0.f;
-    bool nan = false;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const float a = __builtin_fabsf(xf[j]);
-        nan |= __builtin_isnan(a);
-        bamax = a > bamax ? a : bamax;
-    }
-    if (nan) bamax = __builtin_nanf("");
-    const float top = 6.0f * gscale;
-    *bcode = e4m3_encode(bamax / top);
-    const float e = e4m3x2_to_f32(*bcode, false)[0] * gscale;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) codes[j] = e == 0.0f ? 0u : e2m1_encode(xf[j] / e);
-}
-
 __global__ void __launch_bounds__(kWriteThreads) nvfp4_cache_write_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t src_stride,
     const int64_t* __restrict__ slot_mapping, int T, int Hkv, int D, uint8_t* __restrict__ k_cache,

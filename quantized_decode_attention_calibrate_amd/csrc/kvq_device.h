@@ -110,6 +110,39 @@ __device__ __forceinline__ f16x8 e2m1x8_scaled_f16(uint32_t w, _Float16 scale) {
     return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// One NVFP4 block: 16 bf16 elements (two 16-byte words, element order) with
+// the tensor's global scale -> 16 E2M1 codes (one per word of `codes`) and the
+// E4M3 block-scale code.  bscale = E4M3(block amax / fp32(6 * gscale)),
+// e = fp32(value(bscale) * gscale), codes E2M1(x / e) (all zero when e == 0);
+// a NaN element makes the block scale NaN.  Shared by the cache write and the
+// decode kernel's fused append, so both store the same bytes.
+__device__ __forceinline__ void nvfp4_quantize_group(const u32x4& w0, const u32x4& w1, float gscale,
+                                                     uint32_t* codes, uint32_t* bcode) {
+#pragma clang fp contract(off)
+    float xf[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        xf[2 * j] = bf16_lo(w0[j]);
+        xf[2 * j + 1] = bf16_hi(w0[j]);
+        xf[8 + 2 * j] = bf16_lo(w1[j]);
+        xf[8 + 2 * j + 1] = bf16_hi(w1[j]);
+    }
+    float bamax = 0.f;
+    bool nan = false;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const float a = __builtin_fabsf(xf[j]);
+        nan |= __builtin_isnan(a);
+        bamax = a > bamax ? a : bamax;
+    }
+    if (nan) bamax = __builtin_nanf("");
+    const float top = 6.0f * gscale;
+    *bcode = e4m3_encode(bamax / top);
+    const float e = e4m3x2_to_f32(*bcode, false)[0] * gscale;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) codes[j] = e == 0.0f ? 0u : e2m1_encode(xf[j] / e);
+}
+
 // ---- wave helpers ----------------------------------------------------------
 __device__ __forceinline__ float shfl_xor(float v, int mask) {
     int lane = __lane_id();

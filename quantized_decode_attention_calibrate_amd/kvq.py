@@ -60,6 +60,8 @@ def _load() -> ctypes.CDLL:
                                             P, I]),
         "kvq_paged_decode_attn_append": (I, [P, P, I64, P, P, P, P, I, P, I, P, I, I, I, I, I, I, I, F, F, F, P, I,
                                              P, SZ, P, I]),
+        "kvq_nvfp4_paged_decode_attn_append": (I, [P, P, I64, P, P, P, P, P, I, P, I, I, I, I, I, I, I, F, F, F, P,
+                                                   I, P, SZ, P, I]),
         "kvq_cache_block_bytes": (SZ, [I, I, I, I]),
         "kvq_gather_blocks": (I, [P, SZ, P, I, P, P]),
         "kvq_scatter_blocks": (I, [P, SZ, P, I, P, P]),
@@ -181,6 +183,31 @@ def kvq_nvfp4_paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache:
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens),
         max_seq_len, B, Hq, Hkv, D, BLOCK_SIZE, k_cache.shape[0], k_gscale, v_gscale, sm_scale, _ptr(out),
         out_dtype, _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream), split_tokens))
+
+
+def kvq_nvfp4_paged_decode_attn_append(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+                                       q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                       block_tables: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                                       Hkv: int, k_gscale: float, v_gscale: float, sm_scale: float,
+                                       out: torch.Tensor, workspace: torch.Tensor, split_tokens: int = 0,
+                                       stream=None) -> None:
+    """kvq_nvfp4_cache_write of each sequence's newest token followed by
+    kvq_nvfp4_paged_decode_attn, in one launch (arguments as
+    kvq_paged_decode_attn_append, with the global scales)."""
+    B, Hq, D = q.shape
+    assert q.dtype == torch.bfloat16 and q.is_contiguous() and out.is_contiguous() and out.shape == q.shape
+    assert k_new.dtype == torch.bfloat16 and v_new.dtype == torch.bfloat16 and slot_mapping.dtype == torch.int64
+    assert k_new.shape == (B, Hkv, D) and v_new.shape == k_new.shape and k_new.stride(0) == v_new.stride(0)
+    assert k_new.stride(2) == 1 and k_new.stride(1) == D and v_new.stride(2) == 1 and v_new.stride(1) == D
+    assert slot_mapping.shape == (B,) and slot_mapping.is_contiguous()
+    assert block_tables.dtype == torch.int32 and block_tables.is_contiguous() and block_tables.shape[0] == B
+    assert seq_lens.dtype == torch.int32 and seq_lens.shape == (B,)
+    out_dtype = {torch.bfloat16: KVQ_OUT_BF16, torch.float32: KVQ_OUT_F32}[out.dtype]
+    _check("kvq_nvfp4_paged_decode_attn_append", _lib.kvq_nvfp4_paged_decode_attn_append(
+        _ptr(k_new), _ptr(v_new), k_new.stride(0), _ptr(slot_mapping), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+        _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), max_seq_len, B, Hq, Hkv, D, BLOCK_SIZE,
+        k_cache.shape[0], k_gscale, v_gscale, sm_scale, _ptr(out), out_dtype, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream), split_tokens))
 
 
 def kvq_e2m1_decode(codes: torch.Tensor, scale_code: int, out: torch.Tensor, stream=None) -> None:

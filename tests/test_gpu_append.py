@@ -9,15 +9,19 @@ attention is within the path's tolerance of the oracle's.  Also checked
 against the two-launch path on the same inputs (kvq_cache_write then
 kvq_paged_decode_attn): the same cache bytes and bit-identical outputs.
 Shapes cover D 64 / 128 / 256, newest tokens at every position class in a
-chunk (first, last, mid-block, a whole multiple of the chunk), one- and
-many-split plans, an empty sequence, and a sequence whose slot is -1."""
+chunk (first, last, mid-block, a whole multiple of the chunk; odd and even
+slots, which matters for NVFP4's shared V code bytes), one- and many-split
+plans, an empty sequence, and a sequence whose slot is -1, for FP8, BF16 and
+NVFP4 caches."""
 import numpy as np
 import pytest
 import torch
 
+import oracle
 from quantized_decode_attention_calibrate_amd import workloads
 
 from gpu_common import Setup, assert_attention_close, bits_u8, gpu_or_skip, kvq, say
+from test_gpu_nvfp4 import NvSetup
 
 pytestmark = pytest.mark.gpu
 
@@ -51,19 +55,47 @@ def append_call(K, s, k_new, v_new, slots, split, kc=None, vc=None):
     w = s.w
     out = torch.empty(w.B, w.Hq, w.D, dtype=torch.float32, device="cuda")
     ws = K.new_workspace(w.B, w.Hq, w.Hkv, w.D, w.max_seq_len, split)
-    K.kvq_paged_decode_attn_append(k_new, v_new, slots, s.q, s.kc if kc is None else kc, s.vc if vc is None else vc,
-                                   s.kv_dtype, s.bt, s.sl, w.max_seq_len, w.Hkv, s.ks, s.vs, s.sm_scale, out, ws,
-                                   split_tokens=split)
+    if isinstance(s, NvSetup):
+        sl = torch.tensor(w.seq_lens, dtype=torch.int32, device="cuda")
+        K.kvq_nvfp4_paged_decode_attn_append(k_new, v_new, slots, w.q.cuda(), s.kc, s.vc, w.block_tables.cuda(),
+                                             sl, w.max_seq_len, w.Hkv, s.gk, s.gv, s.sm, out, ws, split_tokens=split)
+    else:
+        K.kvq_paged_decode_attn_append(k_new, v_new, slots, s.q, s.kc if kc is None else kc,
+                                       s.vc if vc is None else vc, s.kv_dtype, s.bt, s.sl, w.max_seq_len, w.Hkv,
+                                       s.ks, s.vs, s.sm_scale, out, ws, split_tokens=split)
     torch.cuda.synchronize()
     return out
 
 
-@pytest.mark.parametrize("kv", [1, 0], ids=["fp8", "bf16"])
+def nvfp4_oracle(s):
+    """The oracle's NVFP4 caches of every token and its attention over them."""
+    w = s.w
+    okc, ovc = oracle.new_caches(oracle.KV_NVFP4, w.num_blocks, w.Hkv, w.D, 16, fill=0xFF)
+    oracle.nvfp4_cache_write(w.k, w.v, w.slot_mapping, okc, ovc, 16, s.gk, s.gv)
+    ref = oracle.decode_attn(w.q, okc, ovc, oracle.KV_NVFP4, w.block_tables, w.seq_lens, w.Hkv, 16, s.gk, s.gv,
+                             s.sm, nthreads=8)
+    return okc, ovc, ref
+
+
+@pytest.mark.parametrize("kv", [1, 0, 2], ids=["fp8", "bf16", "nvfp4"])
 @pytest.mark.parametrize("case", range(len(CASES)))
 def test_append_matches_oracle_and_two_launches(K, case, kv):
     name, seed, lens, shape, split = CASES[case]
     w = workloads.make(name, seed=seed, seq_lens=lens, shape=shape)
     say(f"append case {case} kv={kv}: lens={lens} Hq={w.Hq} Hkv={w.Hkv} D={w.D} split={split}")
+    if kv == 2:
+        fused = NvSetup(K, w, write_newest=False)
+        two = NvSetup(K, w, scales=(fused.gk, fused.gv), write_newest=False)
+        k_new, v_new, slots = newest(w)
+        got = append_call(K, fused, k_new, v_new, slots, split).cpu().numpy()
+        okc, ovc, ref = nvfp4_oracle(fused)
+        assert np.array_equal(fused.kc.cpu().numpy(), okc) and np.array_equal(fused.vc.cpu().numpy(), ovc)
+        assert_attention_close(got, ref, f"append case {case} nvfp4")
+        K.kvq_nvfp4_cache_write(k_new, v_new, slots, two.kc, two.vc, two.gk, two.gv)
+        out2 = two.attend(torch.float32, split_tokens=split).cpu().numpy()
+        assert torch.equal(two.kc, fused.kc) and torch.equal(two.vc, fused.vc)
+        assert np.array_equal(got.view(np.uint32), out2.view(np.uint32))
+        return
     fused = Setup(w, kv, write_newest=False)
     two = Setup(w, kv, scales=(fused.ks, fused.vs), write_newest=False)
     k_new, v_new, slots = newest(w)

@@ -125,7 +125,7 @@ CASES = [
 
 
 class NvSetup:
-    def __init__(self, K, w, scales=None):
+    def __init__(self, K, w, scales=None, write_newest=True):
         self.K, self.w = K, w
         self.gk, self.gv = scales if scales is not None else gpu_gscales(K, w)
         self.kc, self.vc = K.new_nvfp4_caches(w.num_blocks, w.Hkv, w.D)
@@ -134,8 +134,9 @@ class NvSetup:
         K.kvq_nvfp4_cache_write(w.k.cuda(), w.v.cuda(), w.prefill_slots().cuda(), self.kc, self.vc, self.gk, self.gv)
         rows = w.last_token_rows()
         rows = rows[rows >= 0]
-        K.kvq_nvfp4_cache_write(w.k[rows].cuda(), w.v[rows].cuda(), w.slot_mapping[rows].contiguous().cuda(),
-                                self.kc, self.vc, self.gk, self.gv)
+        if write_newest:
+            K.kvq_nvfp4_cache_write(w.k[rows].cuda(), w.v[rows].cuda(), w.slot_mapping[rows].contiguous().cuda(),
+                                    self.kc, self.vc, self.gk, self.gv)
         self.sm = float(np.float32(1.0 / math.sqrt(w.D)))
 
     def attend(self, dtype=torch.float32, split_tokens=0, bt=None):
