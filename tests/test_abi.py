@@ -222,3 +222,17 @@ def test_append_host_validation(K):
     assert call(ks=0.0) == -1 and call(ks=float("inf")) == -1
     assert call(D=96, stride=192) == -2
     assert call(B=0, k_new=None, slots=None) == 0                      # nothing to do
+
+
+def test_nvfp4_append_host_validation(K):
+    L = K.lib()
+
+    def call(stride=128, gs=1.0, k_new=FAKE, slots=FAKE, D=64, B=1):
+        return L.kvq_nvfp4_paged_decode_attn_append(k_new, FAKE, stride, slots, FAKE, FAKE, FAKE, FAKE, 8, FAKE,
+                                                    100, B, 16, 2, D, 16, 10, gs, 1.0, 0.125, FAKE, 0, FAKE,
+                                                    1 << 30, None, 0)
+    assert call(stride=120) == -1 and call(stride=132) == -1
+    assert call(k_new=None) == -1 and call(slots=None) == -1 and call(k_new=FAKE + 8) == -1
+    assert call(gs=0.0) == -1 and call(gs=float("nan")) == -1
+    assert call(D=96, stride=192) == -2
+    assert call(B=0, k_new=None, slots=None) == 0
