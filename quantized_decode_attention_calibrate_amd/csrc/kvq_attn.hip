@@ -593,7 +593,8 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
     constexpr int DT = D / 16;
     constexpr int CP = 16 * NT;   // padded columns
     // two chunks in flight per wave where the registers allow it (measured
-    // faster than one for every D <= 128 shape, single and multi-query)
+    // faster than one for every D <= 128 shape, single and multi-query; a
+    // ring of three or four chunks was measured slower at D 64)
     constexpr bool kPrefetch = D <= 128;
     extern __shared__ float lds[];
     int* s_blk = reinterpret_cast<int*>(lds);
