@@ -576,8 +576,16 @@ __device__ __forceinline__ void process_chunk(MfmaState<D, NT>& st, MfmaChunk<D,
 }
 
 // Orders this wave's cache stores before its later loads of the same bytes:
-// at work-group scope it waits for the stores to complete.
-__device__ __forceinline__ void append_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup"); }
+// a work-group-scope fence, plus an explicit wait for every outstanding
+// memory operation of the wave (stores included), so the stores have reached
+// L2 before the chunk's loads are issued.  No other wave has loaded those
+// lines in this kernel, so the loads cannot hit a stale L1 copy.  Waiting here
+// costs nothing measurable: the only loads still in flight are the previous
+// chunk's, which the wave needs next anyway.
+__device__ __forceinline__ void append_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
+}
 
 // APPEND: the fused cache write of each sequence's newest token
 // (kvq_paged_decode_attn_append).  The token's block is read by one
