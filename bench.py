@@ -108,38 +108,52 @@ class Layers:
         self.out = torch.empty(w.B, w.Hq, w.D, dtype=torch.bfloat16, device=dev)
         self.ws = K.new_workspace(w.B, w.Hq, w.Hkv, w.D, w.max_seq_len, device=dev)
         self.sm = float(1.0 / math.sqrt(w.D))
+        # The timed loops call the library through PreparedCall: arguments are
+        # marshalled and checked once per layer cache, so a step costs one
+        # ctypes call per launch on the host and stays device-bound.
+        self._prep = {}
         torch.cuda.synchronize()
 
-    def write(self, i):
+    def _prepared(self, kind, i, impl=0):
+        key = (kind, i % self.R, impl)
+        call = self._prep.get(key)
+        if call is None:
+            call = {"write": self.write, "append": self.append, "attend": self.attend}[kind](i, impl, prepare=True)
+            self._prep[key] = call
+        return call
+
+    def run(self, kind, i, impl=0):
+        self._prepared(kind, i, impl)()
+
+    def write(self, i, impl=0, prepare=False):
         kc, vc = self.caches[i % self.R]
         if self.nvfp4:
-            self.K.kvq_nvfp4_cache_write(self.new_k, self.new_v, self.new_slots, kc, vc, self.ks, self.vs)
-        else:
-            self.K.kvq_cache_write(self.new_k, self.new_v, self.new_slots, kc, vc, self.kv_dtype, self.ks,
-                                   self.vs)
+            return self.K.kvq_nvfp4_cache_write(self.new_k, self.new_v, self.new_slots, kc, vc, self.ks, self.vs,
+                                                prepare=prepare)
+        return self.K.kvq_cache_write(self.new_k, self.new_v, self.new_slots, kc, vc, self.kv_dtype, self.ks,
+                                      self.vs, prepare=prepare)
 
-    def append(self, i):
+    def append(self, i, impl=0, prepare=False):
         """The step as one call: the new token's cache write fused into the decode."""
         kc, vc = self.caches[i % self.R]
         w = self.w
         if self.nvfp4:
-            self.K.kvq_nvfp4_paged_decode_attn_append(self.app_k, self.app_v, self.app_slots, self.q, kc, vc,
-                                                      self.bt, self.sl, w.max_seq_len, w.Hkv, self.ks, self.vs,
-                                                      self.sm, self.out, self.ws)
-        else:
-            self.K.kvq_paged_decode_attn_append(self.app_k, self.app_v, self.app_slots, self.q, kc, vc,
-                                                self.kv_dtype, self.bt, self.sl, w.max_seq_len, w.Hkv, self.ks,
-                                                self.vs, self.sm, self.out, self.ws)
+            return self.K.kvq_nvfp4_paged_decode_attn_append(self.app_k, self.app_v, self.app_slots, self.q, kc,
+                                                             vc, self.bt, self.sl, w.max_seq_len, w.Hkv, self.ks,
+                                                             self.vs, self.sm, self.out, self.ws, prepare=prepare)
+        return self.K.kvq_paged_decode_attn_append(self.app_k, self.app_v, self.app_slots, self.q, kc, vc,
+                                                   self.kv_dtype, self.bt, self.sl, w.max_seq_len, w.Hkv, self.ks,
+                                                   self.vs, self.sm, self.out, self.ws, prepare=prepare)
 
-    def attend(self, i, impl=0):
+    def attend(self, i, impl=0, prepare=False):
         kc, vc = self.caches[i % self.R]
         w = self.w
         if self.nvfp4:
-            self.K.kvq_nvfp4_paged_decode_attn(self.q, kc, vc, self.bt, self.sl, w.max_seq_len, w.Hkv, self.ks,
-                                               self.vs, self.sm, self.out, self.ws)
-        else:
-            self.K.kvq_paged_decode_attn(self.q, kc, vc, self.kv_dtype, self.bt, self.sl, w.max_seq_len, w.Hkv,
-                                         self.ks, self.vs, self.sm, self.out, self.ws, impl=impl)
+            return self.K.kvq_nvfp4_paged_decode_attn(self.q, kc, vc, self.bt, self.sl, w.max_seq_len, w.Hkv,
+                                                      self.ks, self.vs, self.sm, self.out, self.ws, prepare=prepare)
+        return self.K.kvq_paged_decode_attn(self.q, kc, vc, self.kv_dtype, self.bt, self.sl, w.max_seq_len,
+                                            w.Hkv, self.ks, self.vs, self.sm, self.out, self.ws, impl=impl,
+                                            prepare=prepare)
 
 
 def time_steps(torch, layers, steps, warmup, impl=0, fused=False):
@@ -149,10 +163,10 @@ def time_steps(torch, layers, steps, warmup, impl=0, fused=False):
     kvq_cache_write then kvq_paged_decode_attn."""
     def step(i):
         if fused:
-            layers.append(i)
+            layers.run("append", i)
         else:
-            layers.write(i)
-            layers.attend(i, impl)
+            layers.run("write", i)
+            layers.run("attend", i, impl)
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -175,7 +189,7 @@ def time_steps(torch, layers, steps, warmup, impl=0, fused=False):
     a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a0.record(st)
     for i in range(steps):
-        layers.attend(i, impl)
+        layers.run("attend", i, impl)
     a1.record(st)
     torch.cuda.synchronize()
     attn_ms = a0.elapsed_time(a1) / steps
@@ -280,7 +294,12 @@ def measure_multiquery(torch, K, name, q_lens, steps, warmup):
         torch.cuda.synchronize()
         return a0.elapsed_time(a1) / steps * 1e3
 
-    t1 = timed(lambda i: L.attend(i))
+    def prepared(make):
+        """Per layer cache, the call marshalled once (see Layers.run)."""
+        calls = [make(*L.caches[r]) for r in range(L.R)]
+        return lambda i: calls[i % L.R]()
+
+    t1 = timed(lambda i: L.run("attend", i))
     rec["q_len_1_us"] = round(t1, 2)
     # sliding window (gpt-oss alternates full layers with 128-token windows):
     # the call reads only the window's blocks
@@ -289,11 +308,9 @@ def measure_multiquery(torch, K, name, q_lens, steps, warmup):
         out = torch.empty(w.B, 1, w.Hq, w.D, dtype=torch.bfloat16, device="cuda")
         ws = K.new_workspace_mq(w.B, 1, w.Hq, w.Hkv, w.D, w.max_seq_len, window=W)
 
-        def call_w(i, q1=q1, out=out, ws=ws, W=W):
-            kc, vc = L.caches[i % L.R]
-            K.kvq_paged_decode_attn_mq(q1, kc, vc, K.KVQ_KV_FP8_E4M3, L.bt, L.sl, w.max_seq_len, w.Hkv, L.ks, L.vs,
-                                       L.sm, out, ws, window=W)
-        us = timed(call_w)
+        us = timed(prepared(lambda kc, vc, q1=q1, out=out, ws=ws, W=W: K.kvq_paged_decode_attn_mq(
+            q1, kc, vc, K.KVQ_KV_FP8_E4M3, L.bt, L.sl, w.max_seq_len, w.Hkv, L.ks, L.vs, L.sm, out, ws, window=W,
+            prepare=True)))
         wb, _ = step_bytes(w.B, w.Hq, w.Hkv, w.D, [min(W, n) for n in w.seq_lens], 1, w.B)
         rec[f"window_{W}"] = {"attn_us": round(us, 2), "attn_gbps": round(wb / (us * 1e-6) / 1e9, 1)}
     for ql in q_lens:
@@ -301,11 +318,9 @@ def measure_multiquery(torch, K, name, q_lens, steps, warmup):
         out = torch.empty(w.B, ql, w.Hq, w.D, dtype=torch.bfloat16, device="cuda")
         ws = K.new_workspace_mq(w.B, ql, w.Hq, w.Hkv, w.D, w.max_seq_len)
 
-        def call(i, q=q, out=out, ws=ws):
-            kc, vc = L.caches[i % L.R]
-            K.kvq_paged_decode_attn_mq(q, kc, vc, K.KVQ_KV_FP8_E4M3, L.bt, L.sl, w.max_seq_len, w.Hkv, L.ks,
-                                       L.vs, L.sm, out, ws)
-        us = timed(call)
+        us = timed(prepared(lambda kc, vc, q=q, out=out, ws=ws: K.kvq_paged_decode_attn_mq(
+            q, kc, vc, K.KVQ_KV_FP8_E4M3, L.bt, L.sl, w.max_seq_len, w.Hkv, L.ks, L.vs, L.sm, out, ws,
+            prepare=True)))
         # bytes: the KV scan once plus q_len x (q in, out)
         byts = attn_b1 + (ql - 1) * 2 * w.B * w.Hq * w.D * 2
         rec[f"q_len_{ql}"] = {"attn_us": round(us, 2), "attn_gbps": round(byts / (us * 1e-6) / 1e9, 1),
@@ -321,10 +336,8 @@ def measure_multiquery(torch, K, name, q_lens, steps, warmup):
         out = torch.empty(w.B, ql, w.Hq, w.D, dtype=torch.bfloat16, device="cuda")
         ws = K.new_workspace_mq(w.B, ql, w.Hq, w.Hkv, w.D, w.max_seq_len)
 
-        def call_qp(i, q=q, out=out, ws=ws, qs=qs):
-            kc, vc = L.caches[i % L.R]
-            K.kvq_paged_decode_attn_fp8qp(q, kc, vc, L.bt, L.sl, w.max_seq_len, w.Hkv, qs, L.ks, L.vs, L.sm, out, ws)
-        us = timed(call_qp)
+        us = timed(prepared(lambda kc, vc, q=q, out=out, ws=ws, qs=qs: K.kvq_paged_decode_attn_fp8qp(
+            q, kc, vc, L.bt, L.sl, w.max_seq_len, w.Hkv, qs, L.ks, L.vs, L.sm, out, ws, prepare=True)))
         byts = attn_b1 + (ql - 1) * 2 * w.B * w.Hq * w.D * 2
         base = t1 if ql == 1 else rec.get(f"q_len_{ql}", {}).get("attn_us")
         rec[f"fp8qp_q_len_{ql}"] = {"attn_us": round(us, 2), "attn_gbps": round(byts / (us * 1e-6) / 1e9, 1),

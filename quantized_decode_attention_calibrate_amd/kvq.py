@@ -98,6 +98,31 @@ def _check(fn: str, status: int) -> None:
         raise KvqError(fn, status)
 
 
+class PreparedCall:
+    """One library call with its arguments marshalled and checked once.
+    Calling it enqueues the same work again, on the stream it was prepared
+    for, without the Python-side checks: for launch-bound loops such as one
+    decode step per layer cache.  It keeps its tensors alive; their contents
+    may change between calls, their storage may not."""
+    __slots__ = ("_name", "_fn", "_args", "_keep")
+
+    def __init__(self, name: str, fn, args: tuple, keep: tuple):
+        self._name, self._fn, self._args, self._keep = name, fn, args, keep
+
+    def __call__(self) -> None:
+        status = self._fn(*self._args)
+        if status != KVQ_OK:
+            raise KvqError(self._name, status)
+
+
+def _run(name: str, fn, args: tuple, prepare: bool, keep: tuple):
+    """Call now, or (prepare=True) return the call as a PreparedCall."""
+    if prepare:
+        return PreparedCall(name, fn, args, keep)
+    _check(name, fn(*args))
+    return None
+
+
 def _ptr(t) -> int:
     return 0 if t is None else t.data_ptr()
 
@@ -160,29 +185,31 @@ def new_nvfp4_caches(num_blocks: int, Hkv: int, D: int, device="cuda"):
 
 
 def kvq_nvfp4_cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, k_cache: torch.Tensor,
-                          v_cache: torch.Tensor, k_gscale: float, v_gscale: float, stream=None) -> None:
+                          v_cache: torch.Tensor, k_gscale: float, v_gscale: float, stream=None, prepare: bool = False):
     assert k.dtype == torch.bfloat16 and v.dtype == torch.bfloat16 and slot_mapping.dtype == torch.int64
     T, Hkv, D = k.shape
     assert v.shape == k.shape and k.stride(0) == v.stride(0) and k.stride(2) == 1 and k.stride(1) == D
     assert slot_mapping.shape == (T,) and slot_mapping.is_contiguous()
-    _check("kvq_nvfp4_cache_write", _lib.kvq_nvfp4_cache_write(
+    return _run("kvq_nvfp4_cache_write", _lib.kvq_nvfp4_cache_write, (
         _ptr(k), _ptr(v), k.stride(0), _ptr(slot_mapping), T, Hkv, D, _ptr(k_cache), _ptr(v_cache),
-        k_cache.shape[0], BLOCK_SIZE, k_gscale, v_gscale, _stream(stream)))
+        k_cache.shape[0], BLOCK_SIZE, k_gscale, v_gscale, _stream(stream)),
+        prepare, (k, v, slot_mapping, k_cache, v_cache))
 
 
 def kvq_nvfp4_paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                                 block_tables: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, Hkv: int,
                                 k_gscale: float, v_gscale: float, sm_scale: float, out: torch.Tensor,
-                                workspace: torch.Tensor, split_tokens: int = 0, stream=None) -> None:
+                                workspace: torch.Tensor, split_tokens: int = 0, stream=None, prepare: bool = False):
     B, Hq, D = q.shape
     assert q.dtype == torch.bfloat16 and q.is_contiguous() and out.is_contiguous() and out.shape == q.shape
     assert block_tables.dtype == torch.int32 and block_tables.is_contiguous() and block_tables.shape[0] == B
     assert seq_lens.dtype == torch.int32 and seq_lens.shape == (B,)
     out_dtype = {torch.bfloat16: KVQ_OUT_BF16, torch.float32: KVQ_OUT_F32}[out.dtype]
-    _check("kvq_nvfp4_paged_decode_attn", _lib.kvq_nvfp4_paged_decode_attn_ex(
+    return _run("kvq_nvfp4_paged_decode_attn", _lib.kvq_nvfp4_paged_decode_attn_ex, (
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens),
         max_seq_len, B, Hq, Hkv, D, BLOCK_SIZE, k_cache.shape[0], k_gscale, v_gscale, sm_scale, _ptr(out),
-        out_dtype, _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream), split_tokens))
+        out_dtype, _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream), split_tokens),
+        prepare, (q, k_cache, v_cache, block_tables, seq_lens, out, workspace))
 
 
 def kvq_nvfp4_paged_decode_attn_append(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
@@ -190,7 +217,7 @@ def kvq_nvfp4_paged_decode_attn_append(k_new: torch.Tensor, v_new: torch.Tensor,
                                        block_tables: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
                                        Hkv: int, k_gscale: float, v_gscale: float, sm_scale: float,
                                        out: torch.Tensor, workspace: torch.Tensor, split_tokens: int = 0,
-                                       stream=None) -> None:
+                                       stream=None, prepare: bool = False):
     """kvq_nvfp4_cache_write of each sequence's newest token followed by
     kvq_nvfp4_paged_decode_attn, in one launch (arguments as
     kvq_paged_decode_attn_append, with the global scales)."""
@@ -203,11 +230,12 @@ def kvq_nvfp4_paged_decode_attn_append(k_new: torch.Tensor, v_new: torch.Tensor,
     assert block_tables.dtype == torch.int32 and block_tables.is_contiguous() and block_tables.shape[0] == B
     assert seq_lens.dtype == torch.int32 and seq_lens.shape == (B,)
     out_dtype = {torch.bfloat16: KVQ_OUT_BF16, torch.float32: KVQ_OUT_F32}[out.dtype]
-    _check("kvq_nvfp4_paged_decode_attn_append", _lib.kvq_nvfp4_paged_decode_attn_append(
+    return _run("kvq_nvfp4_paged_decode_attn_append", _lib.kvq_nvfp4_paged_decode_attn_append, (
         _ptr(k_new), _ptr(v_new), k_new.stride(0), _ptr(slot_mapping), _ptr(q), _ptr(k_cache), _ptr(v_cache),
         _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), max_seq_len, B, Hq, Hkv, D, BLOCK_SIZE,
         k_cache.shape[0], k_gscale, v_gscale, sm_scale, _ptr(out), out_dtype, _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream), split_tokens))
+        workspace.numel() * workspace.element_size(), _stream(stream), split_tokens),
+        prepare, (k_new, v_new, slot_mapping, q, k_cache, v_cache, block_tables, seq_lens, out, workspace))
 
 
 def kvq_e2m1_decode(codes: torch.Tensor, scale_code: int, out: torch.Tensor, stream=None) -> None:
@@ -233,16 +261,17 @@ def new_caches(kv_dtype: int, num_blocks: int, Hkv: int, D: int, device="cuda"):
 
 def kvq_cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, k_cache: torch.Tensor,
                     v_cache: torch.Tensor, kv_dtype: int, k_scale: float = 1.0, v_scale: float = 1.0,
-                    stream=None) -> None:
+                    stream=None, prepare: bool = False):
     """k, v: bf16 [T][Hkv][D] (token dim may be strided); slot_mapping int64 [T]."""
     assert k.dtype == torch.bfloat16 and v.dtype == torch.bfloat16 and slot_mapping.dtype == torch.int64
     T, Hkv, D = k.shape
     assert v.shape == k.shape and k.stride(0) == v.stride(0) and k.stride(2) == 1 and k.stride(1) == D
     assert slot_mapping.shape == (T,) and slot_mapping.is_contiguous()
     num_blocks = k_cache.shape[0]
-    _check("kvq_cache_write", _lib.kvq_cache_write(
+    return _run("kvq_cache_write", _lib.kvq_cache_write, (
         _ptr(k), _ptr(v), k.stride(0), _ptr(slot_mapping), T, Hkv, D, _ptr(k_cache), _ptr(v_cache),
-        num_blocks, BLOCK_SIZE, kv_dtype, k_scale, v_scale, _stream(stream)))
+        num_blocks, BLOCK_SIZE, kv_dtype, k_scale, v_scale, _stream(stream)),
+        prepare, (k, v, slot_mapping, k_cache, v_cache))
 
 
 def kvq_decode_workspace_bytes(B: int, Hq: int, Hkv: int, D: int, max_seq_len: int, split_tokens: int = 0) -> int:
@@ -263,25 +292,26 @@ def kvq_paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
                           block_tables: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, Hkv: int,
                           k_scale: float, v_scale: float, sm_scale: float, out: torch.Tensor,
                           workspace: torch.Tensor, impl: int = KVQ_IMPL_AUTO, split_tokens: int = 0,
-                          stream=None) -> None:
+                          stream=None, prepare: bool = False):
     """q bf16 [B][Hq][D]; out bf16 or fp32 [B][Hq][D]; block_tables int32 [B][max_blocks]; seq_lens int32 [B]."""
     B, Hq, D = q.shape
     assert q.dtype == torch.bfloat16 and q.is_contiguous() and out.is_contiguous() and out.shape == q.shape
     assert block_tables.dtype == torch.int32 and block_tables.is_contiguous() and block_tables.shape[0] == B
     assert seq_lens.dtype == torch.int32 and seq_lens.shape == (B,)
     out_dtype = {torch.bfloat16: KVQ_OUT_BF16, torch.float32: KVQ_OUT_F32}[out.dtype]
-    _check("kvq_paged_decode_attn", _lib.kvq_paged_decode_attn_ex(
+    return _run("kvq_paged_decode_attn", _lib.kvq_paged_decode_attn_ex, (
         _ptr(q), _ptr(k_cache), _ptr(v_cache), kv_dtype, _ptr(block_tables), block_tables.shape[1],
         _ptr(seq_lens), max_seq_len, B, Hq, Hkv, D, BLOCK_SIZE, k_cache.shape[0], k_scale, v_scale, sm_scale,
         _ptr(out), out_dtype, _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream),
-        impl, split_tokens))
+        impl, split_tokens),
+        prepare, (q, k_cache, v_cache, block_tables, seq_lens, out, workspace))
 
 
 def kvq_paged_decode_attn_append(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
                                  q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_dtype: int,
                                  block_tables: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, Hkv: int,
                                  k_scale: float, v_scale: float, sm_scale: float, out: torch.Tensor,
-                                 workspace: torch.Tensor, split_tokens: int = 0, stream=None) -> None:
+                                 workspace: torch.Tensor, split_tokens: int = 0, stream=None, prepare: bool = False):
     """kvq_cache_write of each sequence's newest token followed by
     kvq_paged_decode_attn, in one launch.  k_new, v_new bf16 [B][Hkv][D] (token
     dim may be strided); slot_mapping int64 [B], the slot of position
@@ -295,11 +325,12 @@ def kvq_paged_decode_attn_append(k_new: torch.Tensor, v_new: torch.Tensor, slot_
     assert block_tables.dtype == torch.int32 and block_tables.is_contiguous() and block_tables.shape[0] == B
     assert seq_lens.dtype == torch.int32 and seq_lens.shape == (B,)
     out_dtype = {torch.bfloat16: KVQ_OUT_BF16, torch.float32: KVQ_OUT_F32}[out.dtype]
-    _check("kvq_paged_decode_attn_append", _lib.kvq_paged_decode_attn_append(
+    return _run("kvq_paged_decode_attn_append", _lib.kvq_paged_decode_attn_append, (
         _ptr(k_new), _ptr(v_new), k_new.stride(0), _ptr(slot_mapping), _ptr(q), _ptr(k_cache), _ptr(v_cache),
         kv_dtype, _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), max_seq_len, B, Hq, Hkv, D, BLOCK_SIZE,
         k_cache.shape[0], k_scale, v_scale, sm_scale, _ptr(out), out_dtype, _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream), split_tokens))
+        workspace.numel() * workspace.element_size(), _stream(stream), split_tokens),
+        prepare, (k_new, v_new, slot_mapping, q, k_cache, v_cache, block_tables, seq_lens, out, workspace))
 
 
 # ---- multi-query decode -------------------------------------------------------
@@ -328,29 +359,32 @@ def _mq_args(q, block_tables, seq_lens, out):
 def kvq_paged_decode_attn_mq(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_dtype: int,
                              block_tables: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, Hkv: int,
                              k_scale: float, v_scale: float, sm_scale: float, out: torch.Tensor,
-                             workspace: torch.Tensor, split_tokens: int = 0, window: int = 0, stream=None) -> None:
+                             workspace: torch.Tensor, split_tokens: int = 0, window: int = 0, stream=None,
+                             prepare: bool = False):
     """q bf16 [B][q_len][Hq][D] (the q_len newest tokens, already in the cache);
     out bf16 or fp32 [B][q_len][Hq][D]; window > 0: sliding-window attention."""
     B, q_len, Hq, D, out_dtype = _mq_args(q, block_tables, seq_lens, out)
-    _check("kvq_paged_decode_attn_mq", _lib.kvq_paged_decode_attn_mq(
+    return _run("kvq_paged_decode_attn_mq", _lib.kvq_paged_decode_attn_mq, (
         _ptr(q), q_len, window, _ptr(k_cache), _ptr(v_cache), kv_dtype, _ptr(block_tables), block_tables.shape[1],
         _ptr(seq_lens), max_seq_len, B, Hq, Hkv, D, BLOCK_SIZE, k_cache.shape[0], k_scale, v_scale, sm_scale,
         _ptr(out), out_dtype, _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream),
-        split_tokens))
+        split_tokens),
+        prepare, (q, k_cache, v_cache, block_tables, seq_lens, out, workspace))
 
 
 def kvq_nvfp4_paged_decode_attn_mq(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                                    block_tables: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, Hkv: int,
                                    k_gscale: float, v_gscale: float, sm_scale: float, out: torch.Tensor,
                                    workspace: torch.Tensor, split_tokens: int = 0, window: int = 0,
-                                   stream=None) -> None:
+                                   stream=None, prepare: bool = False):
     """NVFP4 caches; otherwise as kvq_paged_decode_attn_mq."""
     B, q_len, Hq, D, out_dtype = _mq_args(q, block_tables, seq_lens, out)
-    _check("kvq_nvfp4_paged_decode_attn_mq", _lib.kvq_nvfp4_paged_decode_attn_mq(
+    return _run("kvq_nvfp4_paged_decode_attn_mq", _lib.kvq_nvfp4_paged_decode_attn_mq, (
         _ptr(q), q_len, window, _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1],
         _ptr(seq_lens), max_seq_len, B, Hq, Hkv, D, BLOCK_SIZE, k_cache.shape[0], k_gscale, v_gscale, sm_scale,
         _ptr(out), out_dtype, _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream),
-        split_tokens))
+        split_tokens),
+        prepare, (q, k_cache, v_cache, block_tables, seq_lens, out, workspace))
 
 
 # ---- block copies for a host-memory KV tier ----------------------------------------
@@ -404,11 +438,13 @@ def kvq_restore_blocks(host_src: torch.Tensor, staging: torch.Tensor, block_byte
 def kvq_paged_decode_attn_fp8qp(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                                 block_tables: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, Hkv: int,
                                 q_scale: float, k_scale: float, v_scale: float, sm_scale: float, out: torch.Tensor,
-                                workspace: torch.Tensor, split_tokens: int = 0, window: int = 0, stream=None) -> None:
+                                workspace: torch.Tensor, split_tokens: int = 0, window: int = 0, stream=None,
+                             prepare: bool = False):
     """FP8 cache, FP8 Q (q_scale) and FP8 P on FP8 MFMA; q [B][q_len][Hq][D] as kvq_paged_decode_attn_mq."""
     B, q_len, Hq, D, out_dtype = _mq_args(q, block_tables, seq_lens, out)
-    _check("kvq_paged_decode_attn_fp8qp", _lib.kvq_paged_decode_attn_fp8qp(
+    return _run("kvq_paged_decode_attn_fp8qp", _lib.kvq_paged_decode_attn_fp8qp, (
         _ptr(q), q_len, window, _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1],
         _ptr(seq_lens), max_seq_len, B, Hq, Hkv, D, BLOCK_SIZE, k_cache.shape[0], q_scale, k_scale, v_scale,
         sm_scale, _ptr(out), out_dtype, _ptr(workspace), workspace.numel() * workspace.element_size(),
-        _stream(stream), split_tokens))
+        _stream(stream), split_tokens),
+        prepare, (q, k_cache, v_cache, block_tables, seq_lens, out, workspace))

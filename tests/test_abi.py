@@ -236,3 +236,21 @@ def test_nvfp4_append_host_validation(K):
     assert call(gs=0.0) == -1 and call(gs=float("nan")) == -1
     assert call(D=96, stride=192) == -2
     assert call(B=0, k_new=None, slots=None) == 0
+
+
+def test_prepared_call_defers_and_checks(K):
+    """prepare=True marshals the arguments without calling; calling the
+    PreparedCall runs the library call and raises on its status.  An invalid
+    kv_dtype fails host validation, so nothing is enqueued (CPU tensors are
+    never dereferenced)."""
+    import torch
+    k = torch.zeros(2, 1, 64, dtype=torch.bfloat16)
+    slots = torch.zeros(2, dtype=torch.int64)
+    kc = torch.zeros(4, 1, 16, 64, dtype=torch.uint8)
+    call = K.kvq_cache_write(k, k, slots, kc, kc, 7, 1.0, 1.0, stream=0, prepare=True)   # 0: the null stream
+    assert isinstance(call, K.PreparedCall)
+    with pytest.raises(K.KvqError) as e:
+        call()
+    assert e.value.status == K.KVQ_EINVAL
+    with pytest.raises(K.KvqError):
+        K.kvq_cache_write(k, k, slots, kc, kc, 7, 1.0, 1.0, stream=0)
