@@ -17,6 +17,12 @@ namespace kvq {
 // on gfx950: 16-32 splits per sequence beat 64-128 at 65k-131k tokens).
 constexpr int kTargetWorkGroups = 256;
 constexpr int kMinSplitTokens = 512;
+// When the (sequence, KV head) units alone already fill the chip, splits
+// only balance the tail of a ragged batch: 4,096 tokens measured best on a
+// 64-sequence batch of 1k-131k tokens (FP8 523 -> 516 us, BF16 1,035 -> 1,005
+// us against 8,192), while fewer, longer splits stay best for a few long
+// sequences (4 x 126,976: 7,936 tokens).
+constexpr int kManyUnitSplitTokens = 4096;
 
 static size_t pad256(size_t n) { return (n + 255) / 256 * 256; }
 
@@ -39,6 +45,7 @@ DecodePlan plan_decode(int B, int Hkv, int max_seq_len, int split_tokens_request
         s = (s + kChunkTokens - 1) / kChunkTokens * kChunkTokens;
         if (s < kMinSplitTokens) s = kMinSplitTokens;
         if (s > kMaxSplitTokens) s = kMaxSplitTokens;
+        if (units >= kTargetWorkGroups && s > kManyUnitSplitTokens) s = kManyUnitSplitTokens;
         split = (int)s;
     }
     p.split_tokens = split;

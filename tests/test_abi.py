@@ -126,6 +126,13 @@ def test_plan_and_workspace(K):
             want = pad(B * Hq * SS * 8) + B * Hq * SS * D * 4
             assert K.kvq_decode_workspace_bytes(B, Hq, Hkv, D, L, sp) == want
     assert K.kvq_decode_workspace_bytes(1, 8, 2, 64, 100, 100) == 0   # not a multiple of 64
+    # the measured plan: ~256 work-groups from (sequence, KV head) units, 4,096-token splits once the
+    # units alone fill the chip
+    assert K.kvq_decode_plan_split_tokens(1, 8, 65536) == 2048
+    assert K.kvq_decode_plan_split_tokens(4, 4, 126976) == 7936
+    assert K.kvq_decode_plan_split_tokens(2, 8, 131072) == 8192
+    assert K.kvq_decode_plan_split_tokens(64, 8, 131072) == 4096
+    assert K.kvq_decode_plan_split_tokens(64, 8, 2000) == 2048
 
 
 def test_nvfp4_host_calls(K):
