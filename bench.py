@@ -376,6 +376,59 @@ def measure_workload(torch, K, name, steps, warmup, with_nvfp4=False):
     return rec
 
 
+def measure_quality(torch, K, name):
+    """The comparison the FP8 calibration guide asks for: BF16 KV, FP8 with the
+    default scale 1.0, and FP8 with calibrated scales.  Reports the
+    reconstruction cosine of the whole K and V tensors (fp64 over
+    value(E4M3(x / scale)) * scale, codes from the library's encoder and
+    decoder) and the FP8 attention output's distance from the BF16-KV output
+    on the same queries, with non-finite outputs counted.  Reported, not
+    gated."""
+    from quantized_decode_attention_calibrate_amd import workloads
+    w = workloads.make(name, device="cuda", seed=0)
+    amax = torch.zeros(2, dtype=torch.float32, device="cuda")   # calibrated as the workload says (sample or data)
+    K.kvq_amax_bf16(w.calib_k if w.calib_k is not None else w.k, amax[0:1])
+    K.kvq_amax_bf16(w.calib_v if w.calib_v is not None else w.v, amax[1:2])
+    ks, vs = K.kvq_calibrate(amax.cpu().tolist())
+
+    def recon_cos(x, scale):
+        y = (x.float() / scale).reshape(-1).contiguous()
+        codes = torch.empty(y.numel(), dtype=torch.uint8, device="cuda")
+        K.kvq_e4m3_encode_f32(y, codes)
+        r = torch.empty(y.numel(), dtype=torch.float32, device="cuda")
+        K.kvq_e4m3_decode(codes, r)
+        r = r.double() * scale
+        x64 = x.double().reshape(-1)
+        return round(float((x64 @ r) / (x64.norm() * r.norm())), 7)
+
+    sl = torch.tensor(w.seq_lens, dtype=torch.int32, device="cuda")
+    ws = K.new_workspace(w.B, w.Hq, w.Hkv, w.D, w.max_seq_len)
+    sm = float(1.0 / math.sqrt(w.D))
+
+    def attend(kv, k_s, v_s):
+        kc, vc = K.new_caches(kv, w.num_blocks, w.Hkv, w.D)
+        K.kvq_cache_write(w.k, w.v, w.slot_mapping, kc, vc, kv, k_s, v_s)
+        out = torch.empty(w.B, w.Hq, w.D, dtype=torch.float32, device="cuda")
+        K.kvq_paged_decode_attn(w.q, kc, vc, kv, w.block_tables, sl, w.max_seq_len, w.Hkv, k_s, v_s, sm, out, ws)
+        torch.cuda.synchronize()
+        return out.double()
+
+    ref = attend(K.KVQ_KV_BF16, 1.0, 1.0)
+    rec = {"workload": name, "k_scale": ks, "v_scale": vs}
+    for tag, (k_s, v_s) in (("fp8_calibrated", (ks, vs)), ("fp8_scale_1", (1.0, 1.0))):
+        out = attend(K.KVQ_KV_FP8_E4M3, k_s, v_s)
+        fin = torch.isfinite(out)
+        d = (out - ref)[fin]
+        rec[tag] = {"k_cos": recon_cos(w.k, k_s), "v_cos": recon_cos(w.v, v_s),
+                    "saturated": int(((w.k.float() / k_s).abs() > 448).sum() + ((w.v.float() / v_s).abs() > 448).sum()),
+                    "attn_rel_l2_vs_bf16": round(float(d.norm() / ref[fin].norm()), 6),
+                    "attn_max_abs_vs_bf16": round(float(d.abs().max()), 6),
+                    "nonfinite_outputs": int((~fin).sum())}
+    del w
+    torch.cuda.empty_cache()
+    return rec
+
+
 def env_info(torch):
     """The run's software and device: HIP version torch was built with, the
     compiler, the GPU and its compute units, and a diagnostic streaming rate
@@ -626,6 +679,8 @@ def main():
         result["offload"] = measure_offload(torch, K, "gptoss65k")
         print("[bench] multi-query decode", file=sys.stderr, flush=True)
         result["multiquery"] = measure_multiquery(torch, K, "gptoss65k", (2, 4, 8), 200, 20)
+        print("[bench] quantization quality", file=sys.stderr, flush=True)
+        result["quality"] = [measure_quality(torch, K, n) for n in ("gptoss65k", "agents126k")]
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         w_cpu = workloads.make(args.workload, device="cpu", seed=0)
