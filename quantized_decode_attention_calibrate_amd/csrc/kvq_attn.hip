@@ -620,7 +620,10 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
     }
     const int tok_end = min(L, tok_begin + a.split_tokens);
     const int S = (L - sr.base + a.split_tokens - 1) / a.split_tokens;   // splits holding tokens
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // the wave index as a scalar: every per-wave loop bound below is then uniform,
+    // so its loops branch on SCC instead of masking exec (a masked loop keeps the
+    // prefetch of its last pass live into the header, which then drains all loads)
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int n = lane & 15, grp = lane >> 4;
     const int G = a.G, GQ = G * a.q_len;
 
@@ -796,26 +799,38 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
         // Software pipeline: the next chunk's loads are in flight while the
         // current one is computed.  The prefetch is unconditional so wait
         // counts stay static: past a wave's last chunk it re-issues that
-        // chunk's addresses (L2 hits; the registers are never read).
+        // chunk's addresses (L2 hits; the registers are never read).  A pass
+        // takes two chunks and has no exit inside it, so every path back to
+        // the loop header has consumed the pass's first prefetch; an odd last
+        // chunk is computed after the loop.
         MfmaChunk<D, FMT> A, Bc;
         if (my > 0) {
             int ch = wave;
             if (APPEND && writer && my == 1) append_fence();
             mfma_load(A, a, s_blk, ch, g, n, grp);
-            for (int i = 0; i < my; i += 2) {
-                const int chb = i + 1 < my ? ch + W : ch;
+            for (int i = 0; i + 1 < my; i += 2) {
+                const int chb = ch + W;
                 if (APPEND && writer && i + 2 == my) append_fence();
                 mfma_load(Bc, a, s_blk, chb, g, n, grp);
+                // issue the prefetch before any of the current chunk's math: the
+                // first conversion waits on the current chunk's oldest load.  Only
+                // for single-query tiles at D = 64, where a chunk's math is short;
+                // elsewhere the fence costs registers (a spill with two BF16 tiles
+                // at D = 128) or time (about 1.5% for FP8 at D = 128)
+                if constexpr (NT == 1 && D == 64) __builtin_amdgcn_sched_barrier(0);
                 process_chunk(st, A, qb, cs, cbeg, cend, tok_begin + ch * kChunkTokens, tok_end, tail_from,
                               head_until, sr.first, grp);
-                if (i + 1 >= my) break;
                 const int cha = i + 2 < my ? chb + W : chb;
                 if (APPEND && writer && i + 3 == my) append_fence();
                 mfma_load(A, a, s_blk, cha, g, n, grp);
+                if constexpr (NT == 1 && D == 64) __builtin_amdgcn_sched_barrier(0);
                 process_chunk(st, Bc, qb, cs, cbeg, cend, tok_begin + chb * kChunkTokens, tok_end, tail_from,
                               head_until, sr.first, grp);
                 ch = cha;
             }
+            if (my & 1)
+                process_chunk(st, A, qb, cs, cbeg, cend, tok_begin + ch * kChunkTokens, tok_end, tail_from,
+                              head_until, sr.first, grp);
         }
     } else {
         for (int i = 0; i < my; ++i) {
