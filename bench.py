@@ -362,7 +362,9 @@ def measure_workload(torch, K, name, steps, warmup, with_nvfp4=False):
         attn_b, write_b = step_bytes(w.B, w.Hq, w.Hkv, w.D, w.seq_lens, eb, w.B)
         rec[tag] = {"attn_us": round(attn_ms * 1e3, 2), "attn_gbps": round(attn_b / (attn_ms * 1e-3) / 1e9, 1),
                     "pct_of_hbm_peak": round(100 * attn_b / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1),
-                    "step_us": round(step_ms * 1e3, 2), "layers_rotated": L.R}
+                    "step_us": round(step_ms * 1e3, 2), "layers_rotated": L.R,
+                    # the one-token-per-sequence write's share of the two-launch step
+                    "write_us_step_minus_attn": round((step_ms - attn_ms) * 1e3, 2)}
         fstep, _ = time_steps(torch, L, steps, warmup, fused=True)   # the step as one call
         rec[tag]["step_one_call_us"] = round(fstep * 1e3, 2)
         del L
@@ -431,15 +433,18 @@ def measure_quality(torch, K, name):
 
 def env_info(torch):
     """The run's software and device: HIP version torch was built with, the
-    compiler, the GPU and its compute units, and a diagnostic streaming rate
-    (a 1 GiB device-to-device copy, read + write bytes over its time)."""
-    import subprocess
+    ROCm release, the GPU, its compute units and current clocks, and a
+    diagnostic streaming rate (a 1 GiB device-to-device copy, read + write
+    bytes over its time)."""
     p = torch.cuda.get_device_properties(0)
+    # the ROCm release from its version file (no child process: under a
+    # profiler that preloads its library, a child would initialise the GPU
+    # and then exec)
     try:
-        hipcc = subprocess.run(["/opt/rocm/bin/hipcc", "--version"], capture_output=True, text=True,
-                               timeout=30).stdout.strip().splitlines()[0]
-    except Exception:   # the compiler is optional at run time
-        hipcc = None
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        rocm = None
     src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(3):
@@ -454,9 +459,27 @@ def env_info(torch):
     copy_gbps = 2 * (1 << 30) * 10 / (a.elapsed_time(b) * 1e-3) / 1e9
     del src, dst
     torch.cuda.empty_cache()
-    return {"torch": torch.__version__, "torch_hip": torch.version.hip, "hipcc": hipcc, "device": p.name,
+    return {"torch": torch.__version__, "torch_hip": torch.version.hip, "rocm": rocm, "device": p.name,
             "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
-            "copy_1gib_gbps": round(copy_gbps, 1)}
+            "copy_1gib_gbps": round(copy_gbps, 1), "clocks": read_clocks()}
+
+
+def read_clocks():
+    """The current shader and memory clock levels from the driver's sysfs
+    tables (the line marked '*'), if readable; None otherwise."""
+    import glob
+    out = {}
+    for key, name in (("sclk", "pp_dpm_sclk"), ("mclk", "pp_dpm_mclk")):
+        for path in sorted(glob.glob(f"/sys/class/drm/card*/device/{name}")):
+            try:
+                with open(path) as f:
+                    cur = [ln.split(":", 1)[1].strip().rstrip("*").strip() for ln in f if ln.rstrip().endswith("*")]
+            except OSError:
+                continue
+            if cur:
+                out[key] = cur[0]
+                break
+    return out or None
 
 
 def cpu_baseline(w, ks, vs, n_kv_heads, threads=None):

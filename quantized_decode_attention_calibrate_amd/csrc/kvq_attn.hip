@@ -329,12 +329,21 @@ __device__ __forceinline__ void mfma_process(MfmaState<D, NT>& st, MfmaChunk<D, 
     // The score scale cs (> 0) is applied as exp2(fma(s, cs, -m)); the running
     // max m is kept in scaled units.  Masking runs only on chunks that reach a
     // column's end (a wave-uniform branch).  A column that has seen no token
-    // yet keeps m = -inf; its weights are 0 and alpha is 0.
+    // yet keeps m = -inf; its weights are 0 (and its acc and l are still 0).
     const bool tail = chunk_tok + kChunkTokens > tail_from || chunk_tok < head_until;
     const int tok0 = chunk_tok + 16 * grp;   // token of sv[.][0]
     f16x8 pfh[NT][2], pfl[NT][2];
     bf16x8 pbh[NT][2], pbl[NT][2];
     float alpha[NT];
+    // Lazy rescale (FP8 and BF16): a column's reference max m stays until the
+    // chunk max exceeds it by more than kLazy (log2 units), so most chunks
+    // skip the accumulator rescale; the weights' exp2 offset is 15 - kLazy, so
+    // they still stay below 2^15.  The arithmetic is per column and the same
+    // for every tile count, so a row's result does not depend on how many
+    // queries share the launch.  NVFP4 (VALU-bound at one tile) keeps the
+    // exact-max update (kLazy = 0: bitwise the plain online softmax).
+    constexpr float kLazy = FMT == kFmtNVFP4 ? 0.0f : 8.0f;
+    bool rescale = false;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         if (tail) {
@@ -349,16 +358,20 @@ __device__ __forceinline__ void mfma_process(MfmaState<D, NT>& st, MfmaChunk<D, 
         mloc = fmaxf(mloc, shfl_xor(mloc, 16));
         mloc = fmaxf(mloc, shfl_xor(mloc, 32));
         const float m_new = fmaxf(st.m_run[nt], mloc * cs[nt]);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        alpha[nt] = fast_exp2(st.m_run[nt] - m_use);
-        st.m_run[nt] = m_new;
+        const bool keep = m_new <= st.m_run[nt] + kLazy;
+        const float m_ref = keep ? st.m_run[nt] : m_new;
+        const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+        alpha[nt] = keep ? 1.f : fast_exp2(st.m_run[nt] - m_use);
+        rescale = rescale || !keep;
+        st.m_run[nt] = m_ref;
 
         // Weights in the PV operand layout (half hh = tokens 8hh..8hh+7).  They
-        // are scaled by 2^15 (exp2 offset) so they sit in f16's normal range,
+        // are scaled by 2^(15 - kLazy) (exp2 offset; at most 2^15 over the
+        // reference) so they sit in f16's normal range,
         // and split into hi + lo 16-bit parts so the two PV MFMAs on the same
         // exact V operand reproduce the fp32 weight to ~2^-21.  The scale is
         // common to acc and l and cancels in the final division.
-        const float m_off = m_use - 15.0f;
+        const float m_off = m_use - (15.0f - kLazy);
         float psum = 0.f;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
@@ -435,8 +448,11 @@ __device__ __forceinline__ void mfma_process(MfmaState<D, NT>& st, MfmaChunk<D, 
     // ---- acc = alpha * acc + V^T P^T ----------------------------------------
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
+        // (one tile or NVFP4: unconditional; the multiply by alpha = 1 is exact)
+        if (NT == 1 || FMT == kFmtNVFP4 || __builtin_amdgcn_ballot_w64(rescale) != 0) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) st.acc[nt][dt] *= alpha[nt];
+            for (int nt = 0; nt < NT; ++nt) st.acc[nt][dt] *= alpha[nt];
+        }
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             if constexpr (kF16V) {
