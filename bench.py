@@ -37,7 +37,8 @@ METRIC = "FP8 paged decode-attn achieved HBM GB/s (% of peak) + KV tokens scanne
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["quantized_decode_attention_calibrate_amd/csrc/kvq_attn.hip",
                   "quantized_decode_attention_calibrate_amd/csrc/kvq_device.h",
-                  "quantized_decode_attention_calibrate_amd/csrc/kvq_internal.h"]
+                  "quantized_decode_attention_calibrate_amd/csrc/kvq_internal.h",
+                  "quantized_decode_attention_calibrate_amd/build.py"]   # (its compiler flags)
 
 
 def kernel_source_hash() -> str:

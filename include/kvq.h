@@ -54,8 +54,9 @@ extern "C" {
 #endif
 
 /* 2: multi-query and sliding-window decode, FP8 Q/P variant, fused append,
- *    host-memory block tier */
-#define KVQ_ABI_VERSION 2
+ *    host-memory block tier
+ * 3: kvq_check_flags and the checked build libkvq_check.so */
+#define KVQ_ABI_VERSION 3
 
 enum kvq_status {
     KVQ_OK = 0,
@@ -82,6 +83,26 @@ int kvq_last_hip_error(void);
 
 /* KVQ_ABI_VERSION of the loaded library. */
 int kvq_abi_version(void);
+
+/* ---- checked build -------------------------------------------------------
+ * Device data (block tables, slot mappings, sequence lengths, block-copy ids)
+ * is the caller's contract and the release library libkvq.so does not check
+ * it.  libkvq_check.so is the same library built with device-side checks: a
+ * block-table entry outside [0, num_blocks) reads block 0, a sequence length
+ * outside [0, max_seq_len] is clamped, a slot at or past
+ * num_blocks * block_size (cache writes and the fused append) is skipped,
+ * and a negative block-copy id is skipped (the copy calls take no block
+ * count); each case sets a bit in a device flag word.  Meant for tests and
+ * debugging: results of valid calls are bit-identical to libkvq.so's.
+ * kvq_check_flags copies the OR of the bits to *flags_host and, if clear is
+ * non-zero, zeroes them.  It is synchronous: call it after the streams that
+ * ran the checked calls have finished.  Returns KVQ_EUNSUPPORTED (and 0 in
+ * *flags_host) from libkvq.so, KVQ_EINVAL if flags_host is NULL, KVQ_EHIP if
+ * the copy fails. */
+#define KVQ_CHECK_BLOCK_ID 1u
+#define KVQ_CHECK_SEQ_LEN 2u
+#define KVQ_CHECK_SLOT 4u
+int kvq_check_flags(unsigned* flags_host, int clear);
 
 /* ---- codec utilities (device) ---------------------------------------------
  * The E4M3 codec used by every kernel, exposed for exhaustive checks.

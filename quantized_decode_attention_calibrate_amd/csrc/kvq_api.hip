@@ -87,6 +87,16 @@ int kvq_last_hip_error(void) { return g_last_hip_error; }
 
 int kvq_abi_version(void) { return KVQ_ABI_VERSION; }
 
+int kvq_check_flags(unsigned* flags_host, int clear) {
+    if (!flags_host) return KVQ_EINVAL;
+    *flags_host = 0;
+    if (!KVQ_CHECK) return KVQ_EUNSUPPORTED;
+    const unsigned f = check_flags_attn(clear != 0) | check_flags_cache(clear != 0);
+    if (f == ~0u) return hip_status(hipErrorUnknown);
+    *flags_host = f;
+    return KVQ_OK;
+}
+
 int kvq_e4m3_encode_f32(const float* y_dev, uint8_t* codes_dev, int64_t n, void* hip_stream) {
     if (n < 0) return KVQ_EINVAL;
     if (n == 0) return KVQ_OK;
@@ -155,7 +165,7 @@ int kvq_nvfp4_cache_write(const void* k_dev, const void* v_dev, int64_t src_toke
         return KVQ_EINVAL;
     return hip_status(launch_nvfp4_cache_write(k_dev, v_dev, src_token_stride, slot_mapping_dev, T, Hkv, D,
                                                k_cache_dev, v_cache_dev, k_gscale, v_gscale,
-                                               (hipStream_t)hip_stream));
+                                               (int64_t)num_blocks * kBlockSize, (hipStream_t)hip_stream));
 }
 
 int kvq_cache_write(const void* k_dev, const void* v_dev, int64_t src_token_stride,
@@ -173,7 +183,7 @@ int kvq_cache_write(const void* k_dev, const void* v_dev, int64_t src_token_stri
         return KVQ_EINVAL;
     return hip_status(launch_cache_write(k_dev, v_dev, src_token_stride, slot_mapping_dev, T, Hkv, D,
                                          k_cache_dev, v_cache_dev, block_size, kv_dtype, k_scale, v_scale,
-                                         (hipStream_t)hip_stream));
+                                         (int64_t)num_blocks * kBlockSize, (hipStream_t)hip_stream));
 }
 
 int kvq_decode_plan_split_tokens(int B, int Hkv, int max_seq_len, int block_size) {
@@ -260,6 +270,8 @@ static int decode_common(int fmt, const void* q_dev, int q_len, int window, cons
     a.ws_acc = (float*)((char*)a.ws_ml + decode_ml_bytes(B * q_len, Hq, plan.num_splits));
     a.out = out_dev;
     a.max_blocks = max_blocks_per_seq;
+    a.num_blocks = num_blocks;
+    a.max_seq_len = max_seq_len;
     a.Hq = Hq;
     a.Hkv = Hkv;
     a.G = G;

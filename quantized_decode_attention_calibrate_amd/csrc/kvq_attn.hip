@@ -72,10 +72,15 @@ __host__ __device__ constexpr int lds_merge_floats(int GQ, int D, int W, int NT 
 // masked; the clamp keeps every address inside the cache and reads no table
 // entry outside [first_lb, last_lb]).
 __device__ __forceinline__ void stage_block_ids(int* s_blk, const int32_t* bt_row, int lb0, int n,
-                                                int first_lb, int last_lb) {
+                                                int first_lb, int last_lb, int num_blocks) {
     for (int i = threadIdx.x; i < n; i += blockDim.x) {
         int lb = min(max(lb0 + i, first_lb), last_lb);
-        s_blk[i] = bt_row[lb];
+        int id = bt_row[lb];
+        if (KVQ_CHECK && (unsigned)id >= (unsigned)num_blocks) {
+            check_fail(kCheckBlockId);
+            id = 0;
+        }
+        s_blk[i] = id;
     }
 }
 
@@ -86,9 +91,17 @@ __device__ __forceinline__ void stage_block_ids(int* s_blk, const int32_t* bt_ro
 struct SeqRange {
     int L, first, base;
 };
+__device__ __forceinline__ int seq_len(const DecodeArgs& a, int b) {
+    int L = a.seq_lens[b];
+    if (KVQ_CHECK && (L < 0 || L > a.max_seq_len)) {
+        check_fail(kCheckSeqLen);
+        L = min(max(L, 0), a.max_seq_len);
+    }
+    return L;
+}
 __device__ __forceinline__ SeqRange seq_range(const DecodeArgs& a, int b) {
     SeqRange r;
-    r.L = a.seq_lens[b];
+    r.L = seq_len(a, b);
     r.first = a.window > 0 ? max(0, r.L - a.q_len - a.window + 1) : 0;
     r.base = r.first & ~(kChunkTokens - 1);
     return r;
@@ -654,6 +667,10 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
     if constexpr (APPEND) {
         if (writer) {
             new_slot = a.new_slots[b];
+            if (KVQ_CHECK && new_slot >= (int64_t)a.num_blocks * kBlockSize) {
+                check_fail(kCheckSlot);
+                new_slot = -1;
+            }
             const int64_t row = (int64_t)b * a.new_stride + (int64_t)g * D;
             if constexpr (FMT == kFmtNVFP4) {
                 if (lane < 2 * NG) {
@@ -671,7 +688,7 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
         }
     }
     stage_block_ids(s_blk, a.block_tables + (int64_t)b * a.max_blocks, lb0, n_chunks * 4, sr.first / kBlockSize,
-                    (L + kBlockSize - 1) / kBlockSize - 1);
+                    (L + kBlockSize - 1) / kBlockSize - 1, a.num_blocks);
 
     // Query i (token L - q_len + i) sees tokens [cbeg, cend): cend = that
     // token + 1, cbeg = cend - window (or 0).
@@ -905,7 +922,7 @@ __global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeArgs a) {
     float* s_p = s_q + G * D;                    // [kWaves][16 heads][16 tokens]
 
     const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    const int L = a.seq_lens[b];
+    const int L = seq_len(a, b);
     const int tok_begin = s * a.split_tokens;
     if (tok_begin >= L) {
         if (L <= 0 && s == 0) write_empty(a, b, g, D);
@@ -919,7 +936,7 @@ __global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeArgs a) {
     const int lb0 = tok_begin / kBlockSize;
     const int n_blocks = (tok_end - tok_begin + kBlockSize - 1) / kBlockSize;
     stage_block_ids(s_blk, a.block_tables + (int64_t)b * a.max_blocks, lb0, n_blocks, 0,
-                    (L + kBlockSize - 1) / kBlockSize - 1);
+                    (L + kBlockSize - 1) / kBlockSize - 1, a.num_blocks);
     for (int i = threadIdx.x; i < G * D; i += kThreads) {
         const int h = i / D, d = i - h * D;
         s_q[i] = bits_f32((uint32_t)a.q[((int64_t)b * a.Hq + g * G + h) * D + d] << 16);
@@ -1222,6 +1239,21 @@ hipError_t launch_decode(const DecodeArgs& a, int B, int D, int fmt, int impl, h
         case kFmtFP8QP: return launch_d<kFmtFP8QP>(a, B, D, impl, st);
         default: return hipErrorInvalidValue;
     }
+}
+
+unsigned check_flags_attn(bool clear) {
+#if KVQ_CHECK
+    unsigned v = 0;
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_check_flags), sizeof(v)) != hipSuccess) return ~0u;
+    if (clear) {
+        const unsigned z = 0;
+        if (hipMemcpyToSymbol(HIP_SYMBOL(g_check_flags), &z, sizeof(z)) != hipSuccess) return ~0u;
+    }
+    return v;
+#else
+    (void)clear;
+    return 0;
+#endif
 }
 
 }  // namespace kvq

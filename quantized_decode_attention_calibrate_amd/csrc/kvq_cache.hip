@@ -158,7 +158,7 @@ template <bool FP8>
 __global__ void __launch_bounds__(kWriteThreads) cache_write_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t src_stride,
     const int64_t* __restrict__ slot_mapping, int T, int Hkv, int D, uint8_t* __restrict__ k_cache,
-    uint8_t* __restrict__ v_cache, float k_scale, float v_scale) {
+    uint8_t* __restrict__ v_cache, float k_scale, float v_scale, int64_t n_slots) {
     using Elem = typename std::conditional<FP8, uint8_t, uint16_t>::type;
     extern __shared__ uint32_t lds_w[];
     Elem* vt = reinterpret_cast<Elem*>(lds_w);   // [D][16] V elements of the window
@@ -175,7 +175,11 @@ __global__ void __launch_bounds__(kWriteThreads) cache_write_kernel(
             continue;
         }
         const int64_t src = (int64_t)t * src_stride + (int64_t)g * D + d0;
-        const int64_t slot = slot_mapping[t];
+        int64_t slot = slot_mapping[t];
+        if (KVQ_CHECK && slot >= n_slots) {
+            check_fail(kCheckSlot);
+            slot = -1;
+        }
         const u32x4 kw = *reinterpret_cast<const u32x4*>(k + src);
         const u32x4 vw = *reinterpret_cast<const u32x4*>(v + src);
         if (c == 0) s_slot[tw] = slot;
@@ -222,18 +226,18 @@ __global__ void __launch_bounds__(kWriteThreads) cache_write_kernel(
 
 hipError_t launch_cache_write(const void* k, const void* v, int64_t src_stride, const int64_t* slots, int T,
                               int Hkv, int D, void* k_cache, void* v_cache, int bs, int kv_dtype,
-                              float k_scale, float v_scale, hipStream_t st) {
+                              float k_scale, float v_scale, int64_t n_slots, hipStream_t st) {
     (void)bs;   // validated to be kBlockSize
     const dim3 grid((unsigned)((T + kWriteTokens - 1) / kWriteTokens), (unsigned)Hkv);
     const size_t lds = (size_t)kWriteTokens * D * (kv_dtype == 1 ? 1 : 2);
     if (kv_dtype == 1)
         hipLaunchKernelGGL(cache_write_kernel<true>, grid, dim3(kWriteThreads), lds, st, (const uint16_t*)k,
                            (const uint16_t*)v, src_stride, slots, T, Hkv, D, (uint8_t*)k_cache,
-                           (uint8_t*)v_cache, k_scale, v_scale);
+                           (uint8_t*)v_cache, k_scale, v_scale, n_slots);
     else
         hipLaunchKernelGGL(cache_write_kernel<false>, grid, dim3(kWriteThreads), lds, st, (const uint16_t*)k,
                            (const uint16_t*)v, src_stride, slots, T, Hkv, D, (uint8_t*)k_cache,
-                           (uint8_t*)v_cache, k_scale, v_scale);
+                           (uint8_t*)v_cache, k_scale, v_scale, n_slots);
     return hipGetLastError();
 }
 
@@ -255,7 +259,7 @@ hipError_t launch_cache_write(const void* k, const void* v, int64_t src_stride, 
 __global__ void __launch_bounds__(kWriteThreads) nvfp4_cache_write_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t src_stride,
     const int64_t* __restrict__ slot_mapping, int T, int Hkv, int D, uint8_t* __restrict__ k_cache,
-    uint8_t* __restrict__ v_cache, float k_gscale, float v_gscale) {
+    uint8_t* __restrict__ v_cache, float k_gscale, float v_gscale, int64_t n_slots) {
     extern __shared__ uint32_t lds_w[];
     uint8_t* vt = reinterpret_cast<uint8_t*>(lds_w);   // [D][16] V codes of the window, one per byte
     __shared__ int64_t s_slot[kWriteTokens];
@@ -273,7 +277,11 @@ __global__ void __launch_bounds__(kWriteThreads) nvfp4_cache_write_kernel(
         // the lane reads its token's slot itself, alongside the K/V loads (the
         // source address does not depend on it): one round trip
         const int64_t src = (int64_t)t * src_stride + (int64_t)g * D + grp * 16;
-        const int64_t slot = slot_mapping[t];
+        int64_t slot = slot_mapping[t];
+        if (KVQ_CHECK && slot >= n_slots) {
+            check_fail(kCheckSlot);
+            slot = -1;
+        }
         const u32x4 k0 = *reinterpret_cast<const u32x4*>(k + src), k1 = *reinterpret_cast<const u32x4*>(k + src + 8);
         const u32x4 v0 = *reinterpret_cast<const u32x4*>(v + src), v1 = *reinterpret_cast<const u32x4*>(v + src + 8);
         if (grp == 0) s_slot[tw] = slot;
@@ -319,11 +327,11 @@ __global__ void __launch_bounds__(kWriteThreads) nvfp4_cache_write_kernel(
 
 hipError_t launch_nvfp4_cache_write(const void* k, const void* v, int64_t src_stride, const int64_t* slots, int T,
                                     int Hkv, int D, void* k_cache, void* v_cache, float k_gscale, float v_gscale,
-                                    hipStream_t st) {
+                                    int64_t n_slots, hipStream_t st) {
     const dim3 grid((unsigned)((T + kWriteTokens - 1) / kWriteTokens), (unsigned)Hkv);
     hipLaunchKernelGGL(nvfp4_cache_write_kernel, grid, dim3(kWriteThreads), (size_t)kWriteTokens * D, st,
                        (const uint16_t*)k, (const uint16_t*)v, src_stride, slots, T, Hkv, D, (uint8_t*)k_cache,
-                       (uint8_t*)v_cache, k_gscale, v_gscale);
+                       (uint8_t*)v_cache, k_gscale, v_gscale, n_slots);
     return hipGetLastError();
 }
 
@@ -337,6 +345,10 @@ __global__ void __launch_bounds__(256) block_copy_kernel(const u32x4* __restrict
                                                          int64_t words, int gather) {
     for (int i = blockIdx.x; i < n; i += gridDim.x) {
         const int64_t blk = ids[i];
+        if (KVQ_CHECK && blk < 0) {   // (the copy calls take no block count: only the sign is checked)
+            if (threadIdx.x == 0) check_fail(kCheckBlockId);
+            continue;
+        }
         const u32x4* s = src + (gather ? blk : (int64_t)i) * words;
         u32x4* d = dst + (gather ? (int64_t)i : blk) * words;
         for (int64_t w = threadIdx.x; w < words; w += blockDim.x) d[w] = s[w];
@@ -364,6 +376,21 @@ __global__ void __launch_bounds__(256) e2m1_decode_kernel(const uint8_t* __restr
 hipError_t launch_e2m1_decode(const uint8_t* codes, uint32_t scale_code, void* out, int64_t n, hipStream_t st) {
     hipLaunchKernelGGL(e2m1_decode_kernel, dim3(grid_for(n)), dim3(256), 0, st, codes, scale_code, (f16x2*)out, n);
     return hipGetLastError();
+}
+
+unsigned check_flags_cache(bool clear) {
+#if KVQ_CHECK
+    unsigned v = 0;
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_check_flags), sizeof(v)) != hipSuccess) return ~0u;
+    if (clear) {
+        const unsigned z = 0;
+        if (hipMemcpyToSymbol(HIP_SYMBOL(g_check_flags), &z, sizeof(z)) != hipSuccess) return ~0u;
+    }
+    return v;
+#else
+    (void)clear;
+    return 0;
+#endif
 }
 
 }  // namespace kvq

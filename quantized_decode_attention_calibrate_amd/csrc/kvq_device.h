@@ -6,6 +6,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#ifndef KVQ_CHECK
+#define KVQ_CHECK 0   // 1: device-side checks of the caller's data contract (kvq_internal.h)
+#endif
+
 namespace kvq {
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -150,5 +154,14 @@ __device__ __forceinline__ float shfl_xor(float v, int mask) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+#if KVQ_CHECK
+// One flag word per translation unit (a static device variable; read on the
+// host with hipMemcpyFromSymbol by that unit's check_flags_* function).
+static __device__ unsigned g_check_flags;
+__device__ __forceinline__ void check_fail(unsigned bit) { atomicOr(&g_check_flags, bit); }
+#else
+__device__ __forceinline__ void check_fail(unsigned) {}
+#endif
 
 }  // namespace kvq

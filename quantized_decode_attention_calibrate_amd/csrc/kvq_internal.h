@@ -24,6 +24,21 @@ constexpr int kMaxQueryLen = 16;   // queries per sequence of a multi-query deco
 enum : int { kFmtBF16 = 0, kFmtFP8 = 1, kFmtNVFP4 = 2, kFmtFP8QP = 3 };
 constexpr int kBlockSize = 16;
 
+// Device-side checks of the caller's data contract, compiled in only with
+// -DKVQ_CHECK=1 (libkvq_check.so): block-table entries in [0, num_blocks),
+// sequence lengths in [0, max_seq_len], slots below num_blocks * block_size
+// (and block-copy ids >= 0).  A violation sets a bit in the translation
+// unit's device flag word and the access is replaced by a safe one (block 0,
+// a clamped length, a skipped write).
+#ifndef KVQ_CHECK
+#define KVQ_CHECK 0
+#endif
+enum : unsigned { kCheckBlockId = 1u, kCheckSeqLen = 2u, kCheckSlot = 4u };
+// Flag words of the kernel translation units: OR of the set bits; clear = zero
+// them afterwards.  Synchronous copies (0 when compiled without checks).
+unsigned check_flags_attn(bool clear);
+unsigned check_flags_cache(bool clear);
+
 struct DecodeArgs {
     const uint16_t* q;           // bf16 [B][q_len][Hq][D]
     const uint8_t* k_cache;      // FP8 or BF16 paged K cache (bytes)
@@ -51,6 +66,9 @@ struct DecodeArgs {
     int64_t new_stride;
     const int64_t* new_slots;
     float k_scale_w, v_scale_w;  // cache quantization scales of the write (FP8)
+    // the caller's bounds (read by the checked build only)
+    int num_blocks;
+    int max_seq_len;
 };
 
 // Workspace: [ml: B*Hq*S*2 f32][acc: B*Hq*S*D f32], the second region starting
@@ -63,12 +81,13 @@ hipError_t launch_amax_bf16(const void* x, int64_t rows, int64_t cols, int64_t s
                             hipStream_t st);
 hipError_t launch_e4m3_encode(const float* y, uint8_t* codes, int64_t n, hipStream_t st);
 hipError_t launch_e4m3_decode(const uint8_t* codes, void* out, int kind, int64_t n, hipStream_t st);
+// n_slots = num_blocks * block_size (slots at or past it: a contract violation)
 hipError_t launch_cache_write(const void* k, const void* v, int64_t src_stride, const int64_t* slots, int T,
                               int Hkv, int D, void* k_cache, void* v_cache, int bs, int kv_dtype,
-                              float k_scale, float v_scale, hipStream_t st);
+                              float k_scale, float v_scale, int64_t n_slots, hipStream_t st);
 hipError_t launch_nvfp4_cache_write(const void* k, const void* v, int64_t src_stride, const int64_t* slots, int T,
                                     int Hkv, int D, void* k_cache, void* v_cache, float k_gscale, float v_gscale,
-                                    hipStream_t st);
+                                    int64_t n_slots, hipStream_t st);
 hipError_t launch_block_copy(const void* src, void* dst, const int32_t* ids, int n, size_t block_bytes, int gather,
                              hipStream_t st);
 hipError_t launch_e2m1_decode(const uint8_t* codes, uint32_t scale_code, void* out, int64_t n, hipStream_t st);

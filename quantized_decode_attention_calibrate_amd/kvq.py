@@ -12,6 +12,9 @@ import torch  # must be loaded first: libkvq binds to the HIP runtime torch ship
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("KVQ_LIBRARY") or os.path.join(_PKG, "libkvq.so")
+# the same library with device-side checks of the caller's data (kvq_check_flags)
+CHECK_LIB_PATH = os.path.join(_PKG, "libkvq_check.so")
+KVQ_CHECK_BLOCK_ID, KVQ_CHECK_SEQ_LEN, KVQ_CHECK_SLOT = 1, 2, 4
 
 KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_EWORKSPACE, KVQ_EHIP = 0, -1, -2, -3, -4
 KVQ_KV_BF16, KVQ_KV_FP8_E4M3 = 0, 1
@@ -29,15 +32,16 @@ class KvqError(RuntimeError):
         self.status = status
 
 
-def _load() -> ctypes.CDLL:
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m quantized_decode_attention_calibrate_amd.build`")
-    L = ctypes.CDLL(LIB_PATH)
+def _load(path: str) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m quantized_decode_attention_calibrate_amd.build`")
+    L = ctypes.CDLL(path)
     P, I, I64, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     sig = {
         "kvq_strerror": (ctypes.c_char_p, [I]),
         "kvq_last_hip_error": (I, []),
         "kvq_abi_version": (I, []),
+        "kvq_check_flags": (I, [P, I]),
         "kvq_e4m3_encode_f32": (I, [P, P, I64, P]),
         "kvq_e4m3_decode": (I, [P, P, I, I64, P]),
         "kvq_amax_bf16": (I, [P, I64, I64, I64, P, P]),
@@ -80,11 +84,24 @@ def _load() -> ctypes.CDLL:
     return L
 
 
-_lib = _load()
+_lib = _load(LIB_PATH)
 
 
 def lib() -> ctypes.CDLL:
     return _lib
+
+
+def open_library(path: str = CHECK_LIB_PATH) -> ctypes.CDLL:
+    """Another handle with the same signatures, e.g. the checked build (its
+    calls take raw pointers, as lib()'s do)."""
+    return _load(path)
+
+
+def kvq_check_flags(clear: bool = True, L: ctypes.CDLL = None) -> int:
+    """Contract-violation bits of a checked library (synchronous)."""
+    flags = ctypes.c_uint(0)
+    _check("kvq_check_flags", (L or _lib).kvq_check_flags(ctypes.byref(flags), 1 if clear else 0))
+    return flags.value
 
 
 def _stream(stream) -> int:

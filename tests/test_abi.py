@@ -36,10 +36,23 @@ def declared_functions():
 def test_every_declared_symbol_is_exported(K):
     names = declared_functions()
     assert len(names) >= 12
+    checked = K.open_library(K.CHECK_LIB_PATH)   # the build with device-side contract checks
     for n in names:
         assert hasattr(K.lib(), n), n
+        assert hasattr(checked, n), n
+
+
+def test_check_flags_host_side(K):
+    """The release library has no checks; a NULL output is rejected before any
+    HIP call in both builds."""
+    flags = ctypes.c_uint(7)
+    assert K.lib().kvq_check_flags(ctypes.byref(flags), 1) == K.KVQ_EUNSUPPORTED and flags.value == 0
+    with pytest.raises(K.KvqError):
+        K.kvq_check_flags()
+    assert K.lib().kvq_check_flags(None, 0) == K.KVQ_EINVAL
+    assert K.open_library(K.CHECK_LIB_PATH).kvq_check_flags(None, 0) == K.KVQ_EINVAL
     want = int(re.search(r"#define KVQ_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
-    assert K.kvq_abi_version() == want == 2
+    assert K.kvq_abi_version() == want == 3
     assert K.kvq_strerror(-3) == "workspace too small"
 
 
