@@ -17,21 +17,30 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kvq_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "libkvq_oracle.so")
+# KVQ_ORACLE_SANITIZE=1 selects the AddressSanitizer + UndefinedBehaviorSanitizer
+# build (its process must preload gcc's libasan; tests/test_oracle_sanitizers.py)
+SANITIZED = os.environ.get("KVQ_ORACLE_SANITIZE") == "1"
+_PLAIN_LIB = os.path.join(_HERE, "libkvq_oracle.so")
+_SAN_LIB = os.path.join(_HERE, "libkvq_oracle_san.so")
+_LIB_PATH = _SAN_LIB if SANITIZED else _PLAIN_LIB
+_SAN_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+              "-fno-sanitize-recover=all"]
 
 KV_BF16, KV_FP8, KV_NVFP4 = 0, 1, 2
 
 
-def build(force: bool = False) -> str:
-    """Compile the oracle with gcc (no fast-math, no fp contraction)."""
-    if force or not os.path.exists(_LIB_PATH) or (
-        os.path.getmtime(_LIB_PATH) < max(os.path.getmtime(_SRC),
-                                          os.path.getmtime(os.path.join(_HERE, "kvq_oracle.h")))):
-        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off",
+def build(force: bool = False, sanitize: bool = SANITIZED) -> str:
+    """Compile the oracle with gcc (no fast-math, no fp contraction); with
+    sanitize, the instrumented variant."""
+    path = _SAN_LIB if sanitize else _PLAIN_LIB
+    if force or not os.path.exists(path) or (
+        os.path.getmtime(path) < max(os.path.getmtime(_SRC), os.path.getmtime(os.path.join(_HERE, "kvq_oracle.h")))):
+        tmp = path + ".tmp%d" % os.getpid()
+        opt = _SAN_FLAGS if sanitize else ["-O2"]
+        subprocess.check_call(["gcc", *opt, "-std=c99", "-fPIC", "-shared", "-ffp-contract=off",
                                "-fno-fast-math", "-Wall", "-o", tmp, _SRC, "-lm", "-lpthread"])
-        os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+        os.replace(tmp, path)
+    return path
 
 
 _lib = None
