@@ -41,11 +41,27 @@ KERNEL_SOURCES = ["quantized_decode_attention_calibrate_amd/csrc/kvq_attn.hip",
                   "quantized_decode_attention_calibrate_amd/build.py"]   # (its compiler flags)
 
 
+def _code_only(text: str, python: bool) -> str:
+    """The text without comments and blank space, so that editing a comment
+    does not mark the compiled kernel as changed."""
+    import re
+    if python:
+        text = re.sub(r'"""(?:.|\n)*?"""', "", text)
+        text = re.sub(r"#[^\n]*", "", text)
+    else:
+        text = re.sub(r"/\*(?:.|\n)*?\*/", "", text)
+        text = re.sub(r"//[^\n]*", "", text)
+    return re.sub(r"\s+", " ", text).strip()
+
+
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources and build flags (code only; comments and
+    whitespace do not count).  A stored traffic summary is used only while it
+    matches."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            h.update(_code_only(f.read(), p.endswith(".py")).encode())
     return h.hexdigest()[:16]
 
 

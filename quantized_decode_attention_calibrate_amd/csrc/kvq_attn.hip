@@ -13,11 +13,11 @@
 // levels are the per-split online softmax (fp32 m, l, acc) and the fp32
 // log-sum-exp merge across splits.
 //
-// Work decomposition (MI355X: 256 CUs, wave64): one work-group of 4 waves per
-// (split s, KV head g, sequence b).  A split is a fixed range of logical
-// tokens (a multiple of 64), so results do not depend on physical block
-// placement.  Each wave walks 64-token chunks (4 blocks of 16) of the split
-// round-robin; the 4 waves merge through LDS and write one fp32 partial
+// Work decomposition (MI355X: 256 CUs, wave64): one work-group of 4 waves (8
+// for NVFP4 at D 64) per (split s, KV head g, sequence b).  A split is a
+// fixed range of logical tokens (a multiple of 64), so results do not depend
+// on physical block placement.  Each wave walks 64-token chunks (4 blocks of
+// 16) of the split round-robin; the waves merge through LDS and write one fp32 partial
 // (m, l, acc[G][D]) per head to the workspace; the merge kernel combines the
 // splits and applies v_scale.
 //
