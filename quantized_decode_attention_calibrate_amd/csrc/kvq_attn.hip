@@ -368,8 +368,7 @@ __device__ __forceinline__ void mfma_process(MfmaState<D, NT>& st, MfmaChunk<D, 
         float mloc = sv[nt][0];
 #pragma unroll
         for (int e = 1; e < 16; ++e) mloc = fmaxf(mloc, sv[nt][e]);
-        mloc = fmaxf(mloc, shfl_xor(mloc, 16));
-        mloc = fmaxf(mloc, shfl_xor(mloc, 32));
+        mloc = max_xor32(max_xor16(mloc));
         const float m_new = fmaxf(st.m_run[nt], mloc * cs[nt]);
         const bool keep = m_new <= st.m_run[nt] + kLazy;
         const float m_ref = keep ? st.m_run[nt] : m_new;
@@ -538,8 +537,7 @@ __device__ __forceinline__ void mfma_process_qp8(MfmaState<D, NT>& st, MfmaChunk
         float mloc = sv[nt][0];
 #pragma unroll
         for (int e = 1; e < 16; ++e) mloc = fmaxf(mloc, sv[nt][e]);
-        mloc = fmaxf(mloc, shfl_xor(mloc, 16));
-        mloc = fmaxf(mloc, shfl_xor(mloc, 32));
+        mloc = max_xor32(max_xor16(mloc));
         const float r_new = fmaxf(st.m_run[nt], __builtin_ceilf(mloc * cs));   // integer-valued
         const float r_use = r_new == -INFINITY ? 0.f : r_new;
         alpha[nt] = st.m_run[nt] == -INFINITY ? 0.f : __builtin_ldexpf(1.0f, (int)(st.m_run[nt] - r_use));
@@ -740,8 +738,7 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     qmax = fmaxf(qmax, fmaxf(__builtin_fabsf(bf16_lo(qw[k][e])), __builtin_fabsf(bf16_hi(qw[k][e]))));
-            qmax = fmaxf(qmax, shfl_xor(qmax, 16));
-            qmax = fmaxf(qmax, shfl_xor(qmax, 32));
+            qmax = max_xor32(max_xor16(qmax));
             // exponent of qmax: qmax = m * 2^ex with m in [0.5, 1)
             const int ex = qmax > 0.f ? __builtin_amdgcn_frexp_expf(qmax) : 0;
             const int qs = min(14 - ex, 100);   // denormal-only rows stay finite
@@ -881,8 +878,7 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
     for (int nt = 0; nt < NT; ++nt) {
         float l_run = st.l_run[nt];
         if constexpr (FMT != kFmtFP8QP) {   // (the FP8 Q/P path already holds whole column sums)
-            l_run += shfl_xor(l_run, 16);
-            l_run += shfl_xor(l_run, 32);
+            l_run = sum_xor32(sum_xor16(l_run));
         }
         const int c = 16 * nt + n;
         if (grp == 0) {

@@ -155,6 +155,29 @@ __device__ __forceinline__ float shfl_xor(float v, int mask) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Max / sum of a value and the same value 16 (or 32) lanes away, on gfx950's
+// v_permlane16_swap / v_permlane32_swap (plain VALU ops, no LDS round trip as
+// with ds_bpermute).  A swap of a register with itself leaves each lane the
+// pair {v[i], v[i ^ 16]} (or ^ 32) across its two results, in an order that
+// depends on the lane; max and + are commutative, so every lane gets the
+// same bits as from shfl_xor.
+__device__ __forceinline__ float max_xor16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(f32_bits(v), f32_bits(v), false, false);
+    return fmaxf(bits_f32(r[0]), bits_f32(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(f32_bits(v), f32_bits(v), false, false);
+    return fmaxf(bits_f32(r[0]), bits_f32(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(f32_bits(v), f32_bits(v), false, false);
+    return bits_f32(r[0]) + bits_f32(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(f32_bits(v), f32_bits(v), false, false);
+    return bits_f32(r[0]) + bits_f32(r[1]);
+}
+
 #if KVQ_CHECK
 // One flag word per translation unit (a static device variable; read on the
 // host with hipMemcpyFromSymbol by that unit's check_flags_* function).
