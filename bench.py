@@ -343,6 +343,27 @@ def measure_multiquery(torch, K, name, q_lens, steps, warmup):
         rec[f"q_len_{ql}"] = {"attn_us": round(us, 2), "attn_gbps": round(byts / (us * 1e-6) / 1e9, 1),
                               "over_q_len_1": round(us / t1, 3),
                               "kv_tokens_verified_per_s": round(sum(w.seq_lens) * ql / (us * 1e-6), 1)}
+        # the verification step with the q_len new tokens' cache write: one launch
+        # (kvq_paged_decode_attn_mq_append) and the two-launch form (kvq_cache_write,
+        # then kvq_paged_decode_attn_mq)
+        rows = torch.tensor([s0 + n - ql + i for s0, n in zip(w.seq_starts, w.seq_lens) for i in range(ql)],
+                            device="cuda")
+        k_new = w.k[rows].reshape(w.B, ql, w.Hkv, w.D).contiguous()
+        v_new = w.v[rows].reshape(w.B, ql, w.Hkv, w.D).contiguous()
+        slots = w.slot_mapping.to("cuda")[rows].reshape(w.B, ql).contiguous()
+        one = timed(prepared(lambda kc, vc, q=q, out=out, ws=ws: K.kvq_paged_decode_attn_mq_append(
+            k_new, v_new, slots, q, kc, vc, K.KVQ_KV_FP8_E4M3, L.bt, L.sl, w.max_seq_len, w.Hkv, L.ks, L.vs, L.sm,
+            out, ws, prepare=True)))
+        k_flat, v_flat, s_flat = k_new.view(-1, w.Hkv, w.D), v_new.view(-1, w.Hkv, w.D), slots.view(-1)
+
+        def two_launch(kc, vc, q=q, out=out, ws=ws):
+            write = K.kvq_cache_write(k_flat, v_flat, s_flat, kc, vc, K.KVQ_KV_FP8_E4M3, L.ks, L.vs, prepare=True)
+            attend = K.kvq_paged_decode_attn_mq(q, kc, vc, K.KVQ_KV_FP8_E4M3, L.bt, L.sl, w.max_seq_len, w.Hkv,
+                                                L.ks, L.vs, L.sm, out, ws, prepare=True)
+            return lambda: (write(), attend())
+
+        two = timed(prepared(two_launch))
+        rec[f"q_len_{ql}"].update({"step_one_call_us": round(one, 2), "step_two_launch_us": round(two, 2)})
     # FP8 Q and P variant: both products on FP8 MFMA, q_scale calibrated on the queries
     amax = torch.zeros(1, dtype=torch.float32, device="cuda")
     for ql in (1, 4, 8):
@@ -575,10 +596,10 @@ def pmc_summary(fetch_csv, write_csv, workload="gptoss65k"):
     ref = next(k for k in fetch if k.startswith("e4m3_decode_kernel"))
     fscale = PMC_REF_CODES / (med(fetch[ref]) * 1024)
     wscale = 2 * PMC_REF_CODES / (med(write[ref]) * 1024)
-    # the step's call: the fused append instantiation of the decode kernel (template
-    # argument APPEND = true) and the merge; the plain decode call is listed beside it
-    fused = [k for k in fetch if k.startswith("decode_mfma_kernel") and k.endswith("true>")]
-    plain = [k for k in fetch if k.startswith("decode_mfma_kernel") and not k.endswith("true>")]
+    # the step's call: the one-token append instantiation of the decode kernel (last
+    # template argument, the append mode, 1) and the merge; the plain call (mode 0) beside it
+    fused = [k for k in fetch if k.startswith("decode_mfma_kernel") and k.endswith(",1>")]
+    plain = [k for k in fetch if k.startswith("decode_mfma_kernel") and k.endswith(",0>")]
     mrg = [k for k in fetch if k.startswith("merge_")]
     f_kib = {k: med(fetch[k]) for k in fused + plain + mrg}
     w_kib = {k: med(write[k]) for k in fused + plain + mrg}

@@ -55,8 +55,9 @@ extern "C" {
 
 /* 2: multi-query and sliding-window decode, FP8 Q/P variant, fused append,
  *    host-memory block tier
- * 3: kvq_check_flags and the checked build libkvq_check.so */
-#define KVQ_ABI_VERSION 3
+ * 3: kvq_check_flags and the checked build libkvq_check.so
+ * 4: kvq_paged_decode_attn_mq_append */
+#define KVQ_ABI_VERSION 4
 
 enum kvq_status {
     KVQ_OK = 0,
@@ -348,6 +349,37 @@ int kvq_nvfp4_paged_decode_attn_mq(const void* q_dev, int q_len, int window, con
                                    void* out_dev, int out_dtype,
                                    void* workspace_dev, size_t workspace_bytes, void* hip_stream,
                                    int split_tokens);
+/* kvq_paged_decode_attn_mq_append: the speculative-verification step in one
+ * launch, the same result as kvq_cache_write of the q_len new tokens of every
+ * sequence followed by kvq_paged_decode_attn_mq (FP8 or BF16, MFMA family):
+ * the drafted tokens' K/V go into the cache and all q_len of them are
+ * verified against it.
+ *   k_new_dev, v_new_dev  bf16 rows [B * q_len][Hkv][D]; new token i of
+ *                         sequence b (position seq_lens[b] - q_len + i) is row
+ *                         b * q_len + i, starting at (b * q_len + i) *
+ *                         new_token_stride elements; 16-B aligned
+ *   slot_mapping_dev      int64 [B][q_len]: slot of new token i of sequence
+ *                         b, which must be the slot of its position in
+ *                         block_tables; < 0 writes nothing for that token, and
+ *                         neither does a position below 0 (a sequence shorter
+ *                         than q_len)
+ *   q_dev                 bf16 [B][q_len][Hq][D], the new tokens' queries
+ *   the rest              as kvq_paged_decode_attn_mq (window >= 0), with its
+ *                         workspace (kvq_decode_workspace_bytes_mq)
+ * Each new token is quantized and stored by the work-group and wave that
+ * read its block (the token's 64-token chunk of its split; q_len <= 16, so a
+ * wave writes tokens of one chunk only, its last), before that wave reads it.
+ * The new tokens' blocks must not be read by other sequences in the call
+ * (the sequence's own last blocks).  Errors as kvq_cache_write and
+ * kvq_paged_decode_attn_mq. */
+int kvq_paged_decode_attn_mq_append(const void* k_new_dev, const void* v_new_dev, int64_t new_token_stride,
+                                    const int64_t* slot_mapping_dev, const void* q_dev, int q_len, int window,
+                                    void* k_cache_dev, void* v_cache_dev, int kv_dtype,
+                                    const int32_t* block_tables_dev, int max_blocks_per_seq,
+                                    const int32_t* seq_lens_dev, int max_seq_len, int B, int Hq, int Hkv, int D,
+                                    int block_size, int num_blocks, float k_scale, float v_scale, float sm_scale,
+                                    void* out_dev, int out_dtype, void* workspace_dev, size_t workspace_bytes,
+                                    void* hip_stream, int split_tokens);
 
 /* ---- FP8 Q and P variant -------------------------------------------------------
  * The Radiance FP8 guide observes Q maxima alongside K and V and names a

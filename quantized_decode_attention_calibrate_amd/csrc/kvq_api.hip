@@ -448,6 +448,27 @@ int kvq_paged_decode_attn_append(const void* k_new_dev, const void* v_new_dev, i
                          workspace_bytes, hip_stream, KVQ_IMPL_MFMA, split_tokens, 1.0f, &app);
 }
 
+int kvq_paged_decode_attn_mq_append(const void* k_new_dev, const void* v_new_dev, int64_t new_token_stride,
+                                    const int64_t* slot_mapping_dev, const void* q_dev, int q_len, int window,
+                                    void* k_cache_dev, void* v_cache_dev, int kv_dtype,
+                                    const int32_t* block_tables_dev, int max_blocks_per_seq,
+                                    const int32_t* seq_lens_dev, int max_seq_len, int B, int Hq, int Hkv, int D,
+                                    int block_size, int num_blocks, float k_scale, float v_scale, float sm_scale,
+                                    void* out_dev, int out_dtype, void* workspace_dev, size_t workspace_bytes,
+                                    void* hip_stream, int split_tokens) {
+    if (kv_dtype != KVQ_KV_BF16 && kv_dtype != KVQ_KV_FP8_E4M3) return KVQ_EINVAL;
+    if (B > 0) {
+        if (!k_new_dev || !v_new_dev || !slot_mapping_dev) return KVQ_EINVAL;
+        if (new_token_stride < (int64_t)Hkv * D || (new_token_stride & 7) != 0) return KVQ_EINVAL;
+        if (!aligned16(k_new_dev) || !aligned16(v_new_dev)) return KVQ_EINVAL;
+    }
+    const AppendArgs app = {k_new_dev, v_new_dev, new_token_stride, slot_mapping_dev};
+    return decode_common(kv_dtype == KVQ_KV_FP8_E4M3 ? kFmtFP8 : kFmtBF16, q_dev, q_len, window, k_cache_dev,
+                         v_cache_dev, block_tables_dev, max_blocks_per_seq, seq_lens_dev, max_seq_len, B, Hq, Hkv, D,
+                         block_size, num_blocks, k_scale, v_scale, sm_scale, out_dev, out_dtype, workspace_dev,
+                         workspace_bytes, hip_stream, KVQ_IMPL_MFMA, split_tokens, 1.0f, &app);
+}
+
 int kvq_nvfp4_paged_decode_attn_append(const void* k_new_dev, const void* v_new_dev, int64_t new_token_stride,
                                        const int64_t* slot_mapping_dev, const void* q_dev, void* k_cache_dev,
                                        void* v_cache_dev, const int32_t* block_tables_dev, int max_blocks_per_seq,

@@ -614,15 +614,19 @@ __device__ __forceinline__ void append_fence() {
     __builtin_amdgcn_s_waitcnt(0);
 }
 
-// APPEND: the fused cache write of each sequence's newest token
-// (kvq_paged_decode_attn_append).  The token's block is read by one
-// work-group only, the one holding the sequence's last split for this KV
+// APPEND: the fused cache write of the new tokens (kvq_paged_decode_attn_append:
+// each sequence's newest token, kAppendOne; kvq_paged_decode_attn_mq_append:
+// its q_len newest, kAppendMany).  A new token's block is read by one
+// work-group only, the one holding the split with that token for this KV
 // head, and within it by the wave whose round-robin share ends with the
 // chunk holding that token.  That wave quantizes the token and stores it
 // right after the block ids are staged, and before it loads that chunk it
 // waits for its own stores (a work-group-scope fence), so the chunk's loads
-// see the new bytes.
-template <int D, int FMT, int NT, int W = mfma_waves<D, FMT, NT>(), bool APPEND = false>
+// see the new bytes.  The one-token case has a kernel of its own: the
+// general writer costs the decode step about 0.2 us at D 64.
+constexpr int kAppendNone = 0, kAppendOne = 1, kAppendMany = 2;
+
+template <int D, int FMT, int NT, int W = mfma_waves<D, FMT, NT>(), int APPEND = kAppendNone>
 __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
     constexpr int KJ = D / 64;
     constexpr int DT = D / 16;
@@ -656,13 +660,40 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
 
     const int lb0 = tok_begin / kBlockSize;
     const int n_chunks = (tok_end - tok_begin + kChunkTokens - 1) / kChunkTokens;
-    // fused append: the newest token's bf16 values, loaded early (consumed after the barrier)
-    const bool writer = APPEND && tok_end == L && wave == (n_chunks - 1) % W;
+    // Fused append.  kAppendOne (a decode step: each sequence's newest token):
+    // the wave owning the split's last chunk writes it, one row over the
+    // wave's lanes.  kAppendMany (a verification step: the q_len new tokens,
+    // positions L - q_len .. L - 1 that are >= 0): they lie in the split's
+    // last two chunks at most (q_len <= 16 < 64), each chunk's tokens written
+    // by the wave owning that chunk, this wave's being [new_lo, new_hi).  For
+    // W >= 2 a written chunk is its wave's last, so the wave writes before that
+    // chunk's first load (append_fence).  The bf16 rows are loaded here, in
+    // flight with the block-id staging, and stored after the barrier.
+    int new_lo = 0, new_hi = 0;
+    if constexpr (APPEND == kAppendMany) {
+        const int p0 = max(max(L - a.q_len, 0), tok_begin);   // new tokens of this split: [p0, tok_end)
+        if (p0 < tok_end) {
+            const int c0 = (p0 - tok_begin) / kChunkTokens, c1 = (tok_end - 1 - tok_begin) / kChunkTokens;
+            const int c = c0 % W == wave ? c0 : (c1 % W == wave ? c1 : -1);
+            if (c >= 0) {
+                new_lo = max(p0, tok_begin + c * kChunkTokens);
+                new_hi = min(tok_end, tok_begin + (c + 1) * kChunkTokens);
+            }
+        }
+    }
+    const bool writer = APPEND == kAppendOne ? tok_end == L && wave == (n_chunks - 1) % W
+                                             : APPEND == kAppendMany && new_lo < new_hi;
     constexpr int NG = D / 16;                 // NVFP4 blocks per (token, head) row
-    uint16_t k_new[D / 64], v_new[D / 64];     // FP8 / BF16: dims lane + 64 r
-    u32x4 n_w0 = {}, n_w1 = {};                // NVFP4: lane < NG: K block lane; lane < 2 NG: V block lane - NG
-    int64_t new_slot = -1;
-    if constexpr (APPEND) {
+    uint16_t k_one[D / 64], v_one[D / 64];     // kAppendOne, FP8 / BF16: dims lane + 64 r
+    u32x4 n_w0 = {}, n_w1 = {};                // kAppendOne, NVFP4: lane < NG: K block lane; lane < 2 NG: V block
+    int64_t new_slot = -1;                     // kAppendOne
+    // kAppendMany: token new_lo + k, dims [E lane, E lane + E) of its row (kE
+    // 32-bit words; at D 64 the aligned pair holding the lane's dim); lane
+    // t < new_hi - new_lo holds token new_lo + t's slot
+    constexpr int E = D / 64, kE = (E + 1) / 2, kMany = APPEND == kAppendMany ? kMaxQueryLen : 1;
+    uint32_t nk[kMany][kE], nv[kMany][kE];
+    int64_t ns = -1;
+    if constexpr (APPEND == kAppendOne) {
         if (writer) {
             new_slot = a.new_slots[b];
             if (KVQ_CHECK && new_slot >= (int64_t)a.num_blocks * kBlockSize) {
@@ -679,8 +710,38 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
             } else {
 #pragma unroll
                 for (int r = 0; r < D / 64; ++r) {
-                    k_new[r] = a.k_new[row + lane + 64 * r];
-                    v_new[r] = a.v_new[row + lane + 64 * r];
+                    k_one[r] = a.k_new[row + lane + 64 * r];
+                    v_one[r] = a.v_new[row + lane + 64 * r];
+                }
+            }
+        }
+    } else if constexpr (APPEND == kAppendMany) {
+        if (writer) {
+            const int i0 = new_lo - (L - a.q_len);   // index of token new_lo among the q_len new tokens
+            if (lane < new_hi - new_lo) {
+                ns = a.new_slots[(int64_t)b * a.q_len + i0 + lane];
+                if (KVQ_CHECK && ns >= (int64_t)a.num_blocks * kBlockSize) {
+                    check_fail(kCheckSlot);
+                    ns = -1;
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < kMany; ++k) {
+                if (k < new_hi - new_lo) {
+                    const int64_t row = ((int64_t)b * a.q_len + i0 + k) * a.new_stride + (int64_t)g * D + E * lane;
+                    if constexpr (E == 1) {
+                        nk[k][0] = *reinterpret_cast<const uint32_t*>(a.k_new + (row & ~(int64_t)1));
+                        nv[k][0] = *reinterpret_cast<const uint32_t*>(a.v_new + (row & ~(int64_t)1));
+                    } else if constexpr (E == 2) {
+                        nk[k][0] = *reinterpret_cast<const uint32_t*>(a.k_new + row);
+                        nv[k][0] = *reinterpret_cast<const uint32_t*>(a.v_new + row);
+                    } else {
+                        static_assert(E == 4, "D is 64, 128 or 256");
+                        const u32x2 kw = *reinterpret_cast<const u32x2*>(a.k_new + row);
+                        const u32x2 vw = *reinterpret_cast<const u32x2*>(a.v_new + row);
+                        nk[k][0] = kw[0], nk[k][1] = kw[1];
+                        nv[k][0] = vw[0], nv[k][1] = vw[1];
+                    }
                 }
             }
         }
@@ -763,12 +824,12 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
     const int head_until = a.window > 0 ? max(0, L - a.window) : 0;   // the newest query's window start
     __syncthreads();
     if constexpr (APPEND) {
-        if (writer && new_slot >= 0) {   // the cache write's quantizer, element by element
-            const int64_t blk = new_slot / kBlockSize;
-            const int off = (int)(new_slot - blk * kBlockSize);
-            uint8_t* kc = const_cast<uint8_t*>(a.k_cache);
-            uint8_t* vc = const_cast<uint8_t*>(a.v_cache);
-            if constexpr (FMT == kFmtNVFP4) {
+        uint8_t* kc = const_cast<uint8_t*>(a.k_cache);
+        uint8_t* vc = const_cast<uint8_t*>(a.v_cache);
+        if constexpr (FMT == kFmtNVFP4) {
+            if (writer && new_slot >= 0) {   // the cache write's quantizer
+                const int64_t blk = new_slot / kBlockSize;
+                const int off = (int)(new_slot - blk * kBlockSize);
                 // one lane per block: K codes are a whole token row; a V code byte holds
                 // this token's nibble and the other slot's of the pair, which this
                 // work-group alone touches in the call, so it is read, merged and stored
@@ -795,7 +856,11 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
                         }
                     }
                 }
-            } else {
+            }
+        } else if constexpr (APPEND == kAppendOne) {
+            if (writer && new_slot >= 0) {   // the cache write's quantizer, element by element
+                const int64_t blk = new_slot / kBlockSize;
+                const int off = (int)(new_slot - blk * kBlockSize);
 #pragma unroll
                 for (int r = 0; r < D / 64; ++r) {
                     const int d = lane + 64 * r;
@@ -803,11 +868,70 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
                     const int64_t vi = ((blk * a.Hkv + g) * D + d) * kBlockSize + off;   // [blk][g][d][off]
                     if constexpr (FMT == kFmtFP8) {
 #pragma clang fp contract(off)
-                        kc[ki] = (uint8_t)e4m3_encode(bits_f32((uint32_t)k_new[r] << 16) / a.k_scale_w);
-                        vc[vi] = (uint8_t)e4m3_encode(bits_f32((uint32_t)v_new[r] << 16) / a.v_scale_w);
+                        kc[ki] = (uint8_t)e4m3_encode(bits_f32((uint32_t)k_one[r] << 16) / a.k_scale_w);
+                        vc[vi] = (uint8_t)e4m3_encode(bits_f32((uint32_t)v_one[r] << 16) / a.v_scale_w);
                     } else {
-                        reinterpret_cast<uint16_t*>(kc)[ki] = k_new[r];
-                        reinterpret_cast<uint16_t*>(vc)[vi] = v_new[r];
+                        reinterpret_cast<uint16_t*>(kc)[ki] = k_one[r];
+                        reinterpret_cast<uint16_t*>(vc)[vi] = v_one[r];
+                    }
+                }
+            }
+        } else if (writer) {
+            // the same quantizer: K rows [blk][g][off][d] take this lane's E
+            // contiguous dims, V columns [blk][g][d][off] one element per dim.
+            // One wait for the rows and slots first (vmcnt 0, the other counters
+            // untouched), on every path into the loop: otherwise each token's
+            // first use waits there, and with the previous token's stores then
+            // outstanding that wait is a full write round trip per token
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+#pragma unroll
+            for (int k = 0; k < kMany; ++k) {
+                if (k < new_hi - new_lo) {
+                    const uint32_t s_lo = __builtin_amdgcn_readlane((uint32_t)ns, k);
+                    const uint32_t s_hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)ns >> 32), k);
+                    const int64_t slot = (int64_t)(((uint64_t)s_hi << 32) | s_lo);
+                    if (slot >= 0) {
+                        const int64_t blk = slot / kBlockSize;
+                        const int off = (int)(slot - blk * kBlockSize);
+                        const int64_t ki = ((blk * a.Hkv + g) * kBlockSize + off) * D + E * lane;
+                        const int64_t vi = ((blk * a.Hkv + g) * D + E * lane) * kBlockSize + off;
+                        // this lane's E values: bf16 halves of its words (at D 64 the
+                        // half of the pair that holds its dim)
+                        uint32_t kh[E], vh[E];
+#pragma unroll
+                        for (int j = 0; j < E; ++j) {
+                            const bool hi = (E == 1 ? lane : j) & 1;
+                            kh[j] = hi ? nk[k][j / 2] >> 16 : nk[k][j / 2] & 0xFFFFu;
+                            vh[j] = hi ? nv[k][j / 2] >> 16 : nv[k][j / 2] & 0xFFFFu;
+                        }
+                        if constexpr (FMT == kFmtFP8) {
+#pragma clang fp contract(off)
+                            uint32_t kb[E];
+#pragma unroll
+                            for (int j = 0; j < E; ++j) {
+                                kb[j] = e4m3_encode(bits_f32(kh[j] << 16) / a.k_scale_w);
+                                vc[vi + (int64_t)j * kBlockSize] = (uint8_t)e4m3_encode(bits_f32(vh[j] << 16) / a.v_scale_w);
+                            }
+                            if constexpr (E == 1) {
+                                kc[ki] = (uint8_t)kb[0];
+                            } else if constexpr (E == 2) {
+                                *reinterpret_cast<uint16_t*>(kc + ki) = (uint16_t)(kb[0] | kb[1] << 8);
+                            } else {
+                                *reinterpret_cast<uint32_t*>(kc + ki) = kb[0] | kb[1] << 8 | kb[2] << 16 | kb[3] << 24;
+                            }
+                        } else {
+                            uint16_t* k16 = reinterpret_cast<uint16_t*>(kc);
+                            uint16_t* v16 = reinterpret_cast<uint16_t*>(vc);
+                            if constexpr (E == 1) {
+                                k16[ki] = (uint16_t)kh[0];
+                            } else if constexpr (E == 2) {
+                                *reinterpret_cast<uint32_t*>(k16 + ki) = nk[k][0];
+                            } else {
+                                *reinterpret_cast<u32x2*>(k16 + ki) = u32x2{nk[k][0], nk[k][1]};
+                            }
+#pragma unroll
+                            for (int j = 0; j < E; ++j) v16[vi + (int64_t)j * kBlockSize] = (uint16_t)vh[j];
+                        }
                     }
                 }
             }
@@ -1173,11 +1297,18 @@ static hipError_t launch_family(const DecodeArgs& a, int B, int impl, hipStream_
     constexpr int W = mfma_waves<D, FMT, NT>();
     const int GQ = a.G * a.q_len;
     const size_t lds_mfma = sizeof(float) * (kMaxSplitBlocks + lds_merge_floats(GQ, D, W, NT));
-    if (a.k_new) {   // fused append: single-query FP8 / BF16 / NVFP4 on the MFMA family only
-        if constexpr ((FMT == kFmtFP8 || FMT == kFmtBF16 || FMT == kFmtNVFP4) && NT == 1)
-            hipLaunchKernelGGL((decode_mfma_kernel<D, FMT, NT, W, true>), grid, dim3(W * 64), lds_mfma, st, a);
-        else
+    if (a.k_new) {   // fused append (MFMA family): one new token, or FP8 / BF16 up to kMaxQueryLen
+        constexpr bool kOne = NT == 1 && (FMT == kFmtFP8 || FMT == kFmtBF16 || FMT == kFmtNVFP4);
+        constexpr bool kMany = FMT == kFmtFP8 || FMT == kFmtBF16;
+        if (kOne && a.q_len == 1) {
+            if constexpr (kOne)
+                hipLaunchKernelGGL((decode_mfma_kernel<D, FMT, NT, W, kAppendOne>), grid, dim3(W * 64), lds_mfma, st,
+                                   a);
+        } else if constexpr (kMany) {
+            hipLaunchKernelGGL((decode_mfma_kernel<D, FMT, NT, W, kAppendMany>), grid, dim3(W * 64), lds_mfma, st, a);
+        } else {
             return hipErrorInvalidValue;
+        }
     } else if (FMT == kFmtNVFP4 || FMT == kFmtFP8QP || impl == 2 || NT > 1) {
         hipLaunchKernelGGL((decode_mfma_kernel<D, FMT, NT>), grid, dim3(W * 64), lds_mfma, st, a);
     } else {

@@ -76,6 +76,8 @@ def _load(path: str) -> ctypes.CDLL:
                                          I]),
         "kvq_nvfp4_paged_decode_attn_mq": (I, [P, I, I, P, P, P, I, P, I, I, I, I, I, I, I, F, F, F, P, I, P, SZ,
                                                P, I]),
+        "kvq_paged_decode_attn_mq_append": (I, [P, P, I64, P, P, I, I, P, P, I, P, I, P, I, I, I, I, I, I, I, F, F,
+                                                F, P, I, P, SZ, P, I]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -387,6 +389,33 @@ def kvq_paged_decode_attn_mq(q: torch.Tensor, k_cache: torch.Tensor, v_cache: to
         _ptr(out), out_dtype, _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream),
         split_tokens),
         prepare, (q, k_cache, v_cache, block_tables, seq_lens, out, workspace))
+
+
+def kvq_paged_decode_attn_mq_append(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+                                    q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_dtype: int,
+                                    block_tables: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, Hkv: int,
+                                    k_scale: float, v_scale: float, sm_scale: float, out: torch.Tensor,
+                                    workspace: torch.Tensor, split_tokens: int = 0, window: int = 0, stream=None,
+                                    prepare: bool = False):
+    """kvq_cache_write of the q_len new tokens of every sequence followed by
+    kvq_paged_decode_attn_mq, in one launch.  k_new, v_new bf16 [B][q_len][Hkv][D]
+    (token rows may be strided); slot_mapping int64 [B][q_len], the slots of
+    positions seq_lens[b] - q_len + i (or < 0: not written); the rest as
+    kvq_paged_decode_attn_mq."""
+    B, q_len, Hq, D, out_dtype = _mq_args(q, block_tables, seq_lens, out)
+    assert k_new.dtype == torch.bfloat16 and v_new.dtype == torch.bfloat16 and slot_mapping.dtype == torch.int64
+    assert k_new.shape == (B, q_len, Hkv, D) and v_new.shape == k_new.shape
+    assert k_new.stride(0) == q_len * k_new.stride(1) and k_new.stride(1) == v_new.stride(1)
+    assert v_new.stride(0) == q_len * v_new.stride(1)
+    for t in (k_new, v_new):
+        assert t.stride(3) == 1 and t.stride(2) == D
+    assert slot_mapping.shape == (B, q_len) and slot_mapping.is_contiguous()
+    return _run("kvq_paged_decode_attn_mq_append", _lib.kvq_paged_decode_attn_mq_append, (
+        _ptr(k_new), _ptr(v_new), k_new.stride(1), _ptr(slot_mapping), _ptr(q), q_len, window, _ptr(k_cache),
+        _ptr(v_cache), kv_dtype, _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), max_seq_len, B, Hq, Hkv,
+        D, BLOCK_SIZE, k_cache.shape[0], k_scale, v_scale, sm_scale, _ptr(out), out_dtype, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream), split_tokens),
+        prepare, (k_new, v_new, slot_mapping, q, k_cache, v_cache, block_tables, seq_lens, out, workspace))
 
 
 def kvq_nvfp4_paged_decode_attn_mq(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

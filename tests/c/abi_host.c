@@ -33,7 +33,8 @@ int main(void) {
         (any_fn)kvq_nvfp4_region_bytes, (any_fn)kvq_nvfp4_cache_write, (any_fn)kvq_nvfp4_paged_decode_attn,
         (any_fn)kvq_nvfp4_paged_decode_attn_ex, (any_fn)kvq_nvfp4_paged_decode_attn_append,
         (any_fn)kvq_decode_workspace_bytes_mq, (any_fn)kvq_paged_decode_attn_mq,
-        (any_fn)kvq_nvfp4_paged_decode_attn_mq, (any_fn)kvq_paged_decode_attn_fp8qp, (any_fn)kvq_cache_block_bytes,
+        (any_fn)kvq_nvfp4_paged_decode_attn_mq, (any_fn)kvq_paged_decode_attn_mq_append,
+        (any_fn)kvq_paged_decode_attn_fp8qp, (any_fn)kvq_cache_block_bytes,
         (any_fn)kvq_gather_blocks, (any_fn)kvq_scatter_blocks, (any_fn)kvq_offload_blocks,
         (any_fn)kvq_restore_blocks, (any_fn)kvq_e2m1_decode,
     };

@@ -52,7 +52,7 @@ def test_check_flags_host_side(K):
     assert K.lib().kvq_check_flags(None, 0) == K.KVQ_EINVAL
     assert K.open_library(K.CHECK_LIB_PATH).kvq_check_flags(None, 0) == K.KVQ_EINVAL
     want = int(re.search(r"#define KVQ_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
-    assert K.kvq_abi_version() == want == 3
+    assert K.kvq_abi_version() == want == 4
     assert K.kvq_strerror(-3) == "workspace too small"
 
 
