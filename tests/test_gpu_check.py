@@ -202,6 +202,33 @@ def test_fused_append_slot_past_num_blocks_is_skipped(K, C):
     assert np.array_equal(bits_u8(s.kc), before)
 
 
+def test_mq_fused_append_slot_past_num_blocks_is_skipped(K, C):
+    s = setup(1, seed=126, lens=(300, 40))
+    w = s.w
+    declared = w.num_blocks // 2
+    ql = 4
+    k_new = torch.zeros(w.B, ql, w.Hkv, w.D, dtype=torch.bfloat16, device="cuda")
+    v_new = torch.zeros_like(k_new)
+    slots = torch.full((w.B, ql), -1, dtype=torch.int64, device="cuda")
+    slots[0, 1] = declared * 16 + 5                     # the only slot given: past the declared blocks
+    q = workloads.mq_queries(w, ql, seed=1).cuda()
+    before_k, before_v = bits_u8(s.kc).copy(), bits_u8(s.vc).copy()
+    ws = torch.zeros(K.kvq_decode_workspace_bytes_mq(w.B, ql, w.Hq, w.Hkv, w.D, w.max_seq_len), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty(w.B, ql, w.Hq, w.D, dtype=torch.float32, device="cuda")
+    flags(K, C)
+    say("checked build: multi-query fused append slot past num_blocks")
+    st = C.kvq_paged_decode_attn_mq_append(P(k_new), P(v_new), w.Hkv * w.D, P(slots), P(q), ql, 0, P(s.kc),
+                                           P(s.vc), 1, P(s.bt), s.bt.shape[1], P(s.sl), w.max_seq_len, w.B, w.Hq,
+                                           w.Hkv, w.D, 16, declared, s.ks, s.vs, s.sm_scale, P(out), 1, P(ws),
+                                           ws.numel(), None, 0)
+    torch.cuda.synchronize()
+    assert st == 0
+    got = flags(K, C)
+    assert got & K.KVQ_CHECK_SLOT, got
+    assert np.array_equal(bits_u8(s.kc), before_k) and np.array_equal(bits_u8(s.vc), before_v)
+
+
 def test_block_copy_negative_id_is_skipped(K, C):
     bb = 4096
     base = torch.arange(8 * bb, dtype=torch.int32, device="cuda").view(torch.uint8)[: 8 * bb].contiguous()
