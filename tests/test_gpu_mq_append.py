@@ -12,8 +12,8 @@ cache bytes and bit-identical outputs.  Cases: new tokens inside one chunk,
 across a chunk boundary, across a split boundary (64-token splits), a
 sequence shorter than q_len and one exactly q_len long, an empty sequence,
 skipped slots, a sliding window, q_len 1 to 16, D 64 and 128, FP8 and BF16.
-The single-token call kvq_paged_decode_attn_append runs the same writer and
-is checked the same way (q_len 1)."""
+At q_len 1 both entry points run the one-token writer; the single-token
+call kvq_paged_decode_attn_append is checked the same way."""
 import numpy as np
 import pytest
 import torch
@@ -33,6 +33,7 @@ CASES = [
     (154, [500, 129, 16], dict(Hq=4, Hkv=4), 16, 0, 0),                 # q_len 16, G 1
     (155, [900, 260], dict(Hq=16, Hkv=2), 4, 128, 100),                 # sliding window
     (156, [300, 65], dict(Hq=16, Hkv=2), 1, 64, 0),                     # one new token
+    (159, [300, 65, 1], dict(Hq=16, Hkv=2), 1, 64, 40),                # one new token, window: the multi-query entry
 ]
 
 
@@ -92,8 +93,7 @@ def test_mq_append_matches_oracle_and_two_launches(K, case, kv):
     kc, vc = prefill_caches(K, w, kv, ks, vs, q_len)
     out = torch.empty(w.B, q_len, w.Hq, w.D, dtype=torch.float32, device="cuda")
     ws = K.new_workspace_mq(w.B, q_len, w.Hq, w.Hkv, w.D, w.max_seq_len, split, window=window)
-    if q_len == 1:   # the single-token entry point runs the same writer (no window argument there)
-        assert window == 0
+    if q_len == 1 and window == 0:   # the single-token entry point: the same one-token writer
         K.kvq_paged_decode_attn_append(k_new[:, 0], v_new[:, 0], slots[:, 0].contiguous(), q[:, 0].contiguous(), kc,
                                        vc, kv, bt, sl, w.max_seq_len, w.Hkv, ks, vs, sm, out[:, 0], ws,
                                        split_tokens=split)
