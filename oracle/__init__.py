@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
             "kvqo_decode_attn_fp8qp": (None, [P, I, I, P, P, P, I, P, I, I, I, I, I, F, F, F, F, P, I]),
             "kvqo_decode_attn_fp8qp_band": (None, [P, I, I, P, P, P, I, P, I, I, I, I, I, F, F, F, F,
                                                    ctypes.c_double, P, P, P, P, P, P]),
+            "kvqo_decode_attn_fp8qp_tol": (None, [P, I, I, P, P, P, I, P, I, I, I, I, I, F, F, F, F,
+                                                  ctypes.c_double, P, P, P, P]),
             "kvqo_decode_attn_mq": (None, [P, I, I, P, P, I, P, I, P, I, I, I, I, I, F, F, F, P, I]),
             "kvqo_fp8_cos_sim": (D, [P, I64, F]),
         }
@@ -275,6 +277,32 @@ def decode_attn_fp8qp(q, k_cache: np.ndarray, v_cache: np.ndarray, block_tables,
                                  B, Hq, Hkv, D, block_size, q_scale, k_scale, v_scale, sm_scale, _ptr(out),
                                  nthreads)
     return out
+
+
+def decode_attn_fp8qp_tol(q, k_cache: np.ndarray, v_cache: np.ndarray, block_tables, seq_lens, Hkv: int,
+                          block_size: int, q_scale: float, k_scale: float, v_scale: float, sm_scale: float,
+                          eps: float, window: int = 0, weights: bool = False):
+    """(tol, n_open): per-element tolerance [B][q_len][Hq][D] of
+    decode_attn_fp8qp for an implementation meeting assumptions A1-A3 of
+    kvq_oracle.h with accuracy eps.  weights=True appends the definition's
+    weights w_t and their bounds delta_t, [B][q_len][Hq][max seq_len]."""
+    qb = _bits16(q)
+    B, q_len, Hq, D = qb.shape
+    bt = np.ascontiguousarray(np.asarray(block_tables, dtype=np.int32))
+    sl = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    kc, vc = np.ascontiguousarray(k_cache), np.ascontiguousarray(v_cache)
+    tol = np.zeros((B, q_len, Hq, D), dtype=np.float64)
+    n = np.zeros(1, dtype=np.int64)
+    max_l = max(1, int(sl.max())) if sl.size else 1
+    wt = np.zeros((B, q_len, Hq, max_l)) if weights else None
+    dt = np.zeros_like(wt) if weights else None
+    lib().kvqo_decode_attn_fp8qp_tol(_ptr(qb), q_len, window, _ptr(kc), _ptr(vc), _ptr(bt), bt.shape[1], _ptr(sl),
+                                     B, Hq, Hkv, D, block_size, q_scale, k_scale, v_scale, sm_scale, eps,
+                                     _ptr(tol), _ptr(n), _ptr(wt) if weights else None,
+                                     _ptr(dt) if weights else None)
+    if weights:
+        return tol, int(n[0]), wt, dt
+    return tol, int(n[0])
 
 
 def decode_attn_fp8qp_band(q, k_cache: np.ndarray, v_cache: np.ndarray, block_tables, seq_lens, Hkv: int,

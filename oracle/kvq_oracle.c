@@ -633,6 +633,128 @@ void kvqo_decode_attn_fp8qp(const uint16_t* q, int q_len, int window, const uint
     run_attn(&j, nthreads);
 }
 
+/* Grid spacing of E4M3 at magnitude y: 2^(e - 3) in the binade [2^e, 2^(e+1)),
+ * and the subnormal spacing 2^-9 below 2^-6. */
+static double e4m3_step(double y) {
+    int e;
+    if (y < 0.015625) return ldexp(1.0, -9);
+    frexp(y, &e); /* y = f * 2^e, f in [0.5, 1) */
+    return ldexp(1.0, e - 1 - 3);
+}
+
+/* Tolerance of kvqo_decode_attn_fp8qp: see kvq_oracle.h for the assumptions.
+ * All quantities of one (b, i, h) row are in code units of the definition's
+ * frame R (v_scale applied at the end). */
+void kvqo_decode_attn_fp8qp_tol(const uint16_t* q, int q_len, int window, const uint8_t* k_cache,
+                                const uint8_t* v_cache, const int32_t* block_tables, int max_blocks,
+                                const int32_t* seq_lens, int B, int Hq, int Hkv, int D, int block_size,
+                                float q_scale, float k_scale, float v_scale, float sm_scale, double eps,
+                                double* tol, int64_t* n_open, double* w_out, double* delta_out) {
+    const int G = Hq / Hkv;
+    const double c = (double)(float)((double)sm_scale * (double)q_scale * (double)k_scale * 1.4426950408889634);
+    int max_L = 1;
+    for (int b = 0; b < B; ++b)
+        if (seq_lens[b] > max_L) max_L = seq_lens[b];
+    double* x = (double*)malloc(sizeof(double) * (size_t)max_L);
+    double* dx = (double*)malloc(sizeof(double) * (size_t)max_L);
+    double* w = (double*)malloc(sizeof(double) * (size_t)max_L);
+    double* dl = (double*)malloc(sizeof(double) * (size_t)max_L);
+    *n_open = 0;
+    for (int b = 0; b < B; ++b)
+        for (int i = 0; i < q_len; ++i)
+            for (int h = 0; h < Hq; ++h) {
+                const int64_t row = ((int64_t)b * q_len + i) * Hq + h;
+                double* trow = tol + row * D;
+                for (int d = 0; d < D; ++d) trow[d] = 0.0;
+                const int L = seq_lens[b] - q_len + 1 + i;
+                if (L <= 0) continue;
+                const int t0 = (window > 0 && L > window) ? L - window : 0;
+                const int g = h / G;
+                const uint16_t* qr = q + row * D;
+                double qv[256];
+                for (int d = 0; d < D; ++d) qv[d] = kvqo_e4m3_value(kvqo_e4m3_quantize(qr[d], q_scale));
+                /* scores, as the definition computes them, and their error bound:
+                   (A1) on the dot, plus fp32 rounding of the scale step and exp2 */
+                double xmax = -INFINITY, dxmax = 0.0;
+                for (int t = t0; t < L; ++t) {
+                    const int64_t slot = (int64_t)block_tables[(int64_t)b * max_blocks + t / block_size] *
+                                             block_size + t % block_size;
+                    double dot = 0.0, sabs = 0.0;
+                    for (int d = 0; d < D; ++d) {
+                        const double p = qv[d] * kvqo_e4m3_value(k_cache[k_index(slot, g, d, Hkv, D, block_size)]);
+                        dot += p;
+                        sabs += fabs(p);
+                    }
+                    x[t] = c * dot;
+                    if (x[t] > xmax) xmax = x[t];
+                    dx[t] = eps * fabs(c) * sabs;
+                }
+                const double R = ceil(xmax);
+                int bad = 0;
+                double W = 0.0, DW = 0.0;
+                for (int t = t0; t < L; ++t) {
+                    dx[t] += ldexp(2.0 + fabs(x[t]) + fabs(x[t] - R), -20);
+                    if (dx[t] > dxmax) dxmax = dx[t];
+                    /* the definition's weight, then the extreme arguments a score error of dx allows */
+                    const double a = 448.0 * exp2(x[t] - R);
+                    w[t] = kvqo_e4m3_value(kvqo_e4m3_encode((float)a));
+                    const double lo_a = a * exp2(-dx[t]);
+                    const double hi_a = fmin(448.0, a * exp2(dx[t]));
+                    if (lo_a >= 0.03125) {
+                        /* in the normal range of the definition's frame and of every frame
+                           an implementation may hold (A3: at most one binade coarser, or finer
+                           with the argument still <= 448), where E4M3 rounding commutes with
+                           the power-of-two rescale: the weight is the rounding of an argument
+                           in [lo_a, hi_a], and rounding is monotone */
+                        const double wl = kvqo_e4m3_value(kvqo_e4m3_encode((float)lo_a));
+                        const double wh = kvqo_e4m3_value(kvqo_e4m3_encode((float)hi_a));
+                        dl[t] = fmax(w[t] - wl, wh - w[t]);
+                        if (dl[t] > 0.0) ++*n_open;
+                    } else {
+                        /* near or below the subnormal range: the weight may be rounded on the grid
+                           of any frame up to R + 1, whose spacing at hi_a is at most twice E4M3's at
+                           hi_a / 2, so it moves by at most half that spacing, and never by more than
+                           the value itself; plus the definition's own rounding and the score bound */
+                        dl[t] = fabs(a - w[t]) + (hi_a - a) + fmin(hi_a, e4m3_step(hi_a / 2.0));
+                    }
+                    W += w[t];
+                    DW += dl[t];
+                    if (w_out) {
+                        w_out[row * max_L + t] = w[t];
+                        delta_out[row * max_L + t] = dl[t];
+                    }
+                }
+                if (dxmax >= 0.5 || !(W > DW)) bad = 1;
+                for (int d = 0; d < D; ++d) {
+                    double num = 0.0;
+                    for (int t = t0; t < L; ++t) {
+                        const int64_t slot = (int64_t)block_tables[(int64_t)b * max_blocks + t / block_size] *
+                                                 block_size + t % block_size;
+                        num += w[t] * kvqo_e4m3_value(v_cache[v_index(slot, g, d, Hkv, D, block_size)]);
+                    }
+                    const double o = num / W;
+                    double e1 = 0.0, a_abs = 0.0;
+                    for (int t = t0; t < L; ++t) {
+                        const int64_t slot = (int64_t)block_tables[(int64_t)b * max_blocks + t / block_size] *
+                                                 block_size + t % block_size;
+                        const double vv = kvqo_e4m3_value(v_cache[v_index(slot, g, d, Hkv, D, block_size)]);
+                        e1 += dl[t] * fabs(vv - o);
+                        a_abs += (w[t] + dl[t]) * fabs(vv);
+                    }
+                    /* o' - o = (sum (w'-w)(v - o) + eta_N - o eta_W) / W'', |eta_N| <= eps a_abs,
+                       |eta_W| <= eps (W + DW), W'' >= (W - DW)(1 - eps); then the fp32 epilogue */
+                    trow[d] = bad ? INFINITY
+                                  : (double)v_scale * ((e1 + eps * (a_abs + fabs(o) * (W + DW))) /
+                                                           ((W - DW) * (1.0 - eps)) +
+                                                       ldexp(fabs(o), -20));
+                }
+            }
+    free(x);
+    free(dx);
+    free(w);
+    free(dl);
+}
+
 double kvqo_fp8_cos_sim(const uint16_t* x, int64_t n, float scale) {
     double xy = 0.0, xx = 0.0, yy = 0.0;
     for (int64_t i = 0; i < n; ++i) {

@@ -177,6 +177,38 @@ void kvqo_decode_attn_fp8qp(const uint16_t* q, int q_len, int window, const uint
                             float q_scale, float k_scale, float v_scale, float sm_scale, double* out,
                             int nthreads);
 
+/* Per-element tolerance of kvqo_decode_attn_fp8qp ([B][q_len][Hq][D], v_scale
+ * applied), derived from the definition for any implementation that meets
+ * three stated assumptions (the pages give no accuracy for this variant, and
+ * the matrix-core ISA does not state the rounding inside its FP8 dot steps,
+ * so eps is an assumption, not a measured property):
+ *   (A1) each score sum_d value(qc_d) value(kc_td) is computed within
+ *        eps * sum_d |value(qc_d) value(kc_td)|; the fp32 scale-and-shift step
+ *        and exp2 add at most 2^-20 (2 + |x_t| + |x_t - R|) to x_t;
+ *   (A2) sum_t p_t value(vc_td) and sum_t p_t over the weights p_t it used
+ *        are computed within eps times the sum of the terms' magnitudes;
+ *   (A3) each weight is value(E4M3(fp32(448 * 2^(x'_t - r)))) * 2^(r - R')
+ *        for its computed score x'_t and some integer reference r with
+ *        x'_t <= r <= R' = ceil(max_t x'_t): references are powers of two and
+ *        may grow while the tokens are visited (one pass, splits, merges).
+ * Then, in the definition's frame R, each weight differs from value(pc_t) by
+ * at most delta_t: where 448 * 2^(x_t - R) * 2^(-dx_t) >= 2^-5 the argument is
+ * normal in every such frame (R' <= R + 1), rounding commutes with the
+ * rescale and delta_t is the distance to the codes of the extreme arguments
+ * 448 * 2^(x_t - R +- dx_t); below that, delta_t bounds rounding on a grid up
+ * to twice as coarse (half its spacing, plus the definition's own rounding).  With W = sum w_t, DW = sum delta_t and o the
+ * definition's output in code units:
+ *   tol = v_scale * ( (sum_t delta_t |v_t - o| + eps (sum_t (w_t + delta_t)
+ *         |v_t| + |o| (W + DW))) / ((W - DW)(1 - eps)) + 2^-20 |o| ),
+ * or +Inf when W <= DW or some dx_t >= 1/2.  n_open counts tokens in the
+ * normal range whose code the score bound leaves open.  w_out / delta_out
+ * (NULL to skip): [B][q_len][Hq][max seq_len] receive w_t and delta_t. */
+void kvqo_decode_attn_fp8qp_tol(const uint16_t* q, int q_len, int window, const uint8_t* k_cache,
+                                const uint8_t* v_cache, const int32_t* block_tables, int max_blocks,
+                                const int32_t* seq_lens, int B, int Hq, int Hkv, int D, int block_size,
+                                float q_scale, float k_scale, float v_scale, float sm_scale, double eps,
+                                double* tol, int64_t* n_open, double* w_out, double* delta_out);
+
 /* What a one-pass kernel on FP8 matrix cores may return for
  * kvqo_decode_attn_fp8qp, as lo, hi and tol ([B][q_len][Hq][D], v_scale
  * applied): every output must lie in [lo - tol, hi + tol].  The arithmetic
