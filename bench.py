@@ -416,6 +416,33 @@ def measure_workload(torch, K, name, steps, warmup, with_nvfp4=False):
     return rec
 
 
+def attn_only(torch, K, name, fmt, steps, warmup, impl=0):
+    """Back-to-back attention calls of one workload in one KV format over
+    rotated layer caches (no step loop, no other workloads): the run that
+    kernel traces and counter passes profile."""
+    from quantized_decode_attention_calibrate_amd import workloads
+    kv, eb = {"fp8": (K.KVQ_KV_FP8_E4M3, 1), "bf16": (K.KVQ_KV_BF16, 2), "nvfp4": (NVFP4, NVFP4_BYTES)}[fmt]
+    w = workloads.make(name, device="cuda", seed=0)
+    L = Layers(K, w, kv, layers_for(w, eb), "cuda")
+    for i in range(warmup):
+        L.run("attend", i, impl)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record(st)
+    for i in range(steps):
+        L.run("attend", i, impl)
+    a1.record(st)
+    torch.cuda.synchronize()
+    us = a0.elapsed_time(a1) / steps * 1e3
+    attn_b, _ = step_bytes(w.B, w.Hq, w.Hkv, w.D, w.seq_lens, eb, w.B)
+    return {"workload": name, "kv": fmt, "impl": {0: "auto", 1: "valu", 2: "mfma"}[impl], "steps": steps,
+            "warmup": warmup, "attn_us": round(us, 2), "attn_gbps": round(attn_b / (us * 1e-6) / 1e9, 1),
+            "pct_of_hbm_peak": round(100 * attn_b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 1),
+            "attn_bytes": attn_b, "layers_rotated": L.R,
+            "split_tokens": K.kvq_decode_plan_split_tokens(w.B, w.Hkv, w.max_seq_len)}
+
+
 def measure_quality(torch, K, name):
     """The comparison the FP8 calibration guide asks for: BF16 KV, FP8 with the
     default scale 1.0, and FP8 with calibrated scales.  Reports the
@@ -648,6 +675,8 @@ def main():
     ap.add_argument("--no-compare", action="store_true", help="skip the BF16 comparator")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip the per-workload table (agents126k, mixed64, nvfp4_131k)")
+    ap.add_argument("--attn-only", choices=("fp8", "bf16", "nvfp4"), default=None,
+                    help="time only the attention call of --workload in this KV format (for profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this path has no multi-GPU "
@@ -659,6 +688,10 @@ def main():
     from quantized_decode_attention_calibrate_amd import workloads
 
     dev = "cuda"
+    if args.attn_only:
+        print(json.dumps(attn_only(torch, K, args.workload, args.attn_only, args.steps, args.warmup, args.impl)),
+              flush=True)
+        return
     print(f"[bench] building {args.workload} on {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
     w = workloads.make(args.workload, device=dev, seed=0)
     w_cpu = None
