@@ -209,30 +209,6 @@ void kvqo_decode_attn_fp8qp_tol(const uint16_t* q, int q_len, int window, const 
                                 float q_scale, float k_scale, float v_scale, float sm_scale, double eps,
                                 double* tol, int64_t* n_open, double* w_out, double* delta_out);
 
-/* What a one-pass kernel on FP8 matrix cores may return for
- * kvqo_decode_attn_fp8qp, as lo, hi and tol ([B][q_len][Hq][D], v_scale
- * applied): every output must lie in [lo - tol, hi + tol].  The arithmetic
- * model: an FP8 dot step sums groups of 8 products (8 consecutive dims for QK,
- * 8 tokens aligned at multiples of 8 for PV and the weight sum), each product
- * aligned to the group's largest exponent sum 2^E and cut below 2^E * dot_ulp
- * (toward zero), and adds the group sums in fp32; scores are scaled and
- * shifted with one fp32 rounding and exp2 has 2^-21 relative slack; the kernel
- * quantizes each weight against the reference it holds at the time, any
- * integer from ceil(score) up to the final one.
- *   lo / hi: the exact extremes of sum p v / sum p over each weight p_t in
- *     [pl_t, ph_t], the E4M3 roundings of 448 * 2^(x' - r) over every score x'
- *     within the bound of x_t and every such r (common frame: the largest r).
- *   tol: the bound of the PV and weight-sum accumulation error on top.
- * n_ambiguous counts the tokens whose rounding in the top frame the score
- * bound leaves open.  w_lo / w_hi (NULL to skip): [B][q_len][Hq][max seq_len]
- * receive pl_t / ph_t of the visible tokens. */
-void kvqo_decode_attn_fp8qp_band(const uint16_t* q, int q_len, int window, const uint8_t* k_cache,
-                                 const uint8_t* v_cache, const int32_t* block_tables, int max_blocks,
-                                 const int32_t* seq_lens, int B, int Hq, int Hkv, int D, int block_size,
-                                 float q_scale, float k_scale, float v_scale, float sm_scale, double dot_ulp,
-                                 double* lo, double* hi, double* tol, int* n_ambiguous, double* w_lo,
-                                 double* w_hi);
-
 /* Same as kvqo_decode_attn, for a chosen subset of (b, h) units:
  * units[2*i] = b, units[2*i+1] = h; out is [n_units][D]. */
 void kvqo_decode_attn_units(const uint16_t* q, const void* k_cache, const void* v_cache,

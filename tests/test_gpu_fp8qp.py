@@ -2,23 +2,18 @@
 (E4M3 Q with a calibrated q_scale, power-of-two softmax reference, P codes
 E4M3(448 * 2^(x - R)), quantized weights in numerator and denominator).
 
-The variant's own tolerance comes from its arithmetic.  The FP8 matrix-core
-dot step of gfx950 sums each group of 8 products aligned to the group's
-largest exponent sum 2^E and drops what lies below 2^(E-13) (an in-bounds
-probe of the builtin shows 2^-13 kept and 2^-14 dropped, toward zero, per
-product), so QK scores, PV sums and the weight sum carry a bounded error; a
-score error moves a weight across an E4M3 rounding midpoint now and then,
-and in a few-token sequence one such code moves the output far more than the
-path's 2e-3.  A one-pass kernel also quantizes each weight against the
-running reference it holds at the time, which rounds E4M3 subnormals more
-finely than the final frame.  So the unique part is compared exactly and the
-rest checked for validity: every output element must lie inside the oracle's
-band [lo - tol, hi + tol] for that model (kvqo_decode_attn_fp8qp_band, cut
-2^-13), tokens whose rounding the model leaves open stay rare (< 10%), the
-band stays narrow (median width under 1% of V's rms), and relative L2
-against the nearest-rounding oracle stays below 1e-2.  Also: bf16 =
-RNE(fp32), multi-query, windows, every column-tile count, and the variant's
-distance from the exact FP8 path."""
+The variant quantizes the softmax weights, so a score error of any size can
+move a weight across an E4M3 rounding midpoint, and a one-pass kernel
+quantizes each weight against the running power-of-two reference it holds,
+which rounds the smallest weights on another grid.  Its tolerance therefore
+comes from the definition, not from the kernel: the oracle's
+kvqo_decode_attn_fp8qp_tol bounds every output of an implementation whose
+scores and weighted sums are accurate to eps = 2^-10 of the sum of their
+terms' magnitudes (an assumption: the matrix-core ISA states no rounding for
+its FP8 dot steps) and whose references are powers of two up to the final
+one.  Each output element must lie within that tolerance of the definition's
+fp64 result.  Also: bf16 = RNE(fp32), multi-query, windows, every
+column-tile count, and the variant's distance from the exact FP8 path."""
 import numpy as np
 import pytest
 import torch
@@ -29,6 +24,8 @@ from quantized_decode_attention_calibrate_amd import workloads
 from gpu_common import Setup, assert_attention_close, gpu_or_skip, gpu_calibrate, kvq, say
 
 pytestmark = pytest.mark.gpu
+
+EPS = 2.0 ** -10   # assumed accuracy of the FP8 dot steps and sums (see the module docstring)
 
 CASES = [
     # name, seed, seq_lens, shape, q_len, window, split_tokens
@@ -67,21 +64,19 @@ def test_fp8qp_matches_oracle(K, case):
     kc, vc = s.oracle_caches()
     ref = oracle.decode_attn_fp8qp(q, kc, vc, w.block_tables, w.seq_lens, w.Hkv, 16, qs, s.ks, s.vs, s.sm_scale,
                                    nthreads=8, window=window)
-    lo, hi, tol, n_amb = oracle.decode_attn_fp8qp_band(q, kc, vc, w.block_tables, w.seq_lens, w.Hkv, 16, qs, s.ks,
-                                                       s.vs, s.sm_scale, 2.0 ** -13, window=window)
+    tol, n_open = oracle.decode_attn_fp8qp_tol(q, kc, vc, w.block_tables, w.seq_lens, w.Hkv, 16, qs, s.ks, s.vs,
+                                               s.sm_scale, EPS, window=window)
     out32 = run_qp(K, s, q, qs, split, window)
     got = out32.cpu().numpy()
     n_tok = sum(min(L, window) if window else L for L in w.seq_lens) * q_len * w.Hq
-    outside = np.maximum(lo - tol - got, got - hi - tol).max()
-    width = hi - lo + 2 * tol
+    err = np.abs(got - ref)
+    frac = err / np.maximum(tol, 1e-300)
     rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
-    say(f"  fp8qp case={case}: open roundings {n_amb} of {n_tok}, max outside band {outside:.2e}, "
-        f"rel L2 vs nearest rounding {rel:.2e}, band width median {np.median(width):.2e} max {width.max():.2e}")
-    assert np.isfinite(got).all()
-    assert outside <= 0.0, outside
-    assert n_amb < 0.1 * n_tok
-    assert np.median(width) < 1e-2 * float(w.v.float().pow(2).mean().sqrt())
-    assert rel < 1e-2
+    say(f"  fp8qp case={case}: max |got - def| {err.max():.2e}, max of |got - def| / tol {frac.max():.3f}, "
+        f"tol median {np.median(tol):.2e} max {tol.max():.2e}, open codes {n_open} of {n_tok} tokens, "
+        f"rel L2 vs definition {rel:.2e}")
+    assert np.isfinite(got).all() and np.isfinite(tol).all()
+    assert (err <= tol).all(), float(frac.max())
     out16 = run_qp(K, s, q, qs, split, window, torch.bfloat16)
     assert torch.equal(out16.cpu().view(torch.int16), out32.cpu().to(torch.bfloat16).view(torch.int16))
 

@@ -1,4 +1,4 @@
-"""Pins for the oracle's FP8 Q and P attention variant and for its band.
+"""Pins for the oracle's FP8 Q and P attention variant.
 
 An independent dense formulation (torch's float8_e4m3fn casts for the Q and
 P codes, numpy for the rest, no paging) must agree to 1e-12; closed forms:
@@ -6,11 +6,8 @@ equal keys give the mean of V (every P code is equal), constant V gives the
 constant, one visible token gives its value; and the variant stays close to
 exact attention (it quantizes Q and the softmax weights to 3 mantissa bits).
 
-The band (what a one-pass kernel on FP8 matrix cores may return): it holds
-the nearest-rounding result, its ends are the exact extremes over the weight
-intervals (brute force over every end), and a numpy emulation of such a
-kernel under the same arithmetic model lands inside it for several split
-sizes, windows and multi-query shapes."""
+The variant's tolerance (kvqo_decode_attn_fp8qp_tol) has pins of its own in
+test_oracle_fp8qp_tol.py."""
 import math
 
 import numpy as np
@@ -101,154 +98,3 @@ def test_fp8qp_close_to_exact_attention():
                                   nthreads=8)
     rel = np.linalg.norm(out - exact) / np.linalg.norm(exact)
     assert 1e-2 < rel < 0.15, rel
-
-
-DOT_ULP = 2.0 ** -13
-
-
-def binade(v):
-    """2^floor(log2 |v|) of E4M3 values, 2^-6 for subnormals and zero."""
-    return np.exp2(np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** -6))))
-
-
-def fp8_group_sums(a, b, ulp):
-    """Group sums of a * b over the last axis in groups of 8, each product cut
-    toward zero below ulp * 2^E, 2^E the group's largest binade product (an
-    FP8 matrix-core dot step as modelled by the oracle's band)."""
-    p = (a * b).reshape(*np.broadcast_shapes(a.shape, b.shape)[:-1], -1, 8)
-    e = (binade(a) * binade(b)).reshape(p.shape).max(-1, keepdims=True)
-    quant = e * ulp if ulp > 0 else np.ones_like(e)
-    return (np.trunc(p / quant) * quant).sum(-1) if ulp > 0 else p.sum(-1)
-
-
-def f32_sum(acc, parts):
-    """Add parts (last axis) into acc one at a time, rounding to fp32."""
-    acc = np.float32(acc)
-    for j in range(parts.shape[-1]):
-        acc = (acc + parts[..., j]).astype(np.float32)
-    return acc
-
-
-def emulate_row(qv, K, V, t0, L, c, vs, split, ulp=DOT_ULP):
-    """A one-pass FP8 Q/P decode of one (query, head) over tokens [t0, L) of a
-    sequence whose code values are K, V ([Lseq][D]): splits of `split` tokens
-    from t0 rounded down to 64, chunks of 64 tokens, a running integer
-    reference per split, FP8 dot steps for QK, PV and the weight sum, fp32
-    accumulation, and a merge of the splits."""
-    Lseq, D = K.shape
-    parts = []
-    for s0 in range(t0 & ~63, L, split):
-        m, l, acc = -np.inf, np.float32(0), np.zeros(D, np.float32)
-        for c0 in range(s0, min(s0 + split, L), 64):
-            toks = np.arange(c0, c0 + 64)
-            seen = (toks >= t0) & (toks < L)
-            Kc = np.zeros((64, D))
-            Vc = np.zeros((64, D))
-            Kc[toks < Lseq] = K[toks[toks < Lseq]]
-            Vc[toks < Lseq] = V[toks[toks < Lseq]]
-            s = f32_sum(np.zeros(64), fp8_group_sums(qv[None, :], Kc, ulp))
-            s = np.where(seen, s.astype(np.float64), -np.inf)
-            r = max(m, math.ceil(float(np.float32(np.float32(s.max()) * np.float32(c)))))
-            alpha = 0.0 if m == -np.inf else 2.0 ** (m - r)
-            x = np.where(seen, (s * c - r), -np.inf).astype(np.float32)
-            y = (np.float32(448.0) * np.exp2(x.astype(np.float64)).astype(np.float32)).astype(np.float32)
-            P = np.where(seen, e4m3(y), 0.0)
-            l = f32_sum(np.float32(l * alpha), fp8_group_sums(np.ones(64), P, ulp)[None, :])[0]
-            acc = f32_sum((acc * np.float32(alpha)).astype(np.float32),
-                          fp8_group_sums(P[None, :], Vc.T, ulp))
-            m = r
-        parts.append((m, float(l), acc.astype(np.float64)))
-    M = max(p[0] for p in parts)
-    num = sum(2.0 ** (m - M) * a for m, _, a in parts)
-    den = sum(2.0 ** (m - M) * l for m, l, _ in parts)
-    return float(np.float32(vs)) * num / den
-
-
-def codes_of(w, kc, vc, qs, ks, vs, q):
-    qv = e4m3(np.clip(q.float().numpy() / np.float32(qs), -448, 448))
-    Kd = dense_dequant_fp8(w.k, ks) / np.float64(np.float32(ks))
-    Vd = dense_dequant_fp8(w.v, vs) / np.float64(np.float32(vs))
-    return qv, Kd, Vd
-
-
-def test_band_holds_the_result_and_is_narrow():
-    w = workloads.make("mixed64", seed=75, seq_lens=[45, 130], shape=dict(Hq=8, Hkv=2, D=64))
-    q = workloads.mq_queries(w, 2, seed=4)
-    ks, vs = calibrated(w)
-    qs = q_scale(q)
-    out, kc, vc = run(w, q, qs, ks, vs)
-    lo, hi, tol, n = oracle.decode_attn_fp8qp_band(q, kc, vc, w.block_tables, w.seq_lens, w.Hkv, 16, qs, ks, vs,
-                                                   0.125, DOT_ULP)
-    assert (lo <= out + 1e-15).all() and (out <= hi + 1e-15).all()
-    assert (tol > 0).all() and np.median(hi - lo + 2 * tol) < 1e-2 * np.sqrt((out ** 2).mean())
-    assert n < 0.05 * sum(w.seq_lens) * w.Hq * 2
-    # without the dot-step cut only fp32 slack is left
-    lo0, hi0, tol0, n0 = oracle.decode_attn_fp8qp_band(q, kc, vc, w.block_tables, w.seq_lens, w.Hkv, 16, qs, ks, vs,
-                                                       0.125, 0.0)
-    assert (tol0 < tol).all() and tol0.max() < 1e-5 * np.abs(out).max() and n0 < n
-
-
-def test_band_is_the_exact_extreme_over_the_weight_intervals():
-    # brute force over the ends of each of 6 tokens' weight intervals
-    import itertools
-    w = workloads.make("tiny", seed=76, seq_lens=[6], shape=dict(Hq=2, Hkv=1, D=64))
-    ks, vs = calibrated(w)
-    q = w.q[:, None]
-    qs = q_scale(q)
-    _, kc, vc = run(w, q, qs, ks, vs)
-    lo, hi, tol, n, wl, wh = oracle.decode_attn_fp8qp_band(q, kc, vc, w.block_tables, w.seq_lens, w.Hkv, 16, qs, ks,
-                                                           vs, 0.125, 2.0 ** -6, weights=True)
-    _, _, Vd = codes_of(w, kc, vc, qs, ks, vs, q)
-    for h in range(w.Hq):
-        assert (wl[0, 0, h] < wh[0, 0, h]).sum() >= 3   # a coarse cut leaves several weights open
-        vals = []
-        for combo in itertools.product(*zip(wl[0, 0, h], wh[0, 0, h])):
-            p = np.array(combo)
-            vals.append(float(np.float32(vs)) * (p[:, None] * Vd[:, 0, :]).sum(0) / p.sum())
-        vals = np.array(vals)
-        assert np.abs(lo[0, 0, h] - vals.min(0)).max() < 1e-12
-        assert np.abs(hi[0, 0, h] - vals.max(0)).max() < 1e-12
-
-
-EMULATED = [
-    # seed, seq_lens, shape, q_len, window, split
-    (77, [700, 37, 300], dict(Hq=4, Hkv=1), 2, 0, 64),
-    (77, [700, 37, 300], dict(Hq=4, Hkv=1), 2, 200, 128),
-    (77, [700, 37, 300], dict(Hq=4, Hkv=1), 2, 0, 1024),
-    # early chunks quantized against lower references: weights that are E4M3
-    # subnormals in the final frame round differently there (a band without
-    # the lower frames misses this case by 1e-4)
-    (82, [700, 2100, 5], dict(Hq=16, Hkv=2), 4, 0, 128),
-]
-
-
-@pytest.mark.parametrize("case", range(len(EMULATED)))
-def test_band_covers_an_emulated_fp8_kernel(case):
-    """A one-pass kernel emulated in numpy under the band's arithmetic model
-    (chunked running references, cut FP8 dot steps, fp32 sums) lands inside
-    [lo - tol, hi + tol]; with the cut left out of the band it does not,
-    so the emulation exercises the model's terms."""
-    seed, lens, shape, q_len, window, split = EMULATED[case]
-    w = workloads.make("gptoss65k", seed=seed, seq_lens=lens, shape=shape)
-    q = workloads.mq_queries(w, q_len, seed=seed)
-    ks, vs = calibrated(w)
-    qs = q_scale(q)
-    sm = float(np.float32(1.0 / math.sqrt(w.D)))
-    kc, vc = caches(w, oracle.KV_FP8, ks, vs)
-    lo, hi, tol, _ = oracle.decode_attn_fp8qp_band(q, kc, vc, w.block_tables, w.seq_lens, w.Hkv, 16, qs, ks, vs, sm,
-                                                   DOT_ULP, window=window)
-    lo0, hi0, tol0, _ = oracle.decode_attn_fp8qp_band(q, kc, vc, w.block_tables, w.seq_lens, w.Hkv, 16, qs, ks, vs,
-                                                      sm, 0.0, window=window)
-    qv, Kd, Vd = codes_of(w, kc, vc, qs, ks, vs, q)
-    c = float(np.float32(float(sm) * float(qs) * float(ks) * LOG2E))
-    n_out0 = 0
-    for b, (s0, Lseq) in enumerate(zip(w.seq_starts, w.seq_lens)):
-        for i in range(q_len):
-            L = Lseq - q_len + 1 + i
-            t0 = max(0, L - window) if window else 0
-            for h in range(w.Hq):
-                g = h // w.G
-                got = emulate_row(qv[b, i, h], Kd[s0:s0 + Lseq, g], Vd[s0:s0 + Lseq, g], t0, L, c, vs, split)
-                assert (got >= lo[b, i, h] - tol[b, i, h]).all() and (got <= hi[b, i, h] + tol[b, i, h]).all()
-                n_out0 += int(((got < lo0[b, i, h] - tol0[b, i, h]) | (got > hi0[b, i, h] + tol0[b, i, h])).sum())
-    assert n_out0 > 0
