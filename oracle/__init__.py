@@ -65,8 +65,8 @@ def lib() -> ctypes.CDLL:
             "kvqo_nvfp4_calibrate": (I, [P, P, I]),
             "kvqo_amax_bf16": (F, [P, I64, I64, I64]),
             "kvqo_nvfp4_region_bytes": (I64, [I, I]),
-            "kvqo_cache_write": (None, [P, P, I64, P, I, I, I, P, P, I, I, F, F]),
-            "kvqo_nvfp4_cache_write": (None, [P, P, I64, P, I, I, I, P, P, I, F, F]),
+            "kvqo_cache_write": (None, [P, P, I64, P, I, I, I, P, P, I, I, F, F, I]),
+            "kvqo_nvfp4_cache_write": (None, [P, P, I64, P, I, I, I, P, P, I, F, F, I]),
             "kvqo_nvfp4_k_value": (D, [P, I64, I, I, I, I, I, F]),
             "kvqo_nvfp4_v_value": (D, [P, I64, I, I, I, I, I, F]),
             "kvqo_decode_attn": (None, [P, P, P, I, P, I, P, I, I, I, I, I, F, F, F, P, I]),
@@ -185,8 +185,8 @@ def new_caches(kv_dtype: int, num_blocks: int, Hkv: int, D: int, block_size: int
 
 
 def cache_write(k, v, slot_mapping, k_cache: np.ndarray, v_cache: np.ndarray, kv_dtype: int,
-                k_scale: float = 1.0, v_scale: float = 1.0) -> None:
-    """k, v: bf16 [T][Hkv][D]; writes in place."""
+                k_scale: float = 1.0, v_scale: float = 1.0, nthreads: int = 1) -> None:
+    """k, v: bf16 [T][Hkv][D]; writes in place (nthreads: see kvq_oracle.h)."""
     kb, vb = _bits16(k), _bits16(v)
     T, Hkv, D = kb.shape
     sm = np.ascontiguousarray(np.asarray(slot_mapping, dtype=np.int64))
@@ -194,16 +194,16 @@ def cache_write(k, v, slot_mapping, k_cache: np.ndarray, v_cache: np.ndarray, kv
     bs = k_cache.shape[2] if kv_dtype != KV_NVFP4 else None
     assert kv_dtype in (KV_BF16, KV_FP8)
     lib().kvqo_cache_write(_ptr(kb), _ptr(vb), Hkv * D, _ptr(sm), T, Hkv, D,
-                           _ptr(k_cache), _ptr(v_cache), bs, kv_dtype, k_scale, v_scale)
+                           _ptr(k_cache), _ptr(v_cache), bs, kv_dtype, k_scale, v_scale, nthreads)
 
 
 def nvfp4_cache_write(k, v, slot_mapping, k_cache: np.ndarray, v_cache: np.ndarray, block_size: int,
-                      k_gscale: float, v_gscale: float) -> None:
+                      k_gscale: float, v_gscale: float, nthreads: int = 1) -> None:
     kb, vb = _bits16(k), _bits16(v)
     T, Hkv, D = kb.shape
     sm = np.ascontiguousarray(np.asarray(slot_mapping, dtype=np.int64))
     lib().kvqo_nvfp4_cache_write(_ptr(kb), _ptr(vb), Hkv * D, _ptr(sm), T, Hkv, D,
-                                 _ptr(k_cache), _ptr(v_cache), block_size, k_gscale, v_gscale)
+                                 _ptr(k_cache), _ptr(v_cache), block_size, k_gscale, v_gscale, nthreads)
 
 
 def nvfp4_values(cache: np.ndarray, which: str, slots, Hkv: int, D: int, block_size: int,

@@ -147,28 +147,72 @@ static int64_t v_index(int64_t slot, int g, int d, int Hkv, int D, int bs) {
     return ((blk * Hkv + g) * D + d) * bs + off;
 }
 
-void kvqo_cache_write(const uint16_t* k, const uint16_t* v, int64_t src_stride,
-                      const int64_t* slot_mapping, int T, int Hkv, int D,
-                      void* k_cache, void* v_cache, int block_size, int kv_dtype,
-                      float k_scale, float v_scale) {
-    for (int t = 0; t < T; ++t) {
-        int64_t slot = slot_mapping[t];
-        if (slot < 0) continue;
-        for (int g = 0; g < Hkv; ++g)
-            for (int d = 0; d < D; ++d) {
-                uint16_t xk = k[t * src_stride + (int64_t)g * D + d];
-                uint16_t xv = v[t * src_stride + (int64_t)g * D + d];
-                int64_t ki = k_index(slot, g, d, Hkv, D, block_size);
-                int64_t vi = v_index(slot, g, d, Hkv, D, block_size);
-                if (kv_dtype == 0) {
-                    ((uint16_t*)k_cache)[ki] = xk;
-                    ((uint16_t*)v_cache)[vi] = xv;
+/* Which tokens a write thread handles: those whose slot pair (slot / 2) falls
+ * to it.  Every write to one slot (and to the two slots that share an NVFP4 V
+ * byte) then happens in one thread, in token order, so the bytes equal the
+ * serial write's for any slot mapping, repeated slots included. */
+static int write_share(int64_t slot, int tid, int nthreads) {
+    return slot >= 0 && (int)((slot / 2) % nthreads) == tid;
+}
+
+typedef struct {
+    const uint16_t *k, *v;
+    int64_t src_stride;
+    const int64_t* slot_mapping;
+    int T, Hkv, D;
+    void *k_cache, *v_cache;
+    int block_size, kv_dtype;
+    float k_scale, v_scale;
+    int tid, nthreads;
+} write_job;
+
+static void* cache_write_worker(void* arg) {
+    const write_job* j = (const write_job*)arg;
+    for (int t = 0; t < j->T; ++t) {
+        int64_t slot = j->slot_mapping[t];
+        if (!write_share(slot, j->tid, j->nthreads)) continue;
+        for (int g = 0; g < j->Hkv; ++g)
+            for (int d = 0; d < j->D; ++d) {
+                uint16_t xk = j->k[t * j->src_stride + (int64_t)g * j->D + d];
+                uint16_t xv = j->v[t * j->src_stride + (int64_t)g * j->D + d];
+                int64_t ki = k_index(slot, g, d, j->Hkv, j->D, j->block_size);
+                int64_t vi = v_index(slot, g, d, j->Hkv, j->D, j->block_size);
+                if (j->kv_dtype == 0) {
+                    ((uint16_t*)j->k_cache)[ki] = xk;
+                    ((uint16_t*)j->v_cache)[vi] = xv;
                 } else {
-                    ((uint8_t*)k_cache)[ki] = kvqo_e4m3_quantize(xk, k_scale);
-                    ((uint8_t*)v_cache)[vi] = kvqo_e4m3_quantize(xv, v_scale);
+                    ((uint8_t*)j->k_cache)[ki] = kvqo_e4m3_quantize(xk, j->k_scale);
+                    ((uint8_t*)j->v_cache)[vi] = kvqo_e4m3_quantize(xv, j->v_scale);
                 }
             }
     }
+    return NULL;
+}
+
+/* Runs worker over nthreads shares of the tokens (one share: the caller's thread). */
+static void run_write(write_job* base, void* (*worker)(void*), int nthreads) {
+    if (nthreads < 1) nthreads = 1;
+    write_job* jobs = (write_job*)malloc(sizeof(write_job) * (size_t)nthreads);
+    pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    for (int i = 0; i < nthreads; ++i) {
+        jobs[i] = *base;
+        jobs[i].tid = i;
+        jobs[i].nthreads = nthreads;
+    }
+    for (int i = 1; i < nthreads; ++i) pthread_create(&th[i], NULL, worker, &jobs[i]);
+    worker(&jobs[0]);
+    for (int i = 1; i < nthreads; ++i) pthread_join(th[i], NULL);
+    free(th);
+    free(jobs);
+}
+
+void kvqo_cache_write(const uint16_t* k, const uint16_t* v, int64_t src_stride,
+                      const int64_t* slot_mapping, int T, int Hkv, int D,
+                      void* k_cache, void* v_cache, int block_size, int kv_dtype,
+                      float k_scale, float v_scale, int nthreads) {
+    write_job j = {k, v, src_stride, slot_mapping, T, Hkv, D, k_cache, v_cache, block_size, kv_dtype,
+                   k_scale, v_scale, 0, 1};
+    run_write(&j, cache_write_worker, nthreads);
 }
 
 /* NVFP4: quantize one 16-element group x[0..15] into codes[16] and a scale code */
@@ -206,35 +250,48 @@ static uint8_t get_nibble(const uint8_t* p, int64_t nib_index) {
     return (nib_index % 2 == 0) ? (byte & 0xF) : (byte >> 4);
 }
 
-void kvqo_nvfp4_cache_write(const uint16_t* k, const uint16_t* v, int64_t src_stride,
-                            const int64_t* slot_mapping, int T, int Hkv, int D,
-                            uint8_t* k_cache, uint8_t* v_cache, int block_size,
-                            float k_gscale, float v_gscale) {
+static void* nvfp4_write_worker(void* arg) {
+    const write_job* j = (const write_job*)arg;
+    const int D = j->D, Hkv = j->Hkv, block_size = j->block_size;
     int64_t region = kvqo_nvfp4_region_bytes(D, block_size);
     int64_t codes_bytes = (int64_t)block_size * D / 2;
-    for (int t = 0; t < T; ++t) {
-        int64_t slot = slot_mapping[t];
-        if (slot < 0) continue;
+    uint8_t* k_cache = (uint8_t*)j->k_cache;
+    uint8_t* v_cache = (uint8_t*)j->v_cache;
+    for (int t = 0; t < j->T; ++t) {
+        int64_t slot = j->slot_mapping[t];
+        if (!write_share(slot, j->tid, j->nthreads)) continue;
         int64_t blk = slot / block_size, off = slot % block_size;
         for (int g = 0; g < Hkv; ++g) {
             uint8_t* kr = k_cache + (blk * Hkv + g) * region;
             uint8_t* vr = v_cache + (blk * Hkv + g) * region;
             for (int grp = 0; grp < D / 16; ++grp) {
                 uint8_t codes[16], sc;
-                const uint16_t* xk = k + t * src_stride + (int64_t)g * D + grp * 16;
-                nvfp4_group(xk, k_gscale, codes, &sc);
+                const uint16_t* xk = j->k + t * j->src_stride + (int64_t)g * D + grp * 16;
+                nvfp4_group(xk, j->k_scale, codes, &sc);
                 for (int i = 0; i < 16; ++i)
                     set_nibble(kr, off * D + grp * 16 + i, codes[i]);      /* [bs][D] nibbles */
                 kr[codes_bytes + off * (D / 16) + grp] = sc;
 
-                const uint16_t* xv = v + t * src_stride + (int64_t)g * D + grp * 16;
-                nvfp4_group(xv, v_gscale, codes, &sc);
+                const uint16_t* xv = j->v + t * j->src_stride + (int64_t)g * D + grp * 16;
+                nvfp4_group(xv, j->v_scale, codes, &sc);
                 for (int i = 0; i < 16; ++i)
                     set_nibble(vr, (int64_t)(grp * 16 + i) * block_size + off, codes[i]); /* [D][bs] nibbles */
                 vr[codes_bytes + (int64_t)grp * block_size + off] = sc;                  /* [D/16][bs] */
             }
         }
     }
+    return NULL;
+}
+
+void kvqo_nvfp4_cache_write(const uint16_t* k, const uint16_t* v, int64_t src_stride,
+                            const int64_t* slot_mapping, int T, int Hkv, int D,
+                            uint8_t* k_cache, uint8_t* v_cache, int block_size,
+                            float k_gscale, float v_gscale, int nthreads) {
+    write_job j = {k, v, src_stride, slot_mapping, T, Hkv, D, k_cache, v_cache, block_size, 2,
+                   k_gscale, v_gscale, 0, 1};
+    /* a V code byte holds two slots' nibbles (d * bs + off, d * bs + off + 1): with an
+       odd block size such a pair is not a slot pair, so write on one thread */
+    run_write(&j, nvfp4_write_worker, block_size % 2 ? 1 : nthreads);
 }
 
 double kvqo_nvfp4_k_value(const uint8_t* k_cache, int64_t slot, int g, int d,

@@ -107,20 +107,25 @@ int64_t kvqo_nvfp4_region_bytes(int D, int block_size);
 /* Write T tokens of K and V (bf16, [T][Hkv][D], token stride `src_stride`
  * elements) into the caches at slot_mapping[t]; slot < 0 skips the token.
  * kv_dtype 0 = BF16 (bit copy, scales unused), 1 = FP8 E4M3 with the given
- * per-layer scales.  Bytes not addressed are left unchanged. */
+ * per-layer scales.  Bytes not addressed are left unchanged.  Tokens are
+ * written in order; when one slot appears several times the last write
+ * stays.  `nthreads` > 1 shares the tokens out by slot pair (slot / 2), so
+ * every write to a slot happens in one thread in token order and the bytes
+ * do not depend on it. */
 void kvqo_cache_write(const uint16_t* k, const uint16_t* v, int64_t src_stride,
                       const int64_t* slot_mapping, int T, int Hkv, int D,
                       void* k_cache, void* v_cache, int block_size, int kv_dtype,
-                      float k_scale, float v_scale);
+                      float k_scale, float v_scale, int nthreads);
 
 /* NVFP4 write.  For each (token, head) row and each group of 16 consecutive
  * dims: bamax = max |x| (fp32); bscale = E4M3(bamax / fp32(6 * gscale));
  * e = fp32(value(bscale) * gscale); codes = E2M1(x / e) (fp32), or all zero
- * when e == 0. */
+ * when e == 0.  Order and threads as kvqo_cache_write (a V code byte holds
+ * the nibbles of a slot pair). */
 void kvqo_nvfp4_cache_write(const uint16_t* k, const uint16_t* v, int64_t src_stride,
                             const int64_t* slot_mapping, int T, int Hkv, int D,
                             uint8_t* k_cache, uint8_t* v_cache, int block_size,
-                            float k_gscale, float v_gscale);
+                            float k_gscale, float v_gscale, int nthreads);
 
 /* Dequantized value of element (slot, head g, dim d) of an NVFP4 K or V cache. */
 double kvqo_nvfp4_k_value(const uint8_t* k_cache, int64_t slot, int g, int d,

@@ -2,6 +2,7 @@
 against the pages' byte figures, and gather / scatter against numpy's own
 indexing of the cache viewed as [num_blocks][block_bytes]."""
 import numpy as np
+import pytest
 import torch
 
 import oracle
@@ -52,3 +53,27 @@ def test_round_trip_through_other_blocks_keeps_attention():
     bt[1, :5] = torch.from_numpy(new_ids)
     after = oracle.decode_attn(w.q, kc, vc, oracle.KV_FP8, bt, w.seq_lens, w.Hkv, 16, 0.02, 0.03, 0.125)
     assert np.array_equal(before, after)
+
+
+@pytest.mark.parametrize("fmt", [oracle.KV_BF16, oracle.KV_FP8, oracle.KV_NVFP4])
+def test_threaded_cache_write_equals_the_serial_write(fmt):
+    """Sharing the tokens out over threads by slot pair leaves every byte as the
+    one-thread write leaves it: repeated slots (last write stays), skipped
+    slots, neighbouring slots of one NVFP4 V byte, any slot order."""
+    w = workloads.make("mixed64", seed=31, seq_lens=[300, 77, 150], shape=dict(Hq=4, Hkv=2, D=64))
+    rng = np.random.default_rng(31)
+    sm = w.slot_mapping.numpy().copy()
+    sm[rng.choice(len(sm), 40, replace=False)] = -1                 # skipped
+    dup = rng.choice(len(sm), 60, replace=False)
+    sm[dup[:30]] = sm[dup[30:]]                                     # repeated slots
+    outs = []
+    for nthreads in (1, 3, 8):
+        if fmt == oracle.KV_NVFP4:
+            kc, vc = oracle.new_caches(fmt, w.num_blocks, w.Hkv, w.D, 16, fill=0x5A)
+            oracle.nvfp4_cache_write(w.k, w.v, sm, kc, vc, 16, 0.01, 0.02, nthreads=nthreads)
+        else:
+            kc, vc = oracle.new_caches(fmt, w.num_blocks, w.Hkv, w.D, 16, fill=0x5A)
+            oracle.cache_write(w.k, w.v, sm, kc, vc, fmt, 0.01, 0.02, nthreads=nthreads)
+        outs.append((kc, vc))
+    for kc, vc in outs[1:]:
+        assert np.array_equal(kc, outs[0][0]) and np.array_equal(vc, outs[0][1])
