@@ -187,37 +187,3 @@ def test_nvfp4_physical_placement_is_bit_identical(K):
     w2 = workloads.Workload(**{**w.__dict__, "block_tables": bt2, "slot_mapping": slots2})
     s2 = NvSetup(K, w2, scales=(s1.gk, s1.gv))
     assert torch.equal(s1.attend(), s2.attend())
-
-
-@pytest.mark.parametrize("units", [[(0, 2), (1, 7)]])
-def test_nvfp4_fullsize_sampled_units(K, units):
-    w = workloads.make("nvfp4_131k", device="cuda", seed=0)
-    say(f"nvfp4 full size: B={w.B} L={w.max_seq_len} Hq={w.Hq} Hkv={w.Hkv} D={w.D} "
-        f"split={K.kvq_decode_plan_split_tokens(w.B, w.Hkv, w.max_seq_len)}")
-    amax = torch.zeros(2, dtype=torch.float32, device="cuda")
-    K.kvq_amax_bf16(w.k, amax[0:1])
-    K.kvq_amax_bf16(w.v, amax[1:2])
-    gk, gv = K.kvq_nvfp4_calibrate(amax.cpu().tolist())
-    kc, vc = K.new_nvfp4_caches(w.num_blocks, w.Hkv, w.D)
-    K.kvq_nvfp4_cache_write(w.k, w.v, w.prefill_slots(), kc, vc, gk, gv)
-    rows = w.last_token_rows()
-    rows = rows[rows >= 0].cuda()
-    K.kvq_nvfp4_cache_write(w.k[rows], w.v[rows], w.slot_mapping[rows].contiguous(), kc, vc, gk, gv)
-    sm = float(np.float32(1.0 / math.sqrt(w.D)))
-    out = torch.empty(w.B, w.Hq, w.D, dtype=torch.float32, device="cuda")
-    ws = K.new_workspace(w.B, w.Hq, w.Hkv, w.D, w.max_seq_len)
-    sl = torch.tensor(w.seq_lens, dtype=torch.int32, device="cuda")
-    K.kvq_nvfp4_paged_decode_attn(w.q, kc, vc, w.block_tables, sl, w.max_seq_len, w.Hkv, gk, gv, sm, out, ws)
-    torch.cuda.synchronize()
-    G = w.G
-    for b, g in units:
-        L, s0 = w.seq_lens[b], w.seq_starts[b]
-        nblk = (L + 15) // 16
-        okc, ovc = oracle.new_caches(oracle.KV_NVFP4, nblk, 1, w.D, 16)
-        oracle.nvfp4_cache_write(w.k[s0:s0 + L, g:g + 1].cpu(), w.v[s0:s0 + L, g:g + 1].cpu(), np.arange(L),
-                                 okc, ovc, 16, gk, gv)
-        phys = w.block_tables[b, :nblk].long()
-        assert np.array_equal(kc[phys, g].cpu().numpy(), okc[:, 0]) and np.array_equal(vc[phys, g].cpu().numpy(), ovc[:, 0])
-        ref = oracle.decode_attn(w.q[b:b + 1, g * G:(g + 1) * G].cpu(), okc, ovc, oracle.KV_NVFP4,
-                                 np.arange(nblk, dtype=np.int32)[None], [L], 1, 16, gk, gv, sm, nthreads=8)
-        assert_attention_close(out[b, g * G:(g + 1) * G].cpu().numpy()[None], ref, f"nvfp4 full b={b} g={g}")
