@@ -9,7 +9,8 @@
 - NVFP4 decode attention matches the oracle's fp64 attention over the same
   dequantized values within max abs 2e-3 / rel L2 1e-3 (fp32 epilogue), and
   bf16 output equals the fp32 output rounded to nearest even; physical block
-  placement changes nothing; full size on sampled units.
+  placement changes nothing.  The full 2 x 131,072 shape is checked on every
+  unit in test_gpu_fullsize.py.
 """
 import math
 
