@@ -57,7 +57,7 @@ extern "C" {
  *    host-memory block tier
  * 3: kvq_check_flags and the checked build libkvq_check.so
  * 4: kvq_paged_decode_attn_mq_append */
-#define KVQ_ABI_VERSION 4
+#define KVQ_ABI_VERSION 5
 
 enum kvq_status {
     KVQ_OK = 0,
@@ -262,6 +262,12 @@ int kvq_decode_plan_split_tokens(int B, int Hkv, int max_seq_len, int block_size
  * other tokens are preserved. */
 int kvq_nvfp4_calibrate(const float* amax_host, float* gscale_host, int n);
 size_t kvq_nvfp4_region_bytes(int D, int block_size);
+
+/* Bytes of one physical block of an NVFP4 K (or V) cache, all Hkv heads:
+ * Hkv * kvq_nvfp4_region_bytes(D, block_size) (576 * Hkv at D 64, block 16:
+ * 4.5 bits per element, [RUN26]).  Host only; 0 if Hkv <= 0 or the region
+ * size is 0 (D not a positive multiple of 16, block_size odd or <= 0). */
+size_t kvq_nvfp4_cache_bytes_per_block(int Hkv, int D, int block_size);
 
 /* As kvq_cache_write, into NVFP4 caches [num_blocks][Hkv][region] bytes, with
  * the per-tensor global scales k_gscale, v_gscale (> 0, finite). */

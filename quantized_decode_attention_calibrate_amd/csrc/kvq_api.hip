@@ -144,6 +144,11 @@ size_t kvq_nvfp4_region_bytes(int D, int block_size) {
     return (size_t)block_size * D / 2 + (size_t)block_size * D / 16;
 }
 
+size_t kvq_nvfp4_cache_bytes_per_block(int Hkv, int D, int block_size) {
+    if (Hkv <= 0) return 0;
+    return (size_t)Hkv * kvq_nvfp4_region_bytes(D, block_size);
+}
+
 int kvq_e2m1_decode(const uint8_t* codes_dev, uint8_t scale_code, void* out_dev, int64_t n_bytes, void* hip_stream) {
     if (n_bytes < 0) return KVQ_EINVAL;
     if (n_bytes == 0) return KVQ_OK;

@@ -55,6 +55,7 @@ def _load(path: str) -> ctypes.CDLL:
                                          I, I]),
         "kvq_nvfp4_calibrate": (I, [P, P, I]),
         "kvq_nvfp4_region_bytes": (SZ, [I, I]),
+        "kvq_nvfp4_cache_bytes_per_block": (SZ, [I, I, I]),
         "kvq_nvfp4_cache_write": (I, [P, P, I64, P, I, I, I, P, P, I, I, F, F, P]),
         "kvq_nvfp4_paged_decode_attn": (I, [P, P, P, P, I, P, I, I, I, I, I, I, I, F, F, F, P, I, P, SZ, P]),
         "kvq_nvfp4_paged_decode_attn_ex": (I, [P, P, P, P, I, P, I, I, I, I, I, I, I, F, F, F, P, I, P, SZ, P,
@@ -194,6 +195,10 @@ def kvq_nvfp4_calibrate(amax) -> list:
 
 def kvq_nvfp4_region_bytes(D: int) -> int:
     return _lib.kvq_nvfp4_region_bytes(D, BLOCK_SIZE)
+
+
+def kvq_nvfp4_cache_bytes_per_block(Hkv: int, D: int) -> int:
+    return _lib.kvq_nvfp4_cache_bytes_per_block(Hkv, D, BLOCK_SIZE)
 
 
 def new_nvfp4_caches(num_blocks: int, Hkv: int, D: int, device="cuda"):

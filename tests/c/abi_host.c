@@ -30,7 +30,8 @@ int main(void) {
         (any_fn)kvq_cache_write, (any_fn)kvq_decode_workspace_bytes, (any_fn)kvq_paged_decode_attn,
         (any_fn)kvq_decode_workspace_bytes_ex, (any_fn)kvq_paged_decode_attn_ex,
         (any_fn)kvq_paged_decode_attn_append, (any_fn)kvq_decode_plan_split_tokens, (any_fn)kvq_nvfp4_calibrate,
-        (any_fn)kvq_nvfp4_region_bytes, (any_fn)kvq_nvfp4_cache_write, (any_fn)kvq_nvfp4_paged_decode_attn,
+        (any_fn)kvq_nvfp4_region_bytes, (any_fn)kvq_nvfp4_cache_bytes_per_block,
+        (any_fn)kvq_nvfp4_cache_write, (any_fn)kvq_nvfp4_paged_decode_attn,
         (any_fn)kvq_nvfp4_paged_decode_attn_ex, (any_fn)kvq_nvfp4_paged_decode_attn_append,
         (any_fn)kvq_decode_workspace_bytes_mq, (any_fn)kvq_paged_decode_attn_mq,
         (any_fn)kvq_nvfp4_paged_decode_attn_mq, (any_fn)kvq_paged_decode_attn_mq_append,
@@ -62,6 +63,7 @@ int main(void) {
     CHECK(kvq_decode_workspace_bytes(1, 64, 8, 64, 65536, 16) > 0);
     CHECK(kvq_decode_workspace_bytes_ex(1, 8, 2, 64, 100, 16, 100) == 0);   /* split not a multiple of 64 */
     CHECK(kvq_nvfp4_region_bytes(64, 16) == 9 * 64);
+    CHECK(kvq_nvfp4_cache_bytes_per_block(8, 64, 16) == 8 * 576 && kvq_nvfp4_cache_bytes_per_block(0, 64, 16) == 0);
 
     /* host validation: rejected before any HIP call (pointers never used) */
     char fake[64];

@@ -52,7 +52,7 @@ def test_check_flags_host_side(K):
     assert K.lib().kvq_check_flags(None, 0) == K.KVQ_EINVAL
     assert K.open_library(K.CHECK_LIB_PATH).kvq_check_flags(None, 0) == K.KVQ_EINVAL
     want = int(re.search(r"#define KVQ_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
-    assert K.kvq_abi_version() == want == 4
+    assert K.kvq_abi_version() == want == 5
     assert K.kvq_strerror(-3) == "workspace too small"
 
 
@@ -157,6 +157,10 @@ def test_nvfp4_host_calls(K):
         K.kvq_nvfp4_calibrate([float("nan")])
     for D in (64, 128, 256):
         assert K.kvq_nvfp4_region_bytes(D) == oracle.nvfp4_region_bytes(D, 16) == 9 * D
+        for Hkv in (1, 2, 8):
+            # one physical block of an NVFP4 cache: the oracle's block bytes (4.5 bits per element)
+            assert K.kvq_nvfp4_cache_bytes_per_block(Hkv, D) == oracle.block_bytes(oracle.KV_NVFP4, Hkv, D) \
+                == Hkv * 16 * D * 4.5 / 8 == K.kvq_cache_block_bytes(K.KVQ_FORMAT_NVFP4, Hkv, D)
     L = K.lib()
     args = [FAKE, FAKE, 128, FAKE, 5, 2, 64, FAKE, FAKE, 4, 16, 0.5, 0.5, None]
     assert L.kvq_nvfp4_cache_write(*args[:11], 0.0, 0.5, None) == -1
