@@ -20,6 +20,7 @@ KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_EWORKSPACE, KVQ_EHIP = 0, -1, -2, -3, 
 KVQ_KV_BF16, KVQ_KV_FP8_E4M3 = 0, 1
 KVQ_OUT_BF16, KVQ_OUT_F32 = 0, 1
 KVQ_IMPL_AUTO, KVQ_IMPL_VALU, KVQ_IMPL_MFMA = 0, 1, 2
+KVQ_FORMAT_NVFP4 = 2   # cache-format tag of kvq_cache_block_bytes (the C ABI has separate NVFP4 calls)
 BLOCK_SIZE = 16
 
 
@@ -147,6 +148,56 @@ def _ptr(t) -> int:
     return 0 if t is None else t.data_ptr()
 
 
+def _require(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+_FMT_NAME = {0: "BF16", 1: "FP8 E4M3", 2: "NVFP4"}
+
+
+def _caches(k_cache: torch.Tensor, v_cache: torch.Tensor, fmt: int, Hkv: int, D: int) -> int:
+    """Checks that K and V caches have the dtype and layout the call's format
+    assumes (so no kernel can index past them): FP8 uint8 and BF16 bfloat16
+    [num_blocks][Hkv][16][D] (K) and [num_blocks][Hkv][D][16] (V); NVFP4
+    uint8 [num_blocks][Hkv][kvq_nvfp4_region_bytes(D)] both; contiguous, on
+    one GPU.  Returns num_blocks."""
+    name = _FMT_NAME.get(fmt, str(fmt))
+    _require(fmt in _FMT_NAME, f"unknown cache format {fmt}")
+    want = torch.bfloat16 if fmt == KVQ_KV_BF16 else torch.uint8
+    for t, which in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _require(isinstance(t, torch.Tensor) and t.dtype == want,
+                 f"{which}: a {name} cache is {want}, got {getattr(t, 'dtype', type(t))}")
+    if fmt == KVQ_FORMAT_NVFP4:
+        r = kvq_nvfp4_region_bytes(D)
+        shape_k = shape_v = (Hkv, r)
+    else:
+        shape_k, shape_v = (Hkv, BLOCK_SIZE, D), (Hkv, D, BLOCK_SIZE)
+    _require(k_cache.dim() == 1 + len(shape_k) and tuple(k_cache.shape[1:]) == shape_k,
+             f"k_cache: a {name} cache is [num_blocks]{list(shape_k)}, got {list(k_cache.shape)}")
+    _require(v_cache.dim() == 1 + len(shape_v) and tuple(v_cache.shape[1:]) == shape_v,
+             f"v_cache: a {name} cache is [num_blocks]{list(shape_v)}, got {list(v_cache.shape)}")
+    _require(k_cache.shape[0] == v_cache.shape[0], "k_cache and v_cache hold different numbers of blocks")
+    _require(k_cache.is_contiguous() and v_cache.is_contiguous(), "caches must be contiguous")
+    return int(k_cache.shape[0])
+
+
+def _same_gpu(*tensors) -> None:
+    """Every tensor (None skipped) on one CUDA device."""
+    ts = [t for t in tensors if t is not None]
+    dev = ts[0].device
+    _require(dev.type == "cuda", f"tensors must be on a GPU, got {dev}")
+    for t in ts[1:]:
+        _require(t.device == dev, f"tensors on different devices: {dev} and {t.device}")
+
+
+def _tables(block_tables: torch.Tensor, seq_lens: torch.Tensor, B: int) -> None:
+    _require(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.is_contiguous()
+             and block_tables.shape[0] == B, "block_tables: contiguous int32 [B][max_blocks]")
+    _require(seq_lens.dtype == torch.int32 and tuple(seq_lens.shape) == (B,) and seq_lens.is_contiguous(),
+             "seq_lens: contiguous int32 [B]")
+
+
 def kvq_strerror(status: int) -> str:
     return _lib.kvq_strerror(status).decode()
 
@@ -214,9 +265,11 @@ def kvq_nvfp4_cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.
     T, Hkv, D = k.shape
     assert v.shape == k.shape and k.stride(0) == v.stride(0) and k.stride(2) == 1 and k.stride(1) == D
     assert slot_mapping.shape == (T,) and slot_mapping.is_contiguous()
+    num_blocks = _caches(k_cache, v_cache, KVQ_FORMAT_NVFP4, Hkv, D)
+    _same_gpu(k, v, slot_mapping, k_cache, v_cache)
     return _run("kvq_nvfp4_cache_write", _lib.kvq_nvfp4_cache_write, (
         _ptr(k), _ptr(v), k.stride(0), _ptr(slot_mapping), T, Hkv, D, _ptr(k_cache), _ptr(v_cache),
-        k_cache.shape[0], BLOCK_SIZE, k_gscale, v_gscale, _stream(stream)),
+        num_blocks, BLOCK_SIZE, k_gscale, v_gscale, _stream(stream)),
         prepare, (k, v, slot_mapping, k_cache, v_cache))
 
 
@@ -226,8 +279,9 @@ def kvq_nvfp4_paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache:
                                 workspace: torch.Tensor, split_tokens: int = 0, stream=None, prepare: bool = False):
     B, Hq, D = q.shape
     assert q.dtype == torch.bfloat16 and q.is_contiguous() and out.is_contiguous() and out.shape == q.shape
-    assert block_tables.dtype == torch.int32 and block_tables.is_contiguous() and block_tables.shape[0] == B
-    assert seq_lens.dtype == torch.int32 and seq_lens.shape == (B,)
+    _tables(block_tables, seq_lens, B)
+    _caches(k_cache, v_cache, KVQ_FORMAT_NVFP4, Hkv, D)
+    _same_gpu(q, k_cache, v_cache, block_tables, seq_lens, out, workspace)
     out_dtype = {torch.bfloat16: KVQ_OUT_BF16, torch.float32: KVQ_OUT_F32}[out.dtype]
     return _run("kvq_nvfp4_paged_decode_attn", _lib.kvq_nvfp4_paged_decode_attn_ex, (
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens),
@@ -251,8 +305,9 @@ def kvq_nvfp4_paged_decode_attn_append(k_new: torch.Tensor, v_new: torch.Tensor,
     assert k_new.shape == (B, Hkv, D) and v_new.shape == k_new.shape and k_new.stride(0) == v_new.stride(0)
     assert k_new.stride(2) == 1 and k_new.stride(1) == D and v_new.stride(2) == 1 and v_new.stride(1) == D
     assert slot_mapping.shape == (B,) and slot_mapping.is_contiguous()
-    assert block_tables.dtype == torch.int32 and block_tables.is_contiguous() and block_tables.shape[0] == B
-    assert seq_lens.dtype == torch.int32 and seq_lens.shape == (B,)
+    _tables(block_tables, seq_lens, B)
+    _caches(k_cache, v_cache, KVQ_FORMAT_NVFP4, Hkv, D)
+    _same_gpu(k_new, v_new, slot_mapping, q, k_cache, v_cache, block_tables, seq_lens, out, workspace)
     out_dtype = {torch.bfloat16: KVQ_OUT_BF16, torch.float32: KVQ_OUT_F32}[out.dtype]
     return _run("kvq_nvfp4_paged_decode_attn_append", _lib.kvq_nvfp4_paged_decode_attn_append, (
         _ptr(k_new), _ptr(v_new), k_new.stride(0), _ptr(slot_mapping), _ptr(q), _ptr(k_cache), _ptr(v_cache),
@@ -291,7 +346,9 @@ def kvq_cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor
     T, Hkv, D = k.shape
     assert v.shape == k.shape and k.stride(0) == v.stride(0) and k.stride(2) == 1 and k.stride(1) == D
     assert slot_mapping.shape == (T,) and slot_mapping.is_contiguous()
-    num_blocks = k_cache.shape[0]
+    _require(kv_dtype in (KVQ_KV_BF16, KVQ_KV_FP8_E4M3), f"kv_dtype {kv_dtype}: BF16 or FP8 E4M3")
+    num_blocks = _caches(k_cache, v_cache, kv_dtype, Hkv, D)
+    _same_gpu(k, v, slot_mapping, k_cache, v_cache)
     return _run("kvq_cache_write", _lib.kvq_cache_write, (
         _ptr(k), _ptr(v), k.stride(0), _ptr(slot_mapping), T, Hkv, D, _ptr(k_cache), _ptr(v_cache),
         num_blocks, BLOCK_SIZE, kv_dtype, k_scale, v_scale, _stream(stream)),
@@ -320,8 +377,10 @@ def kvq_paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
     """q bf16 [B][Hq][D]; out bf16 or fp32 [B][Hq][D]; block_tables int32 [B][max_blocks]; seq_lens int32 [B]."""
     B, Hq, D = q.shape
     assert q.dtype == torch.bfloat16 and q.is_contiguous() and out.is_contiguous() and out.shape == q.shape
-    assert block_tables.dtype == torch.int32 and block_tables.is_contiguous() and block_tables.shape[0] == B
-    assert seq_lens.dtype == torch.int32 and seq_lens.shape == (B,)
+    _tables(block_tables, seq_lens, B)
+    _require(kv_dtype in (KVQ_KV_BF16, KVQ_KV_FP8_E4M3), f"kv_dtype {kv_dtype}: BF16 or FP8 E4M3")
+    _caches(k_cache, v_cache, kv_dtype, Hkv, D)
+    _same_gpu(q, k_cache, v_cache, block_tables, seq_lens, out, workspace)
     out_dtype = {torch.bfloat16: KVQ_OUT_BF16, torch.float32: KVQ_OUT_F32}[out.dtype]
     return _run("kvq_paged_decode_attn", _lib.kvq_paged_decode_attn_ex, (
         _ptr(q), _ptr(k_cache), _ptr(v_cache), kv_dtype, _ptr(block_tables), block_tables.shape[1],
@@ -346,8 +405,10 @@ def kvq_paged_decode_attn_append(k_new: torch.Tensor, v_new: torch.Tensor, slot_
     assert k_new.shape == (B, Hkv, D) and v_new.shape == k_new.shape and k_new.stride(0) == v_new.stride(0)
     assert k_new.stride(2) == 1 and k_new.stride(1) == D and v_new.stride(2) == 1 and v_new.stride(1) == D
     assert slot_mapping.shape == (B,) and slot_mapping.is_contiguous()
-    assert block_tables.dtype == torch.int32 and block_tables.is_contiguous() and block_tables.shape[0] == B
-    assert seq_lens.dtype == torch.int32 and seq_lens.shape == (B,)
+    _tables(block_tables, seq_lens, B)
+    _require(kv_dtype in (KVQ_KV_BF16, KVQ_KV_FP8_E4M3), f"kv_dtype {kv_dtype}: BF16 or FP8 E4M3")
+    _caches(k_cache, v_cache, kv_dtype, Hkv, D)
+    _same_gpu(k_new, v_new, slot_mapping, q, k_cache, v_cache, block_tables, seq_lens, out, workspace)
     out_dtype = {torch.bfloat16: KVQ_OUT_BF16, torch.float32: KVQ_OUT_F32}[out.dtype]
     return _run("kvq_paged_decode_attn_append", _lib.kvq_paged_decode_attn_append, (
         _ptr(k_new), _ptr(v_new), k_new.stride(0), _ptr(slot_mapping), _ptr(q), _ptr(k_cache), _ptr(v_cache),
@@ -371,11 +432,12 @@ def new_workspace_mq(B: int, q_len: int, Hq: int, Hkv: int, D: int, max_seq_len:
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
-def _mq_args(q, block_tables, seq_lens, out):
+def _mq_args(q, block_tables, seq_lens, out, k_cache, v_cache, fmt, Hkv, workspace, *more):
     B, q_len, Hq, D = q.shape
     assert q.dtype == torch.bfloat16 and q.is_contiguous() and out.is_contiguous() and out.shape == q.shape
-    assert block_tables.dtype == torch.int32 and block_tables.is_contiguous() and block_tables.shape[0] == B
-    assert seq_lens.dtype == torch.int32 and seq_lens.shape == (B,)
+    _tables(block_tables, seq_lens, B)
+    _caches(k_cache, v_cache, fmt, Hkv, D)
+    _same_gpu(q, k_cache, v_cache, block_tables, seq_lens, out, workspace, *more)
     out_dtype = {torch.bfloat16: KVQ_OUT_BF16, torch.float32: KVQ_OUT_F32}[out.dtype]
     return B, q_len, Hq, D, out_dtype
 
@@ -387,7 +449,8 @@ def kvq_paged_decode_attn_mq(q: torch.Tensor, k_cache: torch.Tensor, v_cache: to
                              prepare: bool = False):
     """q bf16 [B][q_len][Hq][D] (the q_len newest tokens, already in the cache);
     out bf16 or fp32 [B][q_len][Hq][D]; window > 0: sliding-window attention."""
-    B, q_len, Hq, D, out_dtype = _mq_args(q, block_tables, seq_lens, out)
+    _require(kv_dtype in (KVQ_KV_BF16, KVQ_KV_FP8_E4M3), f"kv_dtype {kv_dtype}: BF16 or FP8 E4M3")
+    B, q_len, Hq, D, out_dtype = _mq_args(q, block_tables, seq_lens, out, k_cache, v_cache, kv_dtype, Hkv, workspace)
     return _run("kvq_paged_decode_attn_mq", _lib.kvq_paged_decode_attn_mq, (
         _ptr(q), q_len, window, _ptr(k_cache), _ptr(v_cache), kv_dtype, _ptr(block_tables), block_tables.shape[1],
         _ptr(seq_lens), max_seq_len, B, Hq, Hkv, D, BLOCK_SIZE, k_cache.shape[0], k_scale, v_scale, sm_scale,
@@ -407,7 +470,9 @@ def kvq_paged_decode_attn_mq_append(k_new: torch.Tensor, v_new: torch.Tensor, sl
     (token rows may be strided); slot_mapping int64 [B][q_len], the slots of
     positions seq_lens[b] - q_len + i (or < 0: not written); the rest as
     kvq_paged_decode_attn_mq."""
-    B, q_len, Hq, D, out_dtype = _mq_args(q, block_tables, seq_lens, out)
+    _require(kv_dtype in (KVQ_KV_BF16, KVQ_KV_FP8_E4M3), f"kv_dtype {kv_dtype}: BF16 or FP8 E4M3")
+    B, q_len, Hq, D, out_dtype = _mq_args(q, block_tables, seq_lens, out, k_cache, v_cache, kv_dtype, Hkv, workspace,
+                                          k_new, v_new, slot_mapping)
     assert k_new.dtype == torch.bfloat16 and v_new.dtype == torch.bfloat16 and slot_mapping.dtype == torch.int64
     assert k_new.shape == (B, q_len, Hkv, D) and v_new.shape == k_new.shape
     assert k_new.stride(0) == q_len * k_new.stride(1) and k_new.stride(1) == v_new.stride(1)
@@ -429,7 +494,8 @@ def kvq_nvfp4_paged_decode_attn_mq(q: torch.Tensor, k_cache: torch.Tensor, v_cac
                                    workspace: torch.Tensor, split_tokens: int = 0, window: int = 0,
                                    stream=None, prepare: bool = False):
     """NVFP4 caches; otherwise as kvq_paged_decode_attn_mq."""
-    B, q_len, Hq, D, out_dtype = _mq_args(q, block_tables, seq_lens, out)
+    B, q_len, Hq, D, out_dtype = _mq_args(q, block_tables, seq_lens, out, k_cache, v_cache, KVQ_FORMAT_NVFP4, Hkv,
+                                          workspace)
     return _run("kvq_nvfp4_paged_decode_attn_mq", _lib.kvq_nvfp4_paged_decode_attn_mq, (
         _ptr(q), q_len, window, _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1],
         _ptr(seq_lens), max_seq_len, B, Hq, Hkv, D, BLOCK_SIZE, k_cache.shape[0], k_gscale, v_gscale, sm_scale,
@@ -440,8 +506,6 @@ def kvq_nvfp4_paged_decode_attn_mq(q: torch.Tensor, k_cache: torch.Tensor, v_cac
 
 # ---- block copies for a host-memory KV tier ----------------------------------------
 
-KVQ_FORMAT_NVFP4 = 2
-
 
 def kvq_cache_block_bytes(kv_format: int, Hkv: int, D: int) -> int:
     return _lib.kvq_cache_block_bytes(kv_format, Hkv, D, BLOCK_SIZE)
@@ -451,14 +515,25 @@ def _nbytes(t: torch.Tensor) -> int:
     return t.numel() * t.element_size()
 
 
+def _block_cache(cache: torch.Tensor, block_bytes: int) -> None:
+    _require(cache.is_contiguous() and block_bytes > 0 and _nbytes(cache) % block_bytes == 0,
+             "a cache for block copies is contiguous and holds whole blocks of block_bytes")
+
+
 def kvq_gather_blocks(cache: torch.Tensor, block_bytes: int, ids: torch.Tensor, dst: torch.Tensor, stream=None):
     assert ids.dtype == torch.int32 and ids.is_contiguous() and _nbytes(dst) >= ids.numel() * block_bytes
+    _block_cache(cache, block_bytes)
+    _require(dst.is_contiguous(), "dst must be contiguous")
+    _same_gpu(cache, ids, dst)
     _check("kvq_gather_blocks", _lib.kvq_gather_blocks(_ptr(cache), block_bytes, _ptr(ids), ids.numel(), _ptr(dst),
                                                        _stream(stream)))
 
 
 def kvq_scatter_blocks(src: torch.Tensor, block_bytes: int, ids: torch.Tensor, cache: torch.Tensor, stream=None):
     assert ids.dtype == torch.int32 and ids.is_contiguous() and _nbytes(src) >= ids.numel() * block_bytes
+    _block_cache(cache, block_bytes)
+    _require(src.is_contiguous(), "src must be contiguous")
+    _same_gpu(cache, ids, src)
     _check("kvq_scatter_blocks", _lib.kvq_scatter_blocks(_ptr(src), block_bytes, _ptr(ids), ids.numel(),
                                                          _ptr(cache), _stream(stream)))
 
@@ -470,6 +545,10 @@ def kvq_offload_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_bytes
     assert ids.dtype == torch.int32 and ids.is_contiguous()
     assert _nbytes(staging) >= 2 * n * block_bytes and _nbytes(host_dst) >= 2 * n * block_bytes
     assert host_dst.device.type == "cpu" and host_dst.is_contiguous()
+    _block_cache(k_cache, block_bytes)
+    _block_cache(v_cache, block_bytes)
+    _require(staging.is_contiguous(), "staging must be contiguous")
+    _same_gpu(k_cache, v_cache, ids, staging)
     _check("kvq_offload_blocks", _lib.kvq_offload_blocks(_ptr(k_cache), _ptr(v_cache), block_bytes, _ptr(ids), n,
                                                          _ptr(staging), _ptr(host_dst), _stream(stream)))
 
@@ -480,6 +559,10 @@ def kvq_restore_blocks(host_src: torch.Tensor, staging: torch.Tensor, block_byte
     assert ids.dtype == torch.int32 and ids.is_contiguous()
     assert _nbytes(staging) >= 2 * n * block_bytes and _nbytes(host_src) >= 2 * n * block_bytes
     assert host_src.device.type == "cpu" and host_src.is_contiguous()
+    _block_cache(k_cache, block_bytes)
+    _block_cache(v_cache, block_bytes)
+    _require(staging.is_contiguous(), "staging must be contiguous")
+    _same_gpu(k_cache, v_cache, ids, staging)
     _check("kvq_restore_blocks", _lib.kvq_restore_blocks(_ptr(host_src), _ptr(staging), block_bytes, _ptr(ids), n,
                                                          _ptr(k_cache), _ptr(v_cache), _stream(stream)))
 
@@ -490,9 +573,10 @@ def kvq_paged_decode_attn_fp8qp(q: torch.Tensor, k_cache: torch.Tensor, v_cache:
                                 block_tables: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, Hkv: int,
                                 q_scale: float, k_scale: float, v_scale: float, sm_scale: float, out: torch.Tensor,
                                 workspace: torch.Tensor, split_tokens: int = 0, window: int = 0, stream=None,
-                             prepare: bool = False):
+                                prepare: bool = False):
     """FP8 cache, FP8 Q (q_scale) and FP8 P on FP8 MFMA; q [B][q_len][Hq][D] as kvq_paged_decode_attn_mq."""
-    B, q_len, Hq, D, out_dtype = _mq_args(q, block_tables, seq_lens, out)
+    B, q_len, Hq, D, out_dtype = _mq_args(q, block_tables, seq_lens, out, k_cache, v_cache, KVQ_KV_FP8_E4M3, Hkv,
+                                          workspace)
     return _run("kvq_paged_decode_attn_fp8qp", _lib.kvq_paged_decode_attn_fp8qp, (
         _ptr(q), q_len, window, _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1],
         _ptr(seq_lens), max_seq_len, B, Hq, Hkv, D, BLOCK_SIZE, k_cache.shape[0], q_scale, k_scale, v_scale,
