@@ -11,7 +11,7 @@ the path's tolerance) and against the two-launch step on the same inputs
 cache bytes and bit-identical outputs.  Cases: new tokens inside one chunk,
 across a chunk boundary, across a split boundary (64-token splits), a
 sequence shorter than q_len and one exactly q_len long, an empty sequence,
-skipped slots, a sliding window, q_len 1 to 16, D 64 and 128, FP8 and BF16.
+skipped slots, a sliding window, q_len 1 to 16, D 64, 128 and 256, FP8 and BF16.
 At q_len 1 both entry points run the one-token writer; the single-token
 call kvq_paged_decode_attn_append is checked the same way."""
 import numpy as np
@@ -34,6 +34,10 @@ CASES = [
     (155, [900, 260], dict(Hq=16, Hkv=2), 4, 128, 100),                 # sliding window
     (156, [300, 65], dict(Hq=16, Hkv=2), 1, 64, 0),                     # one new token
     (159, [300, 65, 1], dict(Hq=16, Hkv=2), 1, 64, 40),                # one new token, window: the multi-query entry
+    # D 256 (agents126k-shaped, G 6, 12 columns): a writer lane holds 4 dims (8-byte
+    # bf16 row loads, 4-byte FP8 / 8-byte BF16 K stores); 65 and 129: across a chunk
+    (160, [300, 65, 129, 2], dict(Hq=12, Hkv=2, D=256, calib_tokens=64), 2, 0, 0),
+    (161, [200, 65, 128], dict(Hq=12, Hkv=2, D=256, calib_tokens=64), 2, 64, 0),   # 64-token splits: 65 crosses one
 ]
 
 
