@@ -547,28 +547,65 @@ def read_clocks():
     return out or None
 
 
-def cpu_baseline(w, ks, vs, n_kv_heads, threads=None):
-    """The oracle (fp64 C, brute-force codecs) timed on this host's cores over a
-    bounded sample: n_kv_heads KV heads (all their G query heads) of the
-    workload's decode attention; scaled to the full step by Hkv / n_kv_heads.
-    The oracle's own cache write (untimed) supplies its FP8 cache."""
+def cpu_baseline(name):
+    """The oracle (fp64 C, brute-force codecs) timed on this host's cores on one
+    workload's decode attention in its KV format (FP8; NVFP4 for nvfp4_131k),
+    on bounded samples scaled to the whole step:
+    - N threads, N = the affinity core count: every sequence's units (all G
+      query heads) of the first n KV heads, n just large enough for 4 units per
+      thread; KV heads are independent and cost the same, so the step takes
+      Hkv / n times as long;
+    - one thread: the G query heads of KV head 0 of the longest sequence,
+      scaled by the step's (query head x token) pairs over the sample's.
+    The oracle's cache write of the sample (threaded, untimed) supplies its
+    cache.  Inputs are generated on the GPU and only the sample is copied."""
     import numpy as np
     import oracle
     import torch
-    G = w.Hq // w.Hkv
-    sub_k = w.k[:, :n_kv_heads, :].contiguous()
-    sub_v = w.v[:, :n_kv_heads, :].contiguous()
-    kc, vc = oracle.new_caches(oracle.KV_FP8, w.num_blocks, n_kv_heads, w.D, 16)
-    oracle.cache_write(sub_k, sub_v, w.slot_mapping, kc, vc, oracle.KV_FP8, ks, vs)
-    q = w.q[:, :n_kv_heads * G, :].contiguous()
+    from quantized_decode_attention_calibrate_amd import workloads
+    w = workloads.make(name, device="cuda", seed=0)
+    nv = name == "nvfp4_131k"
+    kvd, eb = (oracle.KV_NVFP4, NVFP4_BYTES) if nv else (oracle.KV_FP8, 1)
     cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
-    cores = max(1, min(cores, 16)) if threads is None else threads
+    G = w.G
+    n = min(w.Hkv, -(-4 * cores // (w.B * G)))
+    k = w.k[:, :n, :].cpu().contiguous()
+    v = w.v[:, :n, :].cpu().contiguous()
+    q = w.q[:, :n * G, :].cpu().contiguous()
+    slots, bt = w.slot_mapping.cpu(), w.block_tables.cpu()
+    lens = list(w.seq_lens)
+    B, Hq, Hkv, D = w.B, w.Hq, w.Hkv, w.D
+    del w
+    torch.cuda.empty_cache()
+    cal = oracle.nvfp4_calibrate if nv else oracle.calibrate
+    ks, vs = (float(x) for x in cal([oracle.amax_bf16(k), oracle.amax_bf16(v)]))
+    nb = int(bt.max()) + 1
+    kc, vc = oracle.new_caches(kvd, nb, n, k.shape[2], 16)
+    if nv:
+        oracle.nvfp4_cache_write(k, v, slots, kc, vc, 16, ks, vs, nthreads=cores)
+    else:
+        oracle.cache_write(k, v, slots, kc, vc, kvd, ks, vs, nthreads=cores)
+    sm = float(np.float32(1.0 / math.sqrt(k.shape[2])))
     t = time.perf_counter()
-    oracle.decode_attn(q, kc, vc, oracle.KV_FP8, w.block_tables, w.seq_lens, n_kv_heads, 16, ks, vs,
-                       float(np.float32(1.0 / math.sqrt(w.D))), nthreads=cores)
-    dt = time.perf_counter() - t
-    step_s = dt * w.Hkv / n_kv_heads
-    return step_s, cores, dt
+    oracle.decode_attn(q, kc, vc, kvd, bt, lens, n, 16, ks, vs, sm, nthreads=cores)
+    dt_n = time.perf_counter() - t
+    b1 = int(np.argmax(lens))
+    t = time.perf_counter()
+    oracle.decode_attn(q, kc, vc, kvd, bt, lens, n, 16, ks, vs, sm, units=[(b1, h) for h in range(G)], nthreads=1)
+    dt_1 = time.perf_counter() - t
+    step_n = dt_n * Hkv / n
+    step_1 = dt_1 * (Hq * sum(lens)) / (G * lens[b1])
+    attn_b, _ = step_bytes(B, Hq, Hkv, D, lens, eb, B)
+    fmt = "NVFP4" if nv else "FP8"
+    return {"value": round(attn_b / step_n / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "kv_tokens_per_s": round(sum(lens) / step_n, 1),
+            "sample": f"oracle {fmt} decode attention (fp64 C) of {name} on {cores} threads: KV heads 0..{n - 1} of "
+                      f"all {B} sequences ({n * G * B} of {Hq * B} (sequence, query head) units), {dt_n:.2f} s wall, "
+                      f"scaled by {Hkv}/{n} to the step ({step_n:.2f} s); the cache write is excluded",
+            "single_thread": {"value": round(attn_b / step_1 / 1e9, 5), "unit": "GB/s",
+                              "sample": f"{G} query heads of KV head 0 of sequence {b1} ({lens[b1]} tokens) on one "
+                                        f"thread: {dt_1:.2f} s wall, scaled by the step's (query head, token) pairs "
+                                        f"over the sample's to {step_1:.1f} s"}}
 
 
 def read_traffic(kernel_hash):
@@ -694,7 +731,6 @@ def main():
         return
     print(f"[bench] building {args.workload} on {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
     w = workloads.make(args.workload, device=dev, seed=0)
-    w_cpu = None
     pmc_reference(torch, K)
     fp8 = Layers(K, w, K.KVQ_KV_FP8_E4M3, args.layers, dev)
     print("[bench] timing FP8", file=sys.stderr, flush=True)
@@ -776,25 +812,18 @@ def main():
         print("[bench] quantization quality", file=sys.stderr, flush=True)
         result["quality"] = [measure_quality(torch, K, n) for n in ("gptoss65k", "agents126k")]
     if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        w_cpu = workloads.make(args.workload, device="cpu", seed=0)
-        amax_k = float(w_cpu.k.float().abs().max())
-        amax_v = float(w_cpu.v.float().abs().max())
-        ks, vs = K.kvq_calibrate([amax_k, amax_v])
-        nh = w_cpu.Hkv
-        step_s, cores, dt = cpu_baseline(w_cpu, ks, vs, n_kv_heads=nh)
-        result["cpu_baseline"] = {
-            "value": round(attn_b / step_s / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"oracle decode attention (fp64 C) over all {w_cpu.Hkv} KV heads ({w_cpu.Hq} query heads) "
-                      f"x {tokens} tokens of one layer: {dt:.2f} s wall on {cores} threads (the step's "
-                      "attention; the cache write is excluded)",
-            "kv_tokens_per_s": round(tokens / step_s, 1)}
-        # one thread over one KV head (its units are independent, so it scales by Hkv)
-        s1, _, dt1 = cpu_baseline(w_cpu, ks, vs, n_kv_heads=1, threads=1)
-        result["cpu_baseline"]["single_thread"] = {
-            "value": round(attn_b / s1 / 1e9, 5), "unit": "GB/s",
-            "sample": f"1 of {w_cpu.Hkv} KV heads ({w_cpu.Hq // w_cpu.Hkv} query heads) x {tokens} tokens on one "
-                      f"thread: {dt1:.2f} s wall, scaled by {w_cpu.Hkv}"}
+        # the oracle on the host's cores, once per workload: the headline workload's
+        # figure is cpu_baseline, every workload's is in cpu_baseline["per_workload"]
+        result["cpu_baseline"] = None
+        per = {}
+        for name in (args.workload, "agents126k", "mixed64", "nvfp4_131k"):
+            if name in per:
+                continue
+            print(f"[bench] timing the CPU oracle on a sample of {name}", file=sys.stderr, flush=True)
+            per[name] = cpu_baseline(name)
+            if args.no_other_workloads:
+                break
+        result["cpu_baseline"] = dict(per[args.workload], per_workload=per)
     print(json.dumps(result), flush=True)
 
 
