@@ -263,18 +263,19 @@ def test_nvfp4_append_host_validation(K):
 
 
 def test_prepared_call_defers_and_checks(K):
-    """prepare=True marshals the arguments without calling; calling the
-    PreparedCall runs the library call and raises on its status.  An invalid
-    kv_dtype fails host validation, so nothing is enqueued (CPU tensors are
-    never dereferenced)."""
+    """A PreparedCall holds marshalled arguments without calling; calling it
+    runs the library call and raises on its status.  An invalid kv_dtype
+    fails the library's host validation, so nothing is enqueued (the
+    addresses are never dereferenced).  The binding itself refuses the same
+    call before marshalling it."""
     import torch
-    k = torch.zeros(2, 1, 64, dtype=torch.bfloat16)
-    slots = torch.zeros(2, dtype=torch.int64)
-    kc = torch.zeros(4, 1, 16, 64, dtype=torch.uint8)
-    call = K.kvq_cache_write(k, k, slots, kc, kc, 7, 1.0, 1.0, stream=0, prepare=True)   # 0: the null stream
-    assert isinstance(call, K.PreparedCall)
+    args = (FAKE, FAKE, 64, FAKE, 2, 1, 64, FAKE, FAKE, 4, 16, 7, 1.0, 1.0, None)
+    call = K.PreparedCall("kvq_cache_write", K.lib().kvq_cache_write, args, ())
     with pytest.raises(K.KvqError) as e:
         call()
     assert e.value.status == K.KVQ_EINVAL
-    with pytest.raises(K.KvqError):
-        K.kvq_cache_write(k, k, slots, kc, kc, 7, 1.0, 1.0, stream=0)
+    k = torch.zeros(2, 1, 64, dtype=torch.bfloat16)
+    slots = torch.zeros(2, dtype=torch.int64)
+    kc = torch.zeros(4, 1, 16, 64, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="kv_dtype"):
+        K.kvq_cache_write(k, k, slots, kc, kc, 7, 1.0, 1.0, stream=0, prepare=True)
