@@ -202,14 +202,21 @@ def time_steps(torch, layers, steps, warmup, impl=0, fused=False):
     step_ms = ev[0].elapsed_time(ev[-1]) / steps
     layers.spread = sorted(ev[j].elapsed_time(ev[j + 1]) / (marks[j + 1] - marks[j]) for j in range(nb))
     # the attention call alone (split kernel + merge kernel), back to back over
-    # the rotated layer caches: its mean launch duration on the launch stream
+    # the rotated layer caches: its mean launch duration on the launch stream.
+    # A diagnostic for the format comparisons, measured the same way for every
+    # format: its own warmup and at least 200 calls, so the first launch after
+    # an idle GPU (several us) is not charged to a short loop
+    n_attn = max(steps, 200)
+    for i in range(max(warmup, 10)):
+        layers.run("attend", i, impl)
+    torch.cuda.synchronize()
     a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a0.record(st)
-    for i in range(steps):
+    for i in range(n_attn):
         layers.run("attend", i, impl)
     a1.record(st)
     torch.cuda.synchronize()
-    attn_ms = a0.elapsed_time(a1) / steps
+    attn_ms = a0.elapsed_time(a1) / n_attn
     return step_ms, attn_ms
 
 
@@ -660,10 +667,12 @@ def pmc_summary(fetch_csv, write_csv, workload="gptoss65k"):
     ref = next(k for k in fetch if k.startswith("e4m3_decode_kernel"))
     fscale = PMC_REF_CODES / (med(fetch[ref]) * 1024)
     wscale = 2 * PMC_REF_CODES / (med(write[ref]) * 1024)
-    # the step's call: the one-token append instantiation of the decode kernel (last
+    # the step's call: the one-token append instantiation of the decode kernel (fifth
     # template argument, the append mode, 1) and the merge; the plain call (mode 0) beside it
-    fused = [k for k in fetch if k.startswith("decode_mfma_kernel") and k.endswith(",1>")]
-    plain = [k for k in fetch if k.startswith("decode_mfma_kernel") and k.endswith(",0>")]
+    def append_mode(k):
+        return int(k[k.index("<") + 1:k.rindex(">")].split(",")[4])
+    fused = [k for k in fetch if k.startswith("decode_mfma_kernel") and append_mode(k) == 1]
+    plain = [k for k in fetch if k.startswith("decode_mfma_kernel") and append_mode(k) == 0]
     mrg = [k for k in fetch if k.startswith("merge_")]
     f_kib = {k: med(fetch[k]) for k in fused + plain + mrg}
     w_kib = {k: med(write[k]) for k in fused + plain + mrg}
