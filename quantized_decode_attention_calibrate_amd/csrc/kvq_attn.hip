@@ -1212,24 +1212,33 @@ __global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeArgs a) {
 // =============================================================================
 // One work-group per (sequence, query head) whose sequence has two or more
 // splits.  Every load is issued up front (the first 4 partial rows per thread
-// and all (m, l) pairs), so the merge costs about one memory round trip: the
-// split weights go to LDS, and P = 256 / (D/4) thread groups each sum every
-// P-th split of one 4-dim column before an LDS reduction.
+// and the first 64 (m, l) pairs), so the merge costs about one memory round
+// trip.  Wave 0 alone turns the (m, l) pairs into split weights and the
+// final scale with cross-lane reductions (permlane swaps and DPP row
+// rotations: no LDS round trips); after one barrier, P = 256 / (D/4) thread
+// groups each sum every P-th split of one 4-dim column, and a second barrier
+// joins the groups.
 constexpr int kMergeThreads = 256;
 
-__device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        const float t = shfl_xor(v, o);
-        v = is_max ? fmaxf(v, t) : v + t;
-    }
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-    __syncthreads();
-    float r = red[0];
-#pragma unroll
-    for (int w = 1; w < kMergeThreads / 64; ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
-    return r;
+// Rotation by K lanes within each row of 16 lanes (DPP row_ror:K).
+template <int K>
+__device__ __forceinline__ float row_ror(float v) {
+    return bits_f32((uint32_t)__builtin_amdgcn_mov_dpp((int)f32_bits(v), 0x120 + K, 0xF, 0xF, false));
+}
+// Max / sum over the 64 lanes of a wave, in every lane.
+__device__ __forceinline__ float wave_max(float v) {
+    v = max_xor32(max_xor16(v));
+    v = fmaxf(v, row_ror<8>(v));
+    v = fmaxf(v, row_ror<4>(v));
+    v = fmaxf(v, row_ror<2>(v));
+    return fmaxf(v, row_ror<1>(v));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+    v = sum_xor32(sum_xor16(v));
+    v += row_ror<8>(v);
+    v += row_ror<4>(v);
+    v += row_ror<2>(v);
+    return v + row_ror<1>(v);
 }
 
 template <int D>
@@ -1238,7 +1247,7 @@ __global__ void __launch_bounds__(kMergeThreads) merge_splits_kernel(DecodeArgs 
     constexpr int P = kMergeThreads / C4;     // split groups: 16, 8, 4 for D = 64, 128, 256
     constexpr int PRE = 4;                    // partial rows loaded up front per thread
     extern __shared__ float s_w[];            // [num_splits] split weights
-    __shared__ float red[kMergeThreads / 64];
+    __shared__ float s_scale;
     __shared__ f32x4 part[P][C4];
     const int hq = blockIdx.x;                // output row (b * q_len + i) * Hq + h
     const int b = hq / (a.Hq * a.q_len);
@@ -1257,22 +1266,26 @@ __global__ void __launch_bounds__(kMergeThreads) merge_splits_kernel(DecodeArgs 
         const int s = p + k * P;
         pre[k] = s < NS ? col[(int64_t)s * C4] : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    const float m0 = t < NS ? ml[2 * t] : -INFINITY, l0 = t < NS ? ml[2 * t + 1] : 0.f;
+    const float m0 = t < NS && t < 64 ? ml[2 * t] : -INFINITY, l0 = t < NS && t < 64 ? ml[2 * t + 1] : 0.f;
     const SeqRange sr = seq_range(a, b);
     const int S = (sr.L - sr.base + a.split_tokens - 1) / a.split_tokens;
     if (S <= 1) return;                       // written by the decode kernel
-    float m = t < S ? m0 : -INFINITY;
-    for (int s = t + kMergeThreads; s < S; s += kMergeThreads) m = fmaxf(m, ml[2 * s]);
-    const float M = block_reduce(m, red, true);
-    float den = 0.f;
-    for (int s = t; s < S; s += kMergeThreads) {
-        // M = -inf: no split saw a token for this row (a query before the start)
-        const float ms = s == t ? m0 : ml[2 * s], ls = s == t ? l0 : ml[2 * s + 1];
-        const float w = M == -INFINITY ? 0.f : fast_exp2(ms - M);
-        s_w[s] = w;
-        den += w * ls;
+    if (t < 64) {                             // wave 0: split weights and the final scale
+        float m = t < S ? m0 : -INFINITY;
+        for (int s = t + 64; s < S; s += 64) m = fmaxf(m, ml[2 * s]);
+        const float M = wave_max(m);
+        float den = 0.f;
+        for (int s = t; s < S; s += 64) {
+            // M = -inf: no split saw a token for this row (a query before the start)
+            const float ms = s == t ? m0 : ml[2 * s], ls = s == t ? l0 : ml[2 * s + 1];
+            const float w = M == -INFINITY ? 0.f : fast_exp2(ms - M);
+            s_w[s] = w;
+            den += w * ls;
+        }
+        den = wave_sum(den);
+        if (t == 0) s_scale = den > 0.f ? a.v_scale / den : 0.f;
     }
-    den = block_reduce(den, red, false);       // its barriers also publish s_w
+    __syncthreads();
     f32x4 num = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < PRE; ++k) {
@@ -1285,7 +1298,7 @@ __global__ void __launch_bounds__(kMergeThreads) merge_splits_kernel(DecodeArgs 
     if (p == 0) {
 #pragma unroll
         for (int q = 1; q < P; ++q) num += part[q][d4];
-        const float scale = den > 0.f ? a.v_scale / den : 0.f;
+        const float scale = s_scale;
         const int64_t o = (int64_t)hq * D + 4 * d4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) store_out(a, o + e, num[e] * scale);
