@@ -56,8 +56,10 @@ extern "C" {
 /* 2: multi-query and sliding-window decode, FP8 Q/P variant, fused append,
  *    host-memory block tier
  * 3: kvq_check_flags and the checked build libkvq_check.so
- * 4: kvq_paged_decode_attn_mq_append */
-#define KVQ_ABI_VERSION 5
+ * 4: kvq_paged_decode_attn_mq_append
+ * 5: kvq_nvfp4_cache_bytes_per_block
+ * 6: kvq_paged_decode_attn_scratch */
+#define KVQ_ABI_VERSION 6
 
 enum kvq_status {
     KVQ_OK = 0,
@@ -209,6 +211,30 @@ int kvq_paged_decode_attn_ex(const void* q_dev, const void* k_cache_dev, const v
                              void* out_dev, int out_dtype,
                              void* workspace_dev, size_t workspace_bytes, void* hip_stream,
                              int impl, int split_tokens);
+
+/* ---- decode attention without a workspace, for callers that cannot allocate ----
+ * For code that may not call hipMalloc or allocate through a framework: inside
+ * HIP graph capture, in a tight serving loop, or under a harness that forbids
+ * allocation.  kvq_paged_decode_attn with the same arguments, results and
+ * kernels (automatic split plan, MFMA family), except that the split partials
+ * go to the library's own scratch: a KVQ_SCRATCH_MAX_BYTES device array that
+ * each GPU the library runs on holds until the process ends.  The call
+ * allocates nothing.  Its first call on a device looks the array's address up
+ * (hipGetSymbolAddress, with that device current; the caller's stream must
+ * belong to the current device).
+ *   Returns KVQ_EWORKSPACE, before any HIP call, when the call needs more than
+ *   KVQ_SCRATCH_MAX_BYTES (kvq_decode_workspace_bytes of the same shape).
+ * Every call on one GPU shares that GPU's array and leaves its partials there
+ * (no call needs them cleared): calls that overlap on one GPU -- on different
+ * streams, or from different threads -- race and must be ordered by the
+ * caller. */
+#define KVQ_SCRATCH_MAX_BYTES (32u * 1024u * 1024u)
+int kvq_paged_decode_attn_scratch(const void* q_dev, const void* k_cache_dev, const void* v_cache_dev,
+                                  int kv_dtype, const int32_t* block_tables_dev, int max_blocks_per_seq,
+                                  const int32_t* seq_lens_dev, int max_seq_len,
+                                  int B, int Hq, int Hkv, int D, int block_size, int num_blocks,
+                                  float k_scale, float v_scale, float sm_scale,
+                                  void* out_dev, int out_dtype, void* hip_stream);
 
 /* kvq_paged_decode_attn_append: one decode step's cache write and attention
  * in one launch, the same result as kvq_cache_write of each sequence's newest

@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "kvq.h"
 #include "kvq_internal.h"
 
@@ -227,13 +229,51 @@ struct AppendArgs {
     const int64_t* slots;
 };
 
+// ---- the library's own scratch, for callers that cannot allocate ----------------
+// kvq_paged_decode_attn_scratch keeps the split partials here instead of in a
+// caller workspace: one array per GPU, held by the loaded code object until the
+// process ends, shared by every such call on that GPU (calls that overlap on one
+// GPU race).  Host code never passes the array's name to a kernel: its address
+// on each device comes from hipGetSymbolAddress, taken once per device with that
+// device current.
+static_assert(KVQ_SCRATCH_MAX_BYTES % 256 == 0, "scratch size is a multiple of 256 bytes");
+static __device__ __align__(256) unsigned char scratch[KVQ_SCRATCH_MAX_BYTES];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+struct ScratchSlot {
+    std::once_flag once;
+    void* ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxScratchDevices];
+}  // namespace
+
+// The current device's scratch address (first call per device: the lookup).
+static int scratch_address(void** out) {
+    int dev = -1;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= kMaxScratchDevices) return KVQ_EUNSUPPORTED;
+    ScratchSlot& slot = g_scratch[dev];
+    std::call_once(slot.once, [&slot] { slot.err = hipGetSymbolAddress(&slot.ptr, HIP_SYMBOL(scratch)); });
+    if (slot.err != hipSuccess) return hip_status(slot.err);
+    *out = slot.ptr;
+    return KVQ_OK;
+}
+
+// Where a decode call's split partials go: the caller's workspace, or the
+// library's scratch (checked against its size before any HIP call).
+enum WorkspaceMode { kCallerWorkspace = 0, kLibraryScratch = 1 };
+
 static int decode_common(int fmt, const void* q_dev, int q_len, int window, const void* k_cache_dev,
                          const void* v_cache_dev,
                          const int32_t* block_tables_dev, int max_blocks_per_seq, const int32_t* seq_lens_dev,
                          int max_seq_len, int B, int Hq, int Hkv, int D, int block_size, int num_blocks,
                          float k_scale, float v_scale, float sm_scale, void* out_dev, int out_dtype,
                          void* workspace_dev, size_t workspace_bytes, void* hip_stream, int impl, int split_tokens,
-                         float q_scale = 1.0f, const AppendArgs* app = nullptr) {
+                         float q_scale = 1.0f, const AppendArgs* app = nullptr,
+                         WorkspaceMode ws_mode = kCallerWorkspace) {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_seq_len < 0)
         return KVQ_EINVAL;
     if (q_len < 1 || q_len > kMaxQueryLen || window < 0) return KVQ_EINVAL;
@@ -253,14 +293,20 @@ static int decode_common(int fmt, const void* q_dev, int q_len, int window, cons
     if (fmt == kFmtFP8QP && !good_scale(q_scale)) return KVQ_EINVAL;
     if (B == 0) return KVQ_OK;
     if (!q_dev || !k_cache_dev || !v_cache_dev || !block_tables_dev || !seq_lens_dev || !out_dev ||
-        !workspace_dev)
+        (ws_mode == kCallerWorkspace && !workspace_dev))
         return KVQ_EINVAL;
     if (!aligned16(q_dev) || !aligned16(k_cache_dev) || !aligned16(v_cache_dev) || !aligned16(out_dev) ||
-        !aligned16(workspace_dev))
+        (ws_mode == kCallerWorkspace && !aligned16(workspace_dev)))
         return KVQ_EINVAL;
     const DecodePlan plan = plan_decode(B, Hkv, plan_span(max_seq_len, q_len, window), split_tokens);
     if (plan.num_splits > kMaxSplits) return KVQ_EUNSUPPORTED;
     const size_t need = decode_workspace_bytes(B * q_len, Hq, D, plan.num_splits);
+    if (ws_mode == kLibraryScratch) {
+        if (need > (size_t)KVQ_SCRATCH_MAX_BYTES) return KVQ_EWORKSPACE;
+        const int st = scratch_address(&workspace_dev);   // the first HIP call of this path
+        if (st != KVQ_OK) return st;
+        workspace_bytes = KVQ_SCRATCH_MAX_BYTES;
+    }
     if (workspace_bytes < need) return KVQ_EWORKSPACE;
     if (impl == KVQ_IMPL_AUTO || fmt == kFmtNVFP4) impl = KVQ_IMPL_MFMA;
 
@@ -312,6 +358,18 @@ int kvq_paged_decode_attn_ex(const void* q_dev, const void* k_cache_dev, const v
                          block_tables_dev, max_blocks_per_seq, seq_lens_dev, max_seq_len, B, Hq, Hkv, D,
                          block_size, num_blocks, k_scale, v_scale, sm_scale, out_dev, out_dtype, workspace_dev,
                          workspace_bytes, hip_stream, impl, split_tokens);
+}
+
+int kvq_paged_decode_attn_scratch(const void* q_dev, const void* k_cache_dev, const void* v_cache_dev, int kv_dtype,
+                                  const int32_t* block_tables_dev, int max_blocks_per_seq,
+                                  const int32_t* seq_lens_dev, int max_seq_len, int B, int Hq, int Hkv, int D,
+                                  int block_size, int num_blocks, float k_scale, float v_scale, float sm_scale,
+                                  void* out_dev, int out_dtype, void* hip_stream) {
+    if (kv_dtype != KVQ_KV_BF16 && kv_dtype != KVQ_KV_FP8_E4M3) return KVQ_EINVAL;
+    return decode_common(kv_dtype == KVQ_KV_FP8_E4M3 ? kFmtFP8 : kFmtBF16, q_dev, 1, 0, k_cache_dev, v_cache_dev,
+                         block_tables_dev, max_blocks_per_seq, seq_lens_dev, max_seq_len, B, Hq, Hkv, D,
+                         block_size, num_blocks, k_scale, v_scale, sm_scale, out_dev, out_dtype, nullptr, 0,
+                         hip_stream, KVQ_IMPL_AUTO, 0, 1.0f, nullptr, kLibraryScratch);
 }
 
 int kvq_nvfp4_paged_decode_attn_ex(const void* q_dev, const void* k_cache_dev, const void* v_cache_dev,

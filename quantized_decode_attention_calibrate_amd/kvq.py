@@ -55,6 +55,7 @@ def _load(path: str) -> ctypes.CDLL:
         "kvq_paged_decode_attn_ex": (I, [P, P, P, I, P, I, P, I, I, I, I, I, I, I, F, F, F, P, I, P, SZ, P,
                                          I, I]),
         "kvq_nvfp4_calibrate": (I, [P, P, I]),
+        "kvq_paged_decode_attn_scratch": (I, [P, P, P, I, P, I, P, I, I, I, I, I, I, I, F, F, F, P, I, P]),
         "kvq_nvfp4_region_bytes": (SZ, [I, I]),
         "kvq_nvfp4_cache_bytes_per_block": (SZ, [I, I, I]),
         "kvq_nvfp4_cache_write": (I, [P, P, I64, P, I, I, I, P, P, I, I, F, F, P]),
@@ -388,6 +389,30 @@ def kvq_paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
         _ptr(out), out_dtype, _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream),
         impl, split_tokens),
         prepare, (q, k_cache, v_cache, block_tables, seq_lens, out, workspace))
+
+
+KVQ_SCRATCH_MAX_BYTES = 32 * 1024 * 1024
+
+
+def kvq_paged_decode_attn_scratch(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_dtype: int,
+                                  block_tables: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, Hkv: int,
+                                  k_scale: float, v_scale: float, sm_scale: float, out: torch.Tensor, stream=None,
+                                  prepare: bool = False):
+    """kvq_paged_decode_attn without a workspace: the split partials go to the
+    library's own per-GPU scratch (KVQ_SCRATCH_MAX_BYTES); the call allocates
+    nothing.  Calls that overlap on one GPU race."""
+    B, Hq, D = q.shape
+    assert q.dtype == torch.bfloat16 and q.is_contiguous() and out.is_contiguous() and out.shape == q.shape
+    _tables(block_tables, seq_lens, B)
+    _require(kv_dtype in (KVQ_KV_BF16, KVQ_KV_FP8_E4M3), f"kv_dtype {kv_dtype}: BF16 or FP8 E4M3")
+    _caches(k_cache, v_cache, kv_dtype, Hkv, D)
+    _same_gpu(q, k_cache, v_cache, block_tables, seq_lens, out)
+    out_dtype = {torch.bfloat16: KVQ_OUT_BF16, torch.float32: KVQ_OUT_F32}[out.dtype]
+    return _run("kvq_paged_decode_attn_scratch", _lib.kvq_paged_decode_attn_scratch, (
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), kv_dtype, _ptr(block_tables), block_tables.shape[1],
+        _ptr(seq_lens), max_seq_len, B, Hq, Hkv, D, BLOCK_SIZE, k_cache.shape[0], k_scale, v_scale, sm_scale,
+        _ptr(out), out_dtype, _stream(stream)),
+        prepare, (q, k_cache, v_cache, block_tables, seq_lens, out))
 
 
 def kvq_paged_decode_attn_append(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,

@@ -37,7 +37,7 @@ int main(void) {
         (any_fn)kvq_nvfp4_paged_decode_attn_mq, (any_fn)kvq_paged_decode_attn_mq_append,
         (any_fn)kvq_paged_decode_attn_fp8qp, (any_fn)kvq_cache_block_bytes,
         (any_fn)kvq_gather_blocks, (any_fn)kvq_scatter_blocks, (any_fn)kvq_offload_blocks,
-        (any_fn)kvq_restore_blocks, (any_fn)kvq_e2m1_decode,
+        (any_fn)kvq_restore_blocks, (any_fn)kvq_e2m1_decode, (any_fn)kvq_paged_decode_attn_scratch,
     };
     for (size_t i = 0; i < sizeof(fns) / sizeof(fns[0]); ++i) CHECK(fns[i] != NULL);
 

@@ -52,7 +52,7 @@ def test_check_flags_host_side(K):
     assert K.lib().kvq_check_flags(None, 0) == K.KVQ_EINVAL
     assert K.open_library(K.CHECK_LIB_PATH).kvq_check_flags(None, 0) == K.KVQ_EINVAL
     want = int(re.search(r"#define KVQ_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
-    assert K.kvq_abi_version() == want == 5
+    assert K.kvq_abi_version() == want == 6
     assert K.kvq_strerror(-3) == "workspace too small"
 
 
@@ -279,3 +279,27 @@ def test_prepared_call_defers_and_checks(K):
     kc = torch.zeros(4, 1, 16, 64, dtype=torch.uint8)
     with pytest.raises(ValueError, match="kv_dtype"):
         K.kvq_cache_write(k, k, slots, kc, kc, 7, 1.0, 1.0, stream=0, prepare=True)
+
+
+def test_scratch_entry_host_validation(K):
+    """kvq_paged_decode_attn_scratch checks its arguments, and its size against
+    the library's scratch, before any HIP call (this runs without a GPU)."""
+    L = K.lib()
+    B, Hq, Hkv, D, Lmax = 2, 8, 2, 64, 1000
+    a = [FAKE, FAKE, FAKE, K.KVQ_KV_FP8_E4M3, FAKE, 64, FAKE, Lmax, B, Hq, Hkv, D, 16, 100, 0.1, 0.1, 0.125, FAKE,
+         K.KVQ_OUT_F32, None]
+    bad = lambda i, v: L.kvq_paged_decode_attn_scratch(*a[:i], v, *a[i + 1:])
+    assert bad(3, 5) == K.KVQ_EINVAL                 # kv_dtype
+    assert bad(10, 3) == K.KVQ_EINVAL                # Hq % Hkv
+    assert bad(11, 96) == K.KVQ_EUNSUPPORTED         # D
+    assert bad(16, -1.0) == K.KVQ_EINVAL             # sm_scale
+    assert bad(0, None) == K.KVQ_EINVAL              # q
+    assert bad(0, FAKE + 4) == K.KVQ_EINVAL          # alignment
+    assert bad(8, 0) == K.KVQ_OK                     # an empty batch enqueues nothing
+    # a call needing more partials than the scratch holds: refused before any HIP call
+    big = [FAKE, FAKE, FAKE, K.KVQ_KV_FP8_E4M3, FAKE, 8192, FAKE, 131072, 64, 32, 8, 256, 16, 1, 0.1, 0.1, 0.0625,
+           FAKE, K.KVQ_OUT_F32, None]
+    assert K.kvq_decode_workspace_bytes(64, 32, 8, 256, 131072) > K.KVQ_SCRATCH_MAX_BYTES
+    assert L.kvq_paged_decode_attn_scratch(*big) == K.KVQ_EWORKSPACE
+    assert K.KVQ_SCRATCH_MAX_BYTES == 32 * 1024 * 1024 == int(
+        re.search(r"#define KVQ_SCRATCH_MAX_BYTES \((\d+)u \* 1024u \* 1024u\)", open(HEADER).read()).group(1)) << 20
