@@ -450,6 +450,103 @@ def attn_only(torch, K, name, fmt, steps, warmup, impl=0):
             "split_tokens": K.kvq_decode_plan_split_tokens(w.B, w.Hkv, w.max_seq_len)}
 
 
+TRACE_LIB = os.path.join(ROOT, "quantized_decode_attention_calibrate_amd", "libkvq_trace.so")
+
+
+def phase_summary(raw, decode_words, merge_words):
+    """Phase breakdown of one traced call from the stamps libkvq_trace.so
+    stores (kvq_trace_set layout, 100 MHz clock), in microseconds:
+    distributions over waves of each decode phase, the merge kernel's start
+    after the last decode wave ended and its own phases, per-XCC loop times
+    (the same work lands on every XCC), and the spread of loop times between
+    the waves of one work-group."""
+    import numpy as np
+    us = 0.01
+
+    def q(x):
+        x = np.asarray(x, dtype=np.float64)
+        if x.size == 0:
+            return None
+        return {"med": round(float(np.median(x)), 2), "p10": round(float(np.percentile(x, 10)), 2),
+                "p90": round(float(np.percentile(x, 90)), 2), "max": round(float(x.max()), 2)}
+
+    dec = raw[:decode_words].reshape(-1, 8)
+    d = dec[(dec[:, 7] & np.uint64(0xFF)) == 1]
+    t = d[:, :6].astype(np.int64)
+    info, ids = d[:, 6], d[:, 7]
+    chunks = (info & np.uint64(0xFFFFF)).astype(np.int64)
+    wg = (info >> np.uint64(20)).astype(np.int64)          # (sequence, head, split) of the wave's work-group
+    xcc = ((ids >> np.uint64(8)) & np.uint64(15)).astype(np.int64)
+    t00 = t[:, 0].min()
+    loop = (t[:, 4] - t[:, 2]) * us
+    first = t[:, 3] > 0
+    out = {
+        "waves": int(len(t)), "chunks_per_wave": q(chunks),
+        "start_skew": q((t[:, 0] - t00) * us),
+        "seq_len": q((t[:, 1] - t[:, 0]) * us),
+        "block_id_staging": q((t[:, 2] - t[:, 1]) * us),
+        "first_chunk": q((t[first, 3] - t[first, 2]) * us),
+        "chunk_loop": q(loop),
+        "epilogue": q((t[:, 5] - t[:, 4]) * us),
+        "decode_end": q((t[:, 5] - t00) * us),
+    }
+    keys, inv = np.unique(wg, return_inverse=True)
+    lo = np.full(len(keys), np.inf)
+    hi = np.full(len(keys), -np.inf)
+    np.minimum.at(lo, inv, loop)
+    np.maximum.at(hi, inv, loop)
+    out["work_groups"] = int(len(keys))
+    out["intra_wg_loop_spread"] = q(hi - lo)
+    out["wg_slowest_wave_loop"] = q(hi)
+    out["per_xcc_loop_med"] = {int(x): round(float(np.median(loop[xcc == x])), 2) for x in np.unique(xcc)}
+    out["per_xcc_decode_end_max"] = {int(x): round(float((t[xcc == x, 5] - t00).max() * us), 2)
+                                     for x in np.unique(xcc)}
+    mer = raw[decode_words:decode_words + merge_words].reshape(-1, 4)
+    m = mer[mer[:, 3] == 1][:, :3].astype(np.int64)
+    if len(m):
+        out["merge_rows"] = int(len(m))
+        out["merge_start_after_decode_end"] = q((m[:, 0] - t[:, 5].max()) * us)
+        out["merge_split_weights"] = q((m[:, 1] - m[:, 0]) * us)
+        out["merge_rest"] = q((m[:, 2] - m[:, 1]) * us)
+        out["call_end"] = round(float((m[:, 2].max() - t00) * us), 2)
+    else:
+        out["call_end"] = round(float((t[:, 5].max() - t00) * us), 2)
+    return out
+
+
+def phases(torch, K, name, fmt, steps, warmup):
+    """Back-to-back attention calls of one workload through libkvq_trace.so;
+    the phase breakdown of the last call."""
+    import numpy as np
+    from quantized_decode_attention_calibrate_amd import workloads
+    kv, eb = {"fp8": (K.KVQ_KV_FP8_E4M3, 1), "bf16": (K.KVQ_KV_BF16, 2), "nvfp4": (NVFP4, NVFP4_BYTES)}[fmt]
+    w = workloads.make(name, device="cuda", seed=0)
+    L = Layers(K, w, kv, layers_for(w, eb), "cuda")
+    split = K.kvq_decode_plan_split_tokens(w.B, w.Hkv, w.max_seq_len)
+    grid = -(-w.max_seq_len // split) * w.Hkv * w.B
+    decode_words, merge_words = grid * 8 * 8, w.B * w.Hq * 4    # room for 8 waves per work-group
+    buf = torch.zeros(decode_words + merge_words, dtype=torch.int64, device="cuda")
+    st = K.lib().kvq_trace_set(buf.data_ptr(), decode_words, merge_words)
+    if st != K.KVQ_OK:
+        raise RuntimeError(f"kvq_trace_set: {K.kvq_strerror(st)} (is {K.LIB_PATH} the trace build?)")
+    try:
+        for i in range(warmup):
+            L.run("attend", i)
+        torch.cuda.synchronize()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        for i in range(steps):
+            L.run("attend", i)
+        a1.record()
+        torch.cuda.synchronize()
+        raw = buf.cpu().numpy().view(np.uint64)
+    finally:
+        K.lib().kvq_trace_set(None, 0, 0)
+    return {"workload": name, "kv": fmt, "split_tokens": split, "traced_calls": steps,
+            "traced_call_us": round(a0.elapsed_time(a1) / steps * 1e3, 2),
+            "phases_us": phase_summary(raw, decode_words, merge_words)}
+
+
 def measure_quality(torch, K, name):
     """The comparison the FP8 calibration guide asks for: BF16 KV, FP8 with the
     default scale 1.0, and FP8 with calibrated scales.  Reports the
@@ -723,7 +820,12 @@ def main():
                     help="skip the per-workload table (agents126k, mixed64, nvfp4_131k)")
     ap.add_argument("--attn-only", choices=("fp8", "bf16", "nvfp4"), default=None,
                     help="time only the attention call of --workload in this KV format (for profiling runs)")
+    ap.add_argument("--phases", choices=("fp8", "bf16", "nvfp4"), default=None,
+                    help="phase breakdown of the attention call of --workload in this KV format, from the "
+                         "timestamps of the trace build (libkvq_trace.so)")
     args = ap.parse_args()
+    if args.phases:   # every library call of this process goes to the trace build
+        os.environ["KVQ_LIBRARY"] = TRACE_LIB
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this path has no multi-GPU "
               "mode: the decode kernel shards by KV head or by sequence with no exchange.", file=sys.stderr)
@@ -734,6 +836,9 @@ def main():
     from quantized_decode_attention_calibrate_amd import workloads
 
     dev = "cuda"
+    if args.phases:
+        print(json.dumps(phases(torch, K, args.workload, args.phases, args.steps, args.warmup)), flush=True)
+        return
     if args.attn_only:
         print(json.dumps(attn_only(torch, K, args.workload, args.attn_only, args.steps, args.warmup, args.impl)),
               flush=True)

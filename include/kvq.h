@@ -58,8 +58,9 @@ extern "C" {
  * 3: kvq_check_flags and the checked build libkvq_check.so
  * 4: kvq_paged_decode_attn_mq_append
  * 5: kvq_nvfp4_cache_bytes_per_block
- * 6: kvq_paged_decode_attn_scratch */
-#define KVQ_ABI_VERSION 6
+ * 6: kvq_paged_decode_attn_scratch
+ * 7: kvq_trace_set and the phase-trace build libkvq_trace.so */
+#define KVQ_ABI_VERSION 7
 
 enum kvq_status {
     KVQ_OK = 0,
@@ -106,6 +107,32 @@ int kvq_abi_version(void);
 #define KVQ_CHECK_SEQ_LEN 2u
 #define KVQ_CHECK_SLOT 4u
 int kvq_check_flags(unsigned* flags_host, int clear);
+
+/* ---- phase trace (libkvq_trace.so) -----------------------------------------
+ * libkvq_trace.so is built from the same sources with -DKVQ_TRACE=1: the MFMA
+ * decode kernel and the merge kernel also store timestamps of their phases
+ * (the 100 MHz real-time counter, s_memrealtime), for attributing a call's
+ * time to its parts.  A stamp first waits for the wave's outstanding memory
+ * operations, so a traced call runs slightly slower; its results are the
+ * release build's.
+ * kvq_trace_set points the kernels at buf_dev, a device buffer of
+ * decode_words + merge_words uint64 words owned by the caller (NULL: tracing
+ * off); it is synchronous and applies to the current device.  Every call
+ * overwrites what the previous one stored.  Layout:
+ *   decode region, words [0, decode_words): 8 words per wave at
+ *     ((x + X * (y + Y * z)) * W + wave) * 8 for work-group (x, y, z) of a
+ *     grid (X, Y, Z) = (splits, KV heads, sequences) and W waves per
+ *     work-group: stamps at the start, after the sequence length, after the
+ *     block-id staging, after the first chunk, at the end of the chunk loop
+ *     and at the end; then chunks | split << 20 | KV head << 36 |
+ *     sequence << 44; then 1 | XCC id << 8 | HW_ID register << 16;
+ *   merge region, words [decode_words, decode_words + merge_words): 4 words
+ *     per output row (b * q_len + i) * Hq + h that has two or more splits:
+ *     start, after the split weights, end, 1.
+ * Waves and rows whose slots fall outside their region store nothing.
+ * Returns KVQ_EUNSUPPORTED from libkvq.so and libkvq_check.so, KVQ_EINVAL for
+ * negative sizes, KVQ_EHIP if setting the device pointer fails. */
+int kvq_trace_set(uint64_t* buf_dev, int64_t decode_words, int64_t merge_words);
 
 /* ---- codec utilities (device) ---------------------------------------------
  * The E4M3 codec used by every kernel, exposed for exhaustive checks.

@@ -1,13 +1,14 @@
 """Build libkvq.so (all HIP sources in csrc/) for gfx950 with hipcc, in-tree,
-and libkvq_check.so, the same sources with -DKVQ_CHECK=1 (device-side checks
-of the caller's block ids, slots and sequence lengths; kvq_check_flags).
+libkvq_check.so, the same sources with -DKVQ_CHECK=1 (device-side checks
+of the caller's block ids, slots and sequence lengths; kvq_check_flags), and
+libkvq_trace.so, with -DKVQ_TRACE=1 (phase timestamps; kvq_trace_set).
 
     python -m quantized_decode_attention_calibrate_amd.build
 
 Flags: -O3, no fast-math (the quantize step is an IEEE fp32 division),
 packed-fp32 VALU ops disabled, MFMA accumulators in VGPRs, code object v5
-(loads under the HIP runtime that PyTorch ships).  Both libraries bind their own symbols first
-(-Bsymbolic), so the two can be loaded into one process.
+(loads under the HIP runtime that PyTorch ships).  The libraries bind their own symbols first
+(-Bsymbolic), so they can be loaded into one process.
 """
 from __future__ import annotations
 
@@ -22,11 +23,13 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkvq.so")
 LIB_CHECK = os.path.join(PKG, "libkvq_check.so")
+LIB_TRACE = os.path.join(PKG, "libkvq_trace.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 # variant -> (library, extra compile flags, object directory)
 VARIANTS = {
     "release": (LIB, [], BUILD_DIR),
     "check": (LIB_CHECK, ["-DKVQ_CHECK=1"], os.path.join(BUILD_DIR, "check")),
+    "trace": (LIB_TRACE, ["-DKVQ_TRACE=1"], os.path.join(BUILD_DIR, "trace")),
 }
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -57,7 +60,7 @@ def _compile(src: str, extra=(), obj_dir: str = BUILD_DIR) -> str:
 
 
 def build(verbose: bool = True) -> str:
-    """Both libraries (the release one's path is returned)."""
+    """Every library variant (the release one's path is returned)."""
     srcs = sources()
     jobs = []
     for lib, extra, obj_dir in VARIANTS.values():
@@ -80,9 +83,10 @@ def build(verbose: bool = True) -> str:
 
 
 def is_stale() -> bool:
-    if not os.path.exists(LIB) or not os.path.exists(LIB_CHECK):
+    libs = [lib for lib, _, _ in VARIANTS.values()]
+    if not all(os.path.exists(lib) for lib in libs):
         return True
-    t = min(os.path.getmtime(LIB), os.path.getmtime(LIB_CHECK))
+    t = min(os.path.getmtime(lib) for lib in libs)
     deps = sources() + [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")]
     deps.append(os.path.join(INCLUDE, "kvq.h"))
     return any(os.path.getmtime(d) > t for d in deps)

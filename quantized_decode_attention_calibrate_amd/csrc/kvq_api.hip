@@ -99,6 +99,13 @@ int kvq_check_flags(unsigned* flags_host, int clear) {
     return KVQ_OK;
 }
 
+int kvq_trace_set(uint64_t* buf_dev, int64_t decode_words, int64_t merge_words) {
+    if (decode_words < 0 || merge_words < 0) return KVQ_EINVAL;
+    if (!KVQ_TRACE) return KVQ_EUNSUPPORTED;
+    const int r = trace_set_attn(buf_dev, decode_words, merge_words);
+    return r == 0 ? KVQ_OK : hip_status(hipErrorUnknown);
+}
+
 int kvq_e4m3_encode_f32(const float* y_dev, uint8_t* codes_dev, int64_t n, void* hip_stream) {
     if (n < 0) return KVQ_EINVAL;
     if (n == 0) return KVQ_OK;

@@ -66,6 +66,57 @@ __host__ __device__ constexpr int lds_merge_floats(int GQ, int D, int W, int NT 
     return W * 32 * NT + W * GQ * D;
 }
 
+// ---- phase trace (KVQ_TRACE builds) ------------------------------------------
+// Decode: 8 words per wave at ((work-group linear id) * W + wave) * 8 of the
+// decode region: stamps at the start, after the sequence length, after the
+// block-id staging, after the first chunk, at the loop end and at the end;
+// then chunks | split << 20 | KV head << 36 | sequence << 44, and
+// 1 | XCC id << 8 | HW_ID << 16.  Merge: 4 words per output row of the merge
+// region: start, after the split weights, end, 1.  Stamps count the 100 MHz
+// real-time clock.
+#if KVQ_TRACE
+__device__ uint64_t* g_trace = nullptr;
+__device__ int64_t g_trace_words[2] = {0, 0};   // decode region, merge region (words)
+__device__ __forceinline__ uint64_t trace_now(bool drain) {
+    if (drain) __builtin_amdgcn_s_waitcnt(0);   // stamp after the loads issued so far have landed
+    return __builtin_amdgcn_s_memrealtime();
+}
+struct PhaseTrace {
+    uint64_t t[6] = {0, 0, 0, 0, 0, 0};
+    __device__ __forceinline__ void mark(int i, bool drain = true) { t[i] = trace_now(drain); }
+    __device__ __forceinline__ void store_decode(int W, int wave, int lane, int chunks, int s, int g, int b) const {
+        const int64_t wg = blockIdx.x + (int64_t)gridDim.x * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+        const int64_t base = (wg * W + wave) * 8;
+        if (lane != 0 || !g_trace || base + 8 > g_trace_words[0]) return;
+        uint64_t* o = g_trace + base;
+        for (int i = 0; i < 6; ++i) o[i] = t[i];
+        o[6] = (uint64_t)chunks | ((uint64_t)s << 20) | ((uint64_t)g << 36) | ((uint64_t)b << 44);
+        const uint32_t xcc = (uint32_t)__builtin_amdgcn_s_getreg(0xF814) & 15u;   // hwreg(HW_REG_XCC_ID)
+        const uint32_t hw = (uint32_t)__builtin_amdgcn_s_getreg(0xF804);          // hwreg(HW_REG_HW_ID)
+        o[7] = 1ull | ((uint64_t)xcc << 8) | ((uint64_t)hw << 16);
+    }
+    __device__ __forceinline__ void store_merge(int64_t row) const {
+        const int64_t base = g_trace_words[0] + row * 4;
+        if (threadIdx.x != 0 || !g_trace || row * 4 + 4 > g_trace_words[1]) return;
+        uint64_t* o = g_trace + base;
+        o[0] = t[0];
+        o[1] = t[1];
+        o[2] = t[2];
+        o[3] = 1ull;
+    }
+};
+#define KVQ_TRACE_DECL PhaseTrace trace_
+#define KVQ_TRACE_MARK(...) trace_.mark(__VA_ARGS__)
+#define KVQ_TRACE_STORE_DECODE(...) trace_.store_decode(__VA_ARGS__)
+#define KVQ_TRACE_STORE_MERGE(row) trace_.store_merge(row)
+#else
+// (release and checked builds: no trace code at all)
+#define KVQ_TRACE_DECL
+#define KVQ_TRACE_MARK(...)
+#define KVQ_TRACE_STORE_DECODE(...)
+#define KVQ_TRACE_STORE_MERGE(row)
+#endif
+
 // Stage the physical block ids of logical blocks [lb0, lb0 + n) into LDS,
 // clamping logical blocks past the sequence to its last block and blocks
 // before a sliding window to the window's first block (those tokens are
@@ -643,6 +694,8 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
     float* s_acc = s_l + W * CP;
 
     const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    KVQ_TRACE_DECL;
+    KVQ_TRACE_MARK(0);
     const SeqRange sr = seq_range(a, b);
     const int L = sr.L;
     const int tok_begin = sr.base + s * a.split_tokens;
@@ -650,6 +703,7 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
         if (L <= 0 && s == 0) write_empty(a, b, g, D);
         return;
     }
+    KVQ_TRACE_MARK(1);
     const int tok_end = min(L, tok_begin + a.split_tokens);
     const int S = (L - sr.base + a.split_tokens - 1) / a.split_tokens;   // splits holding tokens
     // the wave index as a scalar: every per-wave loop bound below is then uniform,
@@ -824,6 +878,7 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
     const int tail_from = min(tok_end, q0_end);
     const int head_until = a.window > 0 ? max(0, L - a.window) : 0;   // the newest query's window start
     __syncthreads();
+    KVQ_TRACE_MARK(2, false);
     if constexpr (APPEND) {
         uint8_t* kc = const_cast<uint8_t*>(a.k_cache);
         uint8_t* vc = const_cast<uint8_t*>(a.v_cache);
@@ -975,6 +1030,9 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
                 if constexpr (NT == 1 && D == 64) __builtin_amdgcn_sched_barrier(0);
                 process_chunk(st, A, qb, cs, cbeg, cend, tok_begin + ch * kChunkTokens, tok_end, tail_from,
                               head_until, sr.first, grp);
+#if KVQ_TRACE
+                if (i == 0) KVQ_TRACE_MARK(3, false);
+#endif
                 const int cha = i + 2 < my ? chb + W : chb;
                 if (APPEND && writer && i + 3 == my) append_fence();
                 mfma_load(A, a, s_blk, cha, g, n, grp);
@@ -983,9 +1041,13 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
                               head_until, sr.first, grp);
                 ch = cha;
             }
-            if (my & 1)
+            if (my & 1) {
                 process_chunk(st, A, qb, cs, cbeg, cend, tok_begin + ch * kChunkTokens, tok_end, tail_from,
                               head_until, sr.first, grp);
+#if KVQ_TRACE
+                if (my == 1) KVQ_TRACE_MARK(3, false);
+#endif
+            }
         }
     } else {
         for (int i = 0; i < my; ++i) {
@@ -995,8 +1057,12 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
             mfma_load(A, a, s_blk, ch, g, n, grp);
             process_chunk(st, A, qb, cs, cbeg, cend, tok_begin + ch * kChunkTokens, tok_end, tail_from,
                           head_until, sr.first, grp);
+#if KVQ_TRACE
+            if (i == 0) KVQ_TRACE_MARK(3, false);
+#endif
         }
     }
+    KVQ_TRACE_MARK(4);
 
     // ---- wave results -> LDS ---------------------------------------------------
 #pragma unroll
@@ -1019,6 +1085,8 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
     }
     __syncthreads();
     finish_split<W, NT>(a, s_m, s_l, s_acc, b, g, s, S, D);
+    KVQ_TRACE_MARK(5);
+    KVQ_TRACE_STORE_DECODE(W, wave, lane, my, s, g, b);
 }
 
 // =============================================================================
@@ -1250,6 +1318,8 @@ __global__ void __launch_bounds__(kMergeThreads) merge_splits_kernel(DecodeArgs 
     __shared__ float s_scale;
     __shared__ f32x4 part[P][C4];
     const int hq = blockIdx.x;                // output row (b * q_len + i) * Hq + h
+    KVQ_TRACE_DECL;
+    KVQ_TRACE_MARK(0);
     const int b = hq / (a.Hq * a.q_len);
     const int t = threadIdx.x;
     const int d4 = t % C4, p = t / C4;
@@ -1286,6 +1356,7 @@ __global__ void __launch_bounds__(kMergeThreads) merge_splits_kernel(DecodeArgs 
         if (t == 0) s_scale = den > 0.f ? a.v_scale / den : 0.f;
     }
     __syncthreads();
+    KVQ_TRACE_MARK(1, false);
     f32x4 num = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < PRE; ++k) {
@@ -1303,6 +1374,8 @@ __global__ void __launch_bounds__(kMergeThreads) merge_splits_kernel(DecodeArgs 
 #pragma unroll
         for (int e = 0; e < 4; ++e) store_out(a, o + e, num[e] * scale);
     }
+    KVQ_TRACE_MARK(2);
+    KVQ_TRACE_STORE_MERGE(hq);
 }
 
 template <int D, int FMT, int NT>
@@ -1380,6 +1453,20 @@ hipError_t launch_decode(const DecodeArgs& a, int B, int D, int fmt, int impl, h
         case kFmtFP8QP: return launch_d<kFmtFP8QP>(a, B, D, impl, st);
         default: return hipErrorInvalidValue;
     }
+}
+
+int trace_set_attn(uint64_t* buf, int64_t decode_words, int64_t merge_words) {
+#if KVQ_TRACE
+    const int64_t words[2] = {buf ? decode_words : 0, buf ? merge_words : 0};
+    if (hipMemcpyToSymbol(HIP_SYMBOL(g_trace), &buf, sizeof(buf)) != hipSuccess) return -1;
+    if (hipMemcpyToSymbol(HIP_SYMBOL(g_trace_words), words, sizeof(words)) != hipSuccess) return -1;
+    return 0;
+#else
+    (void)buf;
+    (void)decode_words;
+    (void)merge_words;
+    return 1;
+#endif
 }
 
 unsigned check_flags_attn(bool clear) {

@@ -34,6 +34,16 @@ constexpr int kBlockSize = 16;
 #define KVQ_CHECK 0
 #endif
 enum : unsigned { kCheckBlockId = 1u, kCheckSeqLen = 2u, kCheckSlot = 4u };
+
+// Phase trace, compiled in only with -DKVQ_TRACE=1 (libkvq_trace.so): the MFMA
+// decode kernel and the merge kernel store s_memrealtime stamps of their
+// phases into a device buffer set by trace_set_attn (null: off).  The stamps
+// wait for outstanding memory operations first, so a traced call runs a
+// little slower; its results are the release build's.
+#ifndef KVQ_TRACE
+#define KVQ_TRACE 0
+#endif
+int trace_set_attn(uint64_t* buf, int64_t decode_words, int64_t merge_words);
 // Flag words of the kernel translation units: OR of the set bits; clear = zero
 // them afterwards.  Synchronous copies (0 when compiled without checks).
 unsigned check_flags_attn(bool clear);

@@ -14,6 +14,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("KVQ_LIBRARY") or os.path.join(_PKG, "libkvq.so")
 # the same library with device-side checks of the caller's data (kvq_check_flags)
 CHECK_LIB_PATH = os.path.join(_PKG, "libkvq_check.so")
+TRACE_LIB_PATH = os.path.join(_PKG, "libkvq_trace.so")
 KVQ_CHECK_BLOCK_ID, KVQ_CHECK_SEQ_LEN, KVQ_CHECK_SLOT = 1, 2, 4
 
 KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_EWORKSPACE, KVQ_EHIP = 0, -1, -2, -3, -4
@@ -43,6 +44,7 @@ def _load(path: str) -> ctypes.CDLL:
         "kvq_last_hip_error": (I, []),
         "kvq_abi_version": (I, []),
         "kvq_check_flags": (I, [P, I]),
+        "kvq_trace_set": (I, [P, I64, I64]),
         "kvq_e4m3_encode_f32": (I, [P, P, I64, P]),
         "kvq_e4m3_decode": (I, [P, P, I, I64, P]),
         "kvq_amax_bf16": (I, [P, I64, I64, I64, P, P]),

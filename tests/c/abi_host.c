@@ -38,6 +38,7 @@ int main(void) {
         (any_fn)kvq_paged_decode_attn_fp8qp, (any_fn)kvq_cache_block_bytes,
         (any_fn)kvq_gather_blocks, (any_fn)kvq_scatter_blocks, (any_fn)kvq_offload_blocks,
         (any_fn)kvq_restore_blocks, (any_fn)kvq_e2m1_decode, (any_fn)kvq_paged_decode_attn_scratch,
+        (any_fn)kvq_trace_set,
     };
     for (size_t i = 0; i < sizeof(fns) / sizeof(fns[0]); ++i) CHECK(fns[i] != NULL);
 
@@ -79,6 +80,7 @@ int main(void) {
                                 p, KVQ_OUT_F32, p, 16, NULL) == KVQ_EWORKSPACE);
     unsigned flags = 1;
     CHECK(kvq_check_flags(&flags, 0) == KVQ_EUNSUPPORTED && flags == 0);   /* the release build */
+    CHECK(kvq_trace_set(NULL, 0, 0) == KVQ_EUNSUPPORTED && kvq_trace_set(NULL, -1, 0) == KVQ_EINVAL);
     printf("c client: ok\n");
     return 0;
 }

@@ -37,9 +37,21 @@ def test_every_declared_symbol_is_exported(K):
     names = declared_functions()
     assert len(names) >= 12
     checked = K.open_library(K.CHECK_LIB_PATH)   # the build with device-side contract checks
+    traced = K.open_library(K.TRACE_LIB_PATH)    # the build with phase timestamps
     for n in names:
         assert hasattr(K.lib(), n), n
         assert hasattr(checked, n), n
+        assert hasattr(traced, n), n
+
+
+def test_trace_set_host_side(K):
+    """Only the trace build stores phase stamps; sizes are checked before any
+    HIP call in every build."""
+    assert K.lib().kvq_trace_set(None, 0, 0) == K.KVQ_EUNSUPPORTED
+    assert K.open_library(K.CHECK_LIB_PATH).kvq_trace_set(None, 0, 0) == K.KVQ_EUNSUPPORTED
+    traced = K.open_library(K.TRACE_LIB_PATH)
+    assert traced.kvq_trace_set(None, -1, 0) == K.KVQ_EINVAL
+    assert traced.kvq_trace_set(None, 0, -8) == K.KVQ_EINVAL
 
 
 def test_check_flags_host_side(K):
@@ -52,7 +64,7 @@ def test_check_flags_host_side(K):
     assert K.lib().kvq_check_flags(None, 0) == K.KVQ_EINVAL
     assert K.open_library(K.CHECK_LIB_PATH).kvq_check_flags(None, 0) == K.KVQ_EINVAL
     want = int(re.search(r"#define KVQ_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
-    assert K.kvq_abi_version() == want == 6
+    assert K.kvq_abi_version() == want == 7
     assert K.kvq_strerror(-3) == "workspace too small"
 
 
