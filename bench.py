@@ -423,13 +423,14 @@ def measure_workload(torch, K, name, steps, warmup, with_nvfp4=False):
     return rec
 
 
-def attn_only(torch, K, name, fmt, steps, warmup, impl=0):
+def attn_only(torch, K, name, fmt, steps, warmup, impl=0, contiguous=False):
     """Back-to-back attention calls of one workload in one KV format over
     rotated layer caches (no step loop, no other workloads): the run that
-    kernel traces and counter passes profile."""
+    kernel traces and counter passes profile.  contiguous: physical blocks in
+    logical order instead of the workload's random permutation."""
     from quantized_decode_attention_calibrate_amd import workloads
     kv, eb = {"fp8": (K.KVQ_KV_FP8_E4M3, 1), "bf16": (K.KVQ_KV_BF16, 2), "nvfp4": (NVFP4, NVFP4_BYTES)}[fmt]
-    w = workloads.make(name, device="cuda", seed=0)
+    w = workloads.make(name, device="cuda", seed=0, contiguous=contiguous)
     L = Layers(K, w, kv, layers_for(w, eb), "cuda")
     for i in range(warmup):
         L.run("attend", i, impl)
@@ -443,7 +444,8 @@ def attn_only(torch, K, name, fmt, steps, warmup, impl=0):
     torch.cuda.synchronize()
     us = a0.elapsed_time(a1) / steps * 1e3
     attn_b, _ = step_bytes(w.B, w.Hq, w.Hkv, w.D, w.seq_lens, eb, w.B)
-    return {"workload": name, "kv": fmt, "impl": {0: "auto", 1: "valu", 2: "mfma"}[impl], "steps": steps,
+    return {"workload": name, "kv": fmt, "impl": {0: "auto", 1: "valu", 2: "mfma"}[impl],
+            "blocks": "contiguous" if contiguous else "permuted", "steps": steps,
             "warmup": warmup, "attn_us": round(us, 2), "attn_gbps": round(attn_b / (us * 1e-6) / 1e9, 1),
             "pct_of_hbm_peak": round(100 * attn_b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 1),
             "attn_bytes": attn_b, "layers_rotated": L.R,
@@ -514,13 +516,13 @@ def phase_summary(raw, decode_words, merge_words):
     return out
 
 
-def phases(torch, K, name, fmt, steps, warmup):
+def phases(torch, K, name, fmt, steps, warmup, contiguous=False):
     """Back-to-back attention calls of one workload through libkvq_trace.so;
     the phase breakdown of the last call."""
     import numpy as np
     from quantized_decode_attention_calibrate_amd import workloads
     kv, eb = {"fp8": (K.KVQ_KV_FP8_E4M3, 1), "bf16": (K.KVQ_KV_BF16, 2), "nvfp4": (NVFP4, NVFP4_BYTES)}[fmt]
-    w = workloads.make(name, device="cuda", seed=0)
+    w = workloads.make(name, device="cuda", seed=0, contiguous=contiguous)
     L = Layers(K, w, kv, layers_for(w, eb), "cuda")
     split = K.kvq_decode_plan_split_tokens(w.B, w.Hkv, w.max_seq_len)
     grid = -(-w.max_seq_len // split) * w.Hkv * w.B
@@ -542,7 +544,8 @@ def phases(torch, K, name, fmt, steps, warmup):
         raw = buf.cpu().numpy().view(np.uint64)
     finally:
         K.lib().kvq_trace_set(None, 0, 0)
-    return {"workload": name, "kv": fmt, "split_tokens": split, "traced_calls": steps,
+    return {"workload": name, "kv": fmt, "blocks": "contiguous" if contiguous else "permuted",
+            "split_tokens": split, "traced_calls": steps,
             "traced_call_us": round(a0.elapsed_time(a1) / steps * 1e3, 2),
             "phases_us": phase_summary(raw, decode_words, merge_words)}
 
@@ -823,6 +826,9 @@ def main():
     ap.add_argument("--phases", choices=("fp8", "bf16", "nvfp4"), default=None,
                     help="phase breakdown of the attention call of --workload in this KV format, from the "
                          "timestamps of the trace build (libkvq_trace.so)")
+    ap.add_argument("--contiguous-blocks", action="store_true",
+                    help="with --attn-only / --phases: physical blocks in logical order instead of the "
+                         "workload's random permutation (what the scattered placement costs)")
     args = ap.parse_args()
     if args.phases:   # every library call of this process goes to the trace build
         os.environ["KVQ_LIBRARY"] = TRACE_LIB
@@ -837,11 +843,12 @@ def main():
 
     dev = "cuda"
     if args.phases:
-        print(json.dumps(phases(torch, K, args.workload, args.phases, args.steps, args.warmup)), flush=True)
+        print(json.dumps(phases(torch, K, args.workload, args.phases, args.steps, args.warmup,
+                                args.contiguous_blocks)), flush=True)
         return
     if args.attn_only:
-        print(json.dumps(attn_only(torch, K, args.workload, args.attn_only, args.steps, args.warmup, args.impl)),
-              flush=True)
+        print(json.dumps(attn_only(torch, K, args.workload, args.attn_only, args.steps, args.warmup, args.impl,
+                                   args.contiguous_blocks)), flush=True)
         return
     print(f"[bench] building {args.workload} on {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
     w = workloads.make(args.workload, device=dev, seed=0)

@@ -18,7 +18,9 @@ Workloads (sizes from the pages' scenarios; the distributions are readings):
   mixed64     64 sequences, lengths log-uniform in [1,024, 131,072], Hq 32 /
               Hkv 8, D 128.
   nvfp4_131k  the gptoss65k layer at 131,072 tokens, batch 2.
-Every workload uses block size 16 and a random permutation of physical blocks.
+Every workload uses block size 16 and a random permutation of physical blocks
+(make(..., contiguous=True): physical blocks in logical order instead, for
+measuring what the scattered placement costs).
 The last token of each sequence is the one a decode step writes.
 """
 from __future__ import annotations
@@ -104,11 +106,14 @@ def _add_outliers(x: torch.Tensor, frac: float, factor: float, g) -> torch.Tenso
     return x
 
 
-def _paging(seq_lens: List[int], bs: int, g, device):
+def _paging(seq_lens: List[int], bs: int, g, device, contiguous: bool = False):
     nblk = [(L + bs - 1) // bs for L in seq_lens]
     num_blocks = max(sum(nblk), 1)
-    perm = torch.randperm(num_blocks, generator=g, device="cpu" if g.device.type == "cpu" else g.device)
-    perm = perm.to("cpu")
+    if contiguous:
+        perm = torch.arange(num_blocks)
+    else:
+        perm = torch.randperm(num_blocks, generator=g, device="cpu" if g.device.type == "cpu" else g.device)
+        perm = perm.to("cpu")
     max_blocks = max(max(nblk) if nblk else 1, 1)
     bt = torch.zeros(len(seq_lens), max_blocks, dtype=torch.int32)
     slots = []
@@ -129,9 +134,10 @@ def _paging(seq_lens: List[int], bs: int, g, device):
 
 
 def make(name: str, device="cpu", seed: int = 0, seq_lens: Optional[List[int]] = None,
-         shape: Optional[dict] = None) -> Workload:
+         shape: Optional[dict] = None, contiguous: bool = False) -> Workload:
     """Build a named workload.  `seq_lens` and `shape` (Hq/Hkv/D/B) override the
-    defaults to get small instances of the same recipe for parity tests."""
+    defaults to get small instances of the same recipe for parity tests;
+    `contiguous` lays the physical blocks out in logical order."""
     device = torch.device(device)
     g = _gen(seed, device)
     cfg = dict(_DEFAULTS[name])
@@ -161,7 +167,7 @@ def make(name: str, device="cpu", seed: int = 0, seq_lens: Optional[List[int]] =
         k = k.to(torch.bfloat16)
         v = v.to(torch.bfloat16)
     gp = _gen(seed + 1, torch.device("cpu"))
-    bt, sm, nb, starts = _paging(seq_lens, BLOCK_SIZE, gp, device)
+    bt, sm, nb, starts = _paging(seq_lens, BLOCK_SIZE, gp, device, contiguous)
     return Workload(name=name, B=B, Hq=Hq, Hkv=Hkv, D=D, block_size=BLOCK_SIZE, seq_lens=list(seq_lens),
                     q=q, k=k, v=v, slot_mapping=sm, block_tables=bt, num_blocks=nb, seq_starts=starts,
                     calib_k=calib_k, calib_v=calib_v, meta=dict(cfg))

@@ -108,6 +108,17 @@ def test_physical_placement_is_bit_identical(K, impl):
     assert torch.equal(o1, o2)
 
 
+def test_contiguous_layout_is_bit_identical(K):
+    """The benchmark's contiguous-block layout (physical blocks in logical
+    order) gives the permuted layout's outputs bit for bit."""
+    w = workloads.make("gptoss65k", seed=7, seq_lens=[900, 333], shape=dict(Hq=16, Hkv=2))
+    wc = workloads.make("gptoss65k", seed=7, seq_lens=[900, 333], shape=dict(Hq=16, Hkv=2), contiguous=True)
+    assert torch.equal(w.k, wc.k) and not torch.equal(w.block_tables, wc.block_tables)
+    s1 = Setup(w, 1)
+    s2 = Setup(wc, 1, scales=(s1.ks, s1.vs))
+    assert torch.equal(s1.attend(torch.float32, impl=MFMA), s2.attend(torch.float32, impl=MFMA))
+
+
 @pytest.mark.parametrize("impl", [VALU, MFMA])
 def test_constant_values_give_the_constant(K, impl):
     w = workloads.make("gptoss65k", seed=8, seq_lens=[2000, 5], shape=dict(Hq=16, Hkv=2))
