@@ -17,7 +17,8 @@
 // for NVFP4 at D 64) per (split s, KV head g, sequence b).  A split is a
 // fixed range of logical tokens (a multiple of 64), so results do not depend
 // on physical block placement.  Each wave walks 64-token chunks (4 blocks of
-// 16) of the split round-robin; the waves merge through LDS and write one fp32 partial
+// 16) of the split round-robin, staging the physical block ids of its own
+// chunks in LDS (no work-group barrier before the loads); the waves merge through LDS and write one fp32 partial
 // (m, l, acc[G][D]) per head to the workspace; the merge kernel combines the
 // splits and applies v_scale.
 //
@@ -672,7 +673,7 @@ __device__ __forceinline__ void append_fence() {
 // work-group only, the one holding the split with that token for this KV
 // head, and within it by the wave whose round-robin share ends with the
 // chunk holding that token.  That wave quantizes the token and stores it
-// right after the block ids are staged, and before it loads that chunk it
+// right after its block ids are staged, and before it loads that chunk it
 // waits for its own stores (a work-group-scope fence), so the chunk's loads
 // see the new bytes.  The one-token case has a kernel of its own: the
 // general writer costs the decode step about 0.2 us at D 64.
@@ -723,7 +724,7 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
     // by the wave owning that chunk, this wave's being [new_lo, new_hi).  For
     // W >= 2 a written chunk is its wave's last, so the wave writes before that
     // chunk's first load (append_fence).  The bf16 rows are loaded here, in
-    // flight with the block-id staging, and stored after the barrier.
+    // flight with the block-id staging, and stored after it.
     int new_lo = 0, new_hi = 0;
     if constexpr (APPEND == kAppendMany) {
         const int p0 = max(max(L - a.q_len, 0), tok_begin);   // new tokens of this split: [p0, tok_end)
@@ -801,8 +802,22 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
             }
         }
     }
-    stage_block_ids(s_blk, a.block_tables + (int64_t)b * a.max_blocks, lb0, n_chunks * 4, sr.first / kBlockSize,
-                    (L + kBlockSize - 1) / kBlockSize - 1, a.num_blocks);
+    // this wave's chunks: wave, wave + W, ...; each wave stages the block ids of
+    // its own chunks only, so no barrier is needed before its loads
+    const int my = wave < n_chunks ? (n_chunks - wave + W - 1) / W : 0;
+    {
+        const int32_t* bt_row = a.block_tables + (int64_t)b * a.max_blocks;
+        const int first_lb = sr.first / kBlockSize, last_lb = (L + kBlockSize - 1) / kBlockSize - 1;
+        for (int i = lane; i < 4 * my; i += 64) {
+            const int e = 4 * (wave + W * (i >> 2)) + (i & 3);   // entry of chunk wave + W * (i / 4)
+            int id = bt_row[min(max(lb0 + e, first_lb), last_lb)];
+            if (KVQ_CHECK && (unsigned)id >= (unsigned)a.num_blocks) {
+                check_fail(kCheckBlockId);
+                id = 0;
+            }
+            s_blk[e] = id;
+        }
+    }
 
     // Query i (token L - q_len + i) sees tokens [cbeg, cend): cend = that
     // token + 1, cbeg = cend - window (or 0).
@@ -877,7 +892,6 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
     }
     const int tail_from = min(tok_end, q0_end);
     const int head_until = a.window > 0 ? max(0, L - a.window) : 0;   // the newest query's window start
-    __syncthreads();
     KVQ_TRACE_MARK(2, false);
     if constexpr (APPEND) {
         uint8_t* kc = const_cast<uint8_t*>(a.k_cache);
@@ -1002,9 +1016,6 @@ __global__ void __launch_bounds__(W * 64) decode_mfma_kernel(DecodeArgs a) {
         st.m_run[nt] = -INFINITY;
         st.l_run[nt] = 0.f;
     }
-    // this wave's chunks: wave, wave + W, ...
-    const int my = wave < n_chunks ? (n_chunks - wave + W - 1) / W : 0;
-
     if constexpr (kPrefetch) {
         // Software pipeline: the next chunk's loads are in flight while the
         // current one is computed.  The prefetch is unconditional so wait
