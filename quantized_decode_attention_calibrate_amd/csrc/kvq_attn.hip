@@ -277,7 +277,11 @@ __device__ __forceinline__ void mfma_load(MfmaChunk<D, FMT>& c, const DecodeArgs
 #pragma unroll
             for (int j = 0; j < KJ; ++j) {
                 c.kc[i][j] = *reinterpret_cast<const u32x2*>(kr + off * (D / 2) + 32 * j + 8 * grp);
-                c.ks[i][j] = kr[codes + off * (D / 16) + 4 * j + grp];
+                // the aligned dword holding this row's 4 block scales of slice j; the
+                // lane's (byte grp) is selected at use.  A byte load here made the
+                // compiler zero-extend the next chunk's scales at the end of the
+                // loop body, which waited on that chunk's just-issued loads.
+                c.ks[i][j] = *reinterpret_cast<const uint32_t*>(kr + codes + off * (D / 16) + 4 * j);
             }
         }
 #pragma unroll
@@ -331,7 +335,8 @@ __device__ __forceinline__ QkOperand<FMT> k_operand(const MfmaChunk<D, FMT>& c, 
     } else if constexpr (FMT == kFmtBF16) {
         return __builtin_bit_cast(bf16x8, c.kw[i][j][hh]);
     } else {
-        return e2m1x8_scaled_f16(c.kc[i][j][hh], e4m3x2_to_f16(c.ks[i][j], false)[0]);
+        const int grp = (threadIdx.x & 63) >> 4;   // the lane's 16-dim block within the 64-dim slice
+        return e2m1x8_scaled_f16(c.kc[i][j][hh], e4m3x2_to_f16(c.ks[i][j] >> (8 * grp), false)[0]);
     }
 }
 
