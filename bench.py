@@ -136,9 +136,13 @@ class Layers:
         # ctypes call per launch on the host and stays device-bound.
         self._prep = {}
         self.prepare_all()
-        # Set-up reads every layer cache once with the attention call (untimed),
-        # so a short timed run does not catch the first reads of each cache.
+        # Each cache then gets its newest token (the prefill wrote every token
+        # but that one), so an attention call on its own reads only written
+        # slots, and is read once with that call (untimed), so a short timed
+        # run does not catch the first reads of each cache.  A step rewrites
+        # the same token with the same bytes.
         for i in range(self.R):
+            self.run("write", i)
             self.run("attend", i)
         torch.cuda.synchronize()
 
