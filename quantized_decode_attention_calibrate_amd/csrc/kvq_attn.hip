@@ -441,6 +441,12 @@ __device__ __forceinline__ void mfma_process(MfmaState<D, NT>& st, MfmaChunk<D, 
         // exact V operand reproduce the fp32 weight to ~2^-21.  The scale is
         // common to acc and l and cancels in the final division.
         const float m_off = m_use - (15.0f - kLazy);
+        // lo = p - hi is exact in fp32 (hi is p truncated to 11 bits), so an
+        // fma with -1 gives the same bits as the subtraction; with the -1 in a
+        // register the compiler takes hi straight from its f16 half
+        // (v_fma_mix_f32) instead of converting it first
+        float neg_one;
+        asm("v_mov_b32 %0, -1.0" : "=v"(neg_one));
         float psum = 0.f;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
@@ -451,8 +457,9 @@ __device__ __forceinline__ void mfma_process(MfmaState<D, NT>& st, MfmaChunk<D, 
                 psum += p0 + p1;
                 if constexpr (kF16V) {
                     const f16x2 h = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(p0, p1));
-                    const f16x2 l =
-                        __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(p0 - (float)h[0], p1 - (float)h[1]));
+                    const f16x2 l = __builtin_bit_cast(
+                        f16x2, __builtin_amdgcn_cvt_pkrtz(__builtin_fmaf((float)h[0], neg_one, p0),
+                                                          __builtin_fmaf((float)h[1], neg_one, p1)));
                     pfh[nt][hh][2 * e2] = h[0];
                     pfh[nt][hh][2 * e2 + 1] = h[1];
                     pfl[nt][hh][2 * e2] = l[0];
