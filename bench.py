@@ -198,6 +198,26 @@ class Layers:
                                             prepare=prepare)
 
 
+SETTLE_MS = 50.0
+
+
+def settle(torch, fn, min_calls, min_ms=SETTLE_MS):
+    """Untimed calls fn(0), fn(1), ... until at least min_calls have run and
+    at least min_ms of wall time has passed.  The loops that measure the
+    attention call alone start from the GPU's steady clock this way: after a
+    short warmup the clock is still rising, which made NVFP4 calls ~5% slower
+    (40.4-41.4 us after 10 calls, 38.2-38.4 us after 200) and FP8 ~2%.
+    Returns the number of calls made."""
+    n = 0
+    t0 = time.perf_counter()
+    while n < min_calls or (time.perf_counter() - t0) * 1e3 < min_ms:
+        for _ in range(10):
+            fn(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
 def time_steps(torch, layers, steps, warmup, impl=0, fused=False):
     """Returns (ms per step, mean ms of the attention call alone), HIP events
     on the launch stream.  A step is the new token's cache write and the
@@ -231,12 +251,11 @@ def time_steps(torch, layers, steps, warmup, impl=0, fused=False):
     # the attention call alone (split kernel + merge kernel), back to back over
     # the rotated layer caches: its mean launch duration on the launch stream.
     # A diagnostic for the format comparisons, measured the same way for every
-    # format: its own warmup and at least 200 calls, so the first launch after
-    # an idle GPU (several us) is not charged to a short loop
+    # format: its own warmup (settle) and at least 200 calls, so neither the
+    # first launch after an idle GPU (several us) nor the clock's ramp is
+    # charged to a short loop
     n_attn = max(steps, 200)
-    for i in range(max(warmup, 10)):
-        layers.run("attend", i, impl)
-    torch.cuda.synchronize()
+    settle(torch, lambda i: layers.run("attend", i, impl), max(warmup, 10))
     a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a0.record(st)
     for i in range(n_attn):
@@ -332,9 +351,7 @@ def measure_multiquery(torch, K, name, q_lens, steps, warmup):
     rec = {"B": w.B, "max_seq_len": w.max_seq_len, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "kv": "fp8_e4m3"}
 
     def timed(fn):
-        for i in range(warmup):
-            fn(i)
-        torch.cuda.synchronize()
+        settle(torch, fn, warmup)
         a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a0.record(st)
         for i in range(steps):
