@@ -145,6 +145,10 @@ class Layers:
             self.run("write", i)
             self.run("attend", i)
         torch.cuda.synchronize()
+        # ... and keeps the GPU busy with that call for SETTLE_MS, so a short
+        # timed run (a few warmup steps) starts at the clock a decode loop
+        # runs at rather than on the way up to it
+        settle(torch, lambda i: self.run("attend", i), self.R)
 
     def prepare_all(self, impl=0):
         """Marshals every call kind for every layer cache now, so no timed loop

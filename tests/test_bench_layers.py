@@ -99,12 +99,12 @@ def test_setup_writes_newest_token_before_any_attention_call(setup):
     w, lib = setup
     L = bench.Layers(lib, w, lib.KVQ_KV_FP8_E4M3, 5, "cpu")
     assert lib.unwritten_reads == []
-    # every cache was read once by the attention call at set-up, after its write
-    attends = [c for kind, c in lib.runs if kind == "attend"]
-    assert sorted(attends) == sorted(id(kc) for kc, _ in L.caches)
+    # every cache was written once and then read by the attention call at
+    # set-up (the set-up then keeps reading them for a while: settle)
     for kc, _ in L.caches:
         kinds = [kind for kind, c in lib.runs if c == id(kc)]
-        assert kinds == ["write", "attend"]
+        assert kinds[0] == "write" and kinds.count("write") == 1 and kinds[1] == "attend", kinds[:4]
+        assert set(kinds[1:]) == {"attend"}
     # later attention calls on their own read written slots only
     for i in range(2 * L.R):
         L.run("attend", i)
